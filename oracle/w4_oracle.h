@@ -1,0 +1,83 @@
+/*
+ * w4_oracle.h -- plain, slow CPU oracle of the INT4 weight-quantized linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this code.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg use it, to check and to time the HIP path.
+ * It shares no source with the HIP library.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [KERAS]  "INT4 quantization in Keras" (Keras guide), section "How it works",
+ *            steps 1-6, and "What Keras does in INT4 mode".
+ *   [W4A16]  "INT4量化 / 4-bit Integer Quantization for LLMs", section
+ *            "量化原理" (weight quantization formula; activations stay high precision).
+ *   [ENCY]   "INT4" concept entry (compassingai), section 4.1 (uniform quantization
+ *            formulas, symmetric and asymmetric scale), 4.2 (group quantization),
+ *            4.5 (hardware execution schemes A and C).
+ *   [BLOG]   hnwysp.cn INT4 article, section 2.1 (Q = round(clamp(v/s,-8,7))) and
+ *            6.2 (scale = max|x| / 7).
+ *
+ * Every function returns 0 on success and a negative value when an input is
+ * not finite (non-finite inputs are outside the method's domain) or when an
+ * integer range assertion fails.
+ *
+ * Parity status of each function is stated in the test suite's pin tests:
+ * every function below is pinned (brute force, closed forms, invariants or
+ * hand-derived golden fixtures).
+ */
+#ifndef W4_ORACLE_H
+#define W4_ORACLE_H
+#include <stdint.h>
+
+#define ORC_OK 0
+#define ORC_ERR_NONFINITE (-1)
+#define ORC_ERR_RANGE (-2)
+#define ORC_ERR_ROUNDMODE (-3)
+#define ORC_ERR_SHAPE (-4)
+
+/* Symmetric per-output-channel int4 weight quantization and packing.
+ * W is [K][N] fp32 row-major (Dense kernel orientation, N output channels).
+ * Outputs: packed [N][(K+1)/2] bytes (k even -> low nibble), sw [N] fp32. */
+int orc_quantize_weight_sym(const float *W, int64_t K, int64_t N,
+                            uint8_t *packed, float *sw);
+
+/* Unpack one signed code (two's complement nibble) from the packed layout. */
+int orc_unpack_signed(const uint8_t *packed, int64_t K, int64_t n, int64_t k);
+
+/* Per-row dynamic int8 activation quantization.
+ * X is [M][K] fp32.  Outputs Xq [M][K] int8 and sx [M] fp32. */
+int orc_quantize_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx);
+
+/* acc[m][n] = sum_k Xq[m][k] * q[n][k]  (exact integer dot product). */
+int orc_matmul_i32(const int8_t *Xq, const uint8_t *packed, int64_t M, int64_t K,
+                   int64_t N, int32_t *acc);
+
+/* y[m][n] = fl(fl(float(acc)) * fl(sx[m]*sw[n])), then fl(y + b[n]) if bias. */
+int orc_dequant(const int32_t *acc, const float *sx, const float *sw,
+                const float *bias, int64_t M, int64_t N, float *Y);
+
+/* The whole W4A8 forward: quantize X per row, integer GEMM, dequant (+bias). */
+int orc_w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N,
+                    const uint8_t *packed, const float *sw, const float *bias,
+                    float *Y);
+
+/* Asymmetric group-wise int4 quantization along K (codes 0..15).
+ * Outputs packed [N][(K+1)/2], scales [N][K/g], zeros [N][K/g] (integer-valued). */
+int orc_quantize_weight_asym(const float *W, int64_t K, int64_t N, int64_t group,
+                             uint8_t *packed, float *scales, float *zeros);
+
+/* fp32 -> bf16 round-half-to-even (bit pattern). */
+uint16_t orc_bf16_rne(float f);
+
+/* Dequantized bf16 weight w'[k][n] = bf16(fl(float(q - zp) * s)) (bit pattern). */
+int orc_w4a16_dequant(const uint8_t *packed, const float *scales, const float *zeros,
+                      int64_t K, int64_t N, int64_t group, uint16_t *Wd /* [K][N] */);
+
+/* y[m][n] = sum_k x[m][k] * w'[k][n] evaluated in fp64 (products are exact);
+ * absy[m][n] = sum_k |x[m][k] * w'[k][n]| (for the fp32 summation bound).
+ * X is bf16 bits [M][K].  absy may be NULL. */
+int orc_w4a16_linear(const uint16_t *X, int64_t M, int64_t K, int64_t N,
+                     const uint8_t *packed, const float *scales, const float *zeros,
+                     int64_t group, double *Y, double *absy);
+
+#endif
