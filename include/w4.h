@@ -1,0 +1,156 @@
+/*
+ * w4.h -- C ABI of the MI355X (gfx950) INT4 weight-quantized linear layer.
+ *
+ * The method (INT4 quantization guide of Keras, "How it works", steps 1-6):
+ *   1. each output channel of a weight matrix gets a symmetric absmax scale,
+ *   2. weights are rounded into [-8, 7] and packed two per byte,
+ *   3. at inference time activations are scaled by a dynamic absmax and
+ *      quantized to INT8,
+ *   4. the packed INT4 weights are unpacked to INT8 values,
+ *   5. an INT8 x INT8 product is accumulated in INT32,
+ *   6. the result is dequantized with input_scale * per_channel_kernel_scale.
+ * A weight-only variant ("4-bit Integer Quantization for LLMs", quantization
+ * principle; "INT4" concept entry, sections 4.1, 4.2 and 4.5) stores
+ * asymmetric group-wise codes in [0, 15] with a scale and zero point per group
+ * and dequantizes them to 16-bit floats (bf16 here) at compute time.
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller (for
+ *     example torch tensors); the library never allocates or frees memory.
+ *   - `stream` is a hipStream_t handle (NULL = the default stream).  Every
+ *     call is asynchronous on that stream.
+ *   - Arguments are checked on the host before anything is launched; on a
+ *     failed check the call returns a negative w4_status and launches nothing.
+ *     After launching, a launch error is reported as W4_ERR_HIP.
+ *   - Row-major layouts throughout.  W is [K][N] (input dim K, N output
+ *     channels), X is [M][K], Y is [M][N].
+ *   - Packed int4 layout: output channel n owns the (K+1)/2 bytes
+ *     packed[n*((K+1)/2) ...]; byte j holds k = 2j in bits 0-3 and k = 2j+1 in
+ *     bits 4-7; a missing last high nibble (odd K) is 0.  Signed codes are
+ *     two's complement nibbles; unsigned codes are plain nibbles.
+ *   - Rounding is round-half-to-even; quotients are correctly rounded fp32
+ *     divisions.  Inputs must be finite (non-finite values are a caller error;
+ *     results are then unspecified).
+ *   - Calls on one stream are ordered; calls that write the same buffers on
+ *     different streams race.
+ */
+#ifndef W4_H
+#define W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4_OK = 0,
+    W4_ERR_NULL = -1,      /* a required pointer is NULL                          */
+    W4_ERR_SHAPE = -2,     /* a size is < 1, or K % group_size != 0, or too large */
+    W4_ERR_ALIGN = -3,     /* a pointer is not aligned to its element size        */
+    W4_ERR_SCHEME = -4,    /* unknown quantization scheme                         */
+    W4_ERR_WORKSPACE = -5, /* workspace missing or smaller than required          */
+    W4_ERR_HIP = -6        /* the HIP runtime reported an error                   */
+} w4_status;
+
+typedef enum {
+    W4_SYM_PER_CHANNEL = 0, /* signed codes [-8,7], scale = absmax/7 per channel  */
+    W4_ASYM_GROUP = 1       /* unsigned codes [0,15], scale + zero point per group */
+} w4_scheme;
+
+/* Largest K accepted by the integer paths: |acc| <= 128*8*K must fit int32
+ * with the 16x headroom the unpacking uses (16*1024*K < 2^31). */
+#define W4_MAX_K 131071
+
+/* Quantize a weight matrix and pack it (Keras guide steps 1-2 for
+ * W4_SYM_PER_CHANNEL; weight-only page's quantization principle and concept
+ * entry 4.1-4.2 for W4_ASYM_GROUP).
+ *   W       [K][N] fp32, finite.
+ *   scheme  W4_SYM_PER_CHANNEL: group_size must be 0, scales is [N]:
+ *             scales[n] = fl(max_k |W[k][n]| / 7) (0 for an all-zero channel),
+ *             code = clamp(rne(fl(W / scale)), -8, 7) (0 where scale is 0);
+ *             zeros must be NULL.
+ *           W4_ASYM_GROUP: group_size >= 1 with K % group_size == 0; groups of
+ *             group_size consecutive k inside one channel; scales and zeros
+ *             are [N][K/group_size]:
+ *               lo, hi = min, max of the group;
+ *               scale = fl(fl(hi - lo) / 15) if hi > lo, else |lo| (1 if lo == 0);
+ *               zero  = 0 - rne(fl(lo / scale))  (integer-valued fp32, not clamped);
+ *               code  = clamp(rne(fl(W / scale)) + zero, 0, 15).
+ *   packed  [N][(K+1)/2] bytes, fully written.
+ * Returns W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_SCHEME or W4_ERR_HIP. */
+int w4_quantize_weight(const float *W, int64_t K, int64_t N, int scheme,
+                       int64_t group_size, uint8_t *packed, float *scales,
+                       float *zeros, void *stream);
+
+/* Per-row dynamic int8 activation quantization (Keras guide step 3).
+ *   X   [M][K] fp32, finite.
+ *   sx  [M]: sx[m] = fl(max_k |X[m][k]| / 127) (0 for an all-zero row).
+ *   Xq  [M][K] int8: clamp(rne(fl(X / sx)), -128, 127) (0 where sx is 0).
+ * Returns W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN or W4_ERR_HIP. */
+int a8_quantize_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx,
+                    void *stream);
+
+/* Bytes of device workspace that w4a8_linear, w4a8_linear_q and
+ * w4a8_matmul_i32 need for this shape (0 when none is needed); 0 also for
+ * invalid sizes. */
+size_t w4a8_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/* The W4A8 forward (Keras guide steps 3-6), with an optional bias added
+ * after dequantization (the Dense layer's bias).
+ *   X       [M][K] fp32 activations.
+ *   packed  [N][(K+1)/2] signed codes and sw [N] scales from
+ *           w4_quantize_weight(..., W4_SYM_PER_CHANNEL, ...); any byte value is
+ *           accepted (code -8 included).
+ *   bias    [N] fp32 or NULL.
+ *   Y       [M][N] fp32: Y = fl(fl(float(acc) * fl(sx[m] * sw[n])) [+ bias[n]]),
+ *           acc = sum_k Xq[m][k] * code[n][k] exactly, Xq and sx as in
+ *           a8_quantize_act.
+ *   workspace  device memory of at least w4a8_workspace_bytes(M, K, N) bytes,
+ *           256-byte aligned (may be NULL when that size is 0); its contents
+ *           are scratch, overwritten by the call.
+ * Returns W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_WORKSPACE or W4_ERR_HIP. */
+int w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N,
+                const uint8_t *packed, const float *sw, const float *bias,
+                float *Y, void *workspace, size_t workspace_bytes, void *stream);
+
+/* The W4A8 forward from already-quantized activations (Keras guide steps 4-6):
+ *   Xq [M][K] int8 and sx [M] fp32 (any values); the rest as w4a8_linear. */
+int w4a8_linear_q(const int8_t *Xq, const float *sx, const uint8_t *packed,
+                  const float *sw, const float *bias, int64_t M, int64_t K,
+                  int64_t N, float *Y, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/* The exact integer product alone (Keras guide steps 4-5), for checking:
+ *   acc [M][N] int32 = sum_k Xq[m][k] * code[n][k]. */
+int w4a8_matmul_i32(const int8_t *Xq, const uint8_t *packed, int64_t M,
+                    int64_t K, int64_t N, int32_t *acc, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/* The weight-only W4A16 forward (weight-only page: activations stay 16-bit,
+ * weights are dequantized at compute time; concept entry 4.5, schemes A/C).
+ *   X_bf16  [M][K] bf16 bit patterns.
+ *   packed  [N][(K+1)/2] unsigned codes; scales, zeros [N][K/group_size] fp32
+ *           from w4_quantize_weight(..., W4_ASYM_GROUP, group_size, ...).
+ *   Y       [M][N] fp32 = sum_k x[m][k] * w'[k][n], with
+ *           w' = bf16_rne(fl(fl(float(code) - zero) * scale)), products and
+ *           sums in fp32 (the summation order is unspecified; the result is
+ *           within K*2^-24 * sum_k |x*w'| of the exact sum).
+ * Returns W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN or W4_ERR_HIP. */
+int w4a16_linear(const uint16_t *X_bf16, int64_t M, int64_t K, int64_t N,
+                 const uint8_t *packed, const float *scales, const float *zeros,
+                 int64_t group_size, float *Y, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *w4_status_string(int status);
+
+/* Name of the kernel variant the last successful call on this thread launched
+ * for its main product (for tests and profiling; never NULL). */
+const char *w4_last_path(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4_H */

@@ -1,0 +1,230 @@
+"""Python binding of libw4.so, the MI355X (gfx950) INT4 weight-quantized linear layer.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/w4.h``.  PyTorch provides the
+device memory (tensors) and the stream (the current HIP stream).  The
+functions carry the C names:
+
+* ``w4_quantize_weight``  -- symmetric per-channel int4 (``scheme="sym"``) or
+  asymmetric group-wise int4 (``scheme="asym"``) weights, packed two per byte;
+* ``a8_quantize_act``     -- per-row dynamic int8 activations;
+* ``w4a8_linear``         -- the W4A8 forward from fp32 activations;
+* ``w4a8_linear_q``       -- the W4A8 forward from int8 activations;
+* ``w4a8_matmul_i32``     -- the exact int32 accumulators alone;
+* ``w4a16_linear``        -- the weight-only forward with bf16 activations.
+
+There is no CPU fallback: without the built library (``build.py``) or
+without a GPU every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4.so")
+
+W4_OK = 0
+W4_SYM_PER_CHANNEL = 0
+W4_ASYM_GROUP = 1
+W4_MAX_K = 131071
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int64
+_Z = ctypes.c_size_t
+_lib = None
+
+
+class W4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {w4_status_string(status)} (status {status})")
+
+
+def lib():
+    """The loaded libw4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP library first "
+                "(python int4_weight_quantized_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        sigs = {
+            "w4_quantize_weight": ([_P, _I, _I, ctypes.c_int, _I, _P, _P, _P, _P], ctypes.c_int),
+            "a8_quantize_act": ([_P, _I, _I, _P, _P, _P], ctypes.c_int),
+            "w4a8_workspace_bytes": ([_I, _I, _I], _Z),
+            "w4a8_linear": ([_P, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P], ctypes.c_int),
+            "w4a8_linear_q": ([_P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _Z, _P], ctypes.c_int),
+            "w4a8_matmul_i32": ([_P, _P, _I, _I, _I, _P, _P, _Z, _P], ctypes.c_int),
+            "w4a16_linear": ([_P, _I, _I, _I, _P, _P, _P, _I, _P, _P], ctypes.c_int),
+            "w4_status_string": ([ctypes.c_int], ctypes.c_char_p),
+            "w4_last_path": ([], ctypes.c_char_p),
+        }
+        for name, (args, res) in sigs.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def w4_status_string(status: int) -> str:
+    return lib().w4_status_string(int(status)).decode()
+
+
+def w4_last_path() -> str:
+    """Kernel variant of the last call's main product (e.g. "gemv_dot4")."""
+    return lib().w4_last_path().decode()
+
+
+def w4a8_workspace_bytes(M: int, K: int, N: int) -> int:
+    return int(lib().w4a8_workspace_bytes(M, K, N))
+
+
+# ------------------------------------------------------------------ helpers
+def _dev(t: torch.Tensor, name: str, dtype) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _opt(t, name, dtype):
+    return None if t is None else _dev(t, name, dtype)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != W4_OK:
+        raise W4Error(fn, rc)
+
+
+def _workspace(M, K, N, device, workspace):
+    need = w4a8_workspace_bytes(M, K, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return workspace, need
+
+
+# ------------------------------------------------------------------ calls
+def w4_quantize_weight(W: torch.Tensor, scheme: str = "sym", group_size: int = 0,
+                       packed=None, scales=None, zeros=None, stream=None):
+    """W [K, N] fp32 -> (packed uint8 [N, ceil(K/2)], scales, zeros).
+
+    ``scheme="sym"``: scales [N], zeros None.  ``scheme="asym"``: scales and
+    zeros [N, K/group_size]."""
+    K, N = W.shape
+    sch = {"sym": W4_SYM_PER_CHANNEL, "asym": W4_ASYM_GROUP}.get(scheme, -1)
+    dev = W.device
+    if packed is None:
+        packed = torch.empty((N, (K + 1) // 2), dtype=torch.uint8, device=dev)
+    if sch == W4_ASYM_GROUP and group_size > 0:
+        G = K // group_size
+        if scales is None:
+            scales = torch.empty((N, G), dtype=torch.float32, device=dev)
+        if zeros is None:
+            zeros = torch.empty((N, G), dtype=torch.float32, device=dev)
+    elif scales is None:
+        scales = torch.empty((N,), dtype=torch.float32, device=dev)
+    rc = lib().w4_quantize_weight(_dev(W, "W", torch.float32), K, N, sch, group_size,
+                                  _dev(packed, "packed", torch.uint8),
+                                  _dev(scales, "scales", torch.float32),
+                                  _opt(zeros, "zeros", torch.float32), _stream(stream))
+    _check("w4_quantize_weight", rc)
+    return packed, scales, zeros
+
+
+def a8_quantize_act(X: torch.Tensor, Xq=None, sx=None, stream=None):
+    """X [M, K] fp32 -> (Xq int8 [M, K], sx fp32 [M])."""
+    M, K = X.shape
+    if Xq is None:
+        Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if sx is None:
+        sx = torch.empty((M,), dtype=torch.float32, device=X.device)
+    rc = lib().a8_quantize_act(_dev(X, "X", torch.float32), M, K, _dev(Xq, "Xq", torch.int8),
+                               _dev(sx, "sx", torch.float32), _stream(stream))
+    _check("a8_quantize_act", rc)
+    return Xq, sx
+
+
+def w4a8_linear(X: torch.Tensor, packed: torch.Tensor, sw: torch.Tensor, bias=None, Y=None,
+                workspace=None, stream=None) -> torch.Tensor:
+    """Y [M, N] fp32 = dequant(quant(X) . unpack(packed)) (+ bias)."""
+    M, K = X.shape
+    N = packed.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    workspace, need = _workspace(M, K, N, X.device, workspace)
+    rc = lib().w4a8_linear(_dev(X, "X", torch.float32), M, K, N,
+                           _dev(packed, "packed", torch.uint8), _dev(sw, "sw", torch.float32),
+                           _opt(bias, "bias", torch.float32), _dev(Y, "Y", torch.float32),
+                           _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                           _stream(stream))
+    _check("w4a8_linear", rc)
+    return Y
+
+
+def w4a8_linear_q(Xq: torch.Tensor, sx: torch.Tensor, packed: torch.Tensor, sw: torch.Tensor,
+                  bias=None, Y=None, workspace=None, stream=None) -> torch.Tensor:
+    M, K = Xq.shape
+    N = packed.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+    workspace, need = _workspace(M, K, N, Xq.device, workspace)
+    rc = lib().w4a8_linear_q(_dev(Xq, "Xq", torch.int8), _dev(sx, "sx", torch.float32),
+                             _dev(packed, "packed", torch.uint8), _dev(sw, "sw", torch.float32),
+                             _opt(bias, "bias", torch.float32), M, K, N,
+                             _dev(Y, "Y", torch.float32),
+                             _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                             _stream(stream))
+    _check("w4a8_linear_q", rc)
+    return Y
+
+
+def w4a8_matmul_i32(Xq: torch.Tensor, packed: torch.Tensor, acc=None, workspace=None,
+                    stream=None) -> torch.Tensor:
+    M, K = Xq.shape
+    N = packed.shape[0]
+    if acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
+    workspace, need = _workspace(M, K, N, Xq.device, workspace)
+    rc = lib().w4a8_matmul_i32(_dev(Xq, "Xq", torch.int8), _dev(packed, "packed", torch.uint8),
+                               M, K, N, _dev(acc, "acc", torch.int32),
+                               _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                               _stream(stream))
+    _check("w4a8_matmul_i32", rc)
+    return acc
+
+
+def w4a16_linear(X_bf16: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                 zeros: torch.Tensor, group_size: int, Y=None, stream=None) -> torch.Tensor:
+    """X_bf16 [M, K] (torch.bfloat16, or int16/uint16 bit patterns) -> Y [M, N] fp32."""
+    M, K = X_bf16.shape
+    N = packed.shape[0]
+    if X_bf16.dtype == torch.bfloat16:
+        xptr = _dev(X_bf16, "X_bf16", torch.bfloat16)
+    elif X_bf16.dtype == torch.int16:
+        xptr = _dev(X_bf16, "X_bf16", torch.int16)
+    else:
+        xptr = _dev(X_bf16, "X_bf16", torch.uint16)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X_bf16.device)
+    rc = lib().w4a16_linear(xptr, M, K, N, _dev(packed, "packed", torch.uint8),
+                            _dev(scales, "scales", torch.float32),
+                            _dev(zeros, "zeros", torch.float32), group_size,
+                            _dev(Y, "Y", torch.float32), _stream(stream))
+    _check("w4a16_linear", rc)
+    return Y

@@ -1,0 +1,219 @@
+// C ABI of the W4A8 / W4A16 linear layer: argument checks (pure host code,
+// before anything is launched) and dispatch to the gfx950 kernels.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/w4.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local const char *g_last_path = "none";
+
+inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? W4_OK : W4_ERR_HIP; }
+
+// Workspace layout: [Xq: M*K bytes, 256-aligned][sx: 4*M bytes, 256-aligned].
+size_t ws_bytes(int64_t M, int64_t K) {
+    return round_up((size_t)M * (size_t)K, 256) + round_up(4 * (size_t)M, 256);
+}
+
+bool shape_ok(int64_t M, int64_t K, int64_t N) {
+    if (M < 1 || K < 1 || N < 1) return false;
+    if (K > W4_MAX_K) return false;
+    const int64_t lim = (int64_t)1 << 40;
+    if (M > lim / K || N > lim / K || M > lim / N) return false;
+    return true;
+}
+
+enum class Src { FP32, Q };
+
+// Shared dispatch of the three W4A8 entry points.
+int w4a8_dispatch(Src src, const float *X, const int8_t *Xq, const float *sx,
+                  const uint8_t *packed, const float *sw, const float *bias, int64_t M,
+                  int64_t K, int64_t N, float *Y, int32_t *acc, void *workspace,
+                  size_t workspace_bytes, hipStream_t st) {
+    using namespace w4;
+    W4A8Args a{};
+    a.X = nullptr;
+    a.Xq = Xq;
+    a.sx = sx;
+    a.packed = packed;
+    a.sw = sw;
+    a.bias = bias;
+    a.Y = Y;
+    a.acc = acc;
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.out = acc ? Out::I32 : Out::Y;
+
+    const bool aligned16 = aligned(packed, 16) && (src == Src::FP32 ? aligned(X, 16) : aligned(Xq, 16));
+    const bool fast = aligned16 && (K % 128 == 0);
+    int8_t *ws_q = reinterpret_cast<int8_t *>(workspace);
+    float *ws_s = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) +
+                                            round_up((size_t)M * (size_t)K, 256));
+    hipError_t e;
+
+    // Few rows: one VALU GEMV launch (activation quantization fused).
+    if (aligned16 && gemv_dot4_ok(M, K)) {
+        if (src == Src::FP32) a.X = X;
+        g_last_path = "gemv_dot4";
+        return hip_status(launch_gemv_dot4(a, st));
+    }
+    // Activations for the MFMA paths: P8 layout in the workspace.
+    if (fast) {
+        if (src == Src::FP32) {
+            e = launch_quant_act(X, M, K, ws_q, ws_s, true, st);
+            if (e != hipSuccess) return W4_ERR_HIP;
+            a.sx = ws_s;
+        } else {
+            e = launch_to_p8(Xq, M, K, ws_q, st);
+            if (e != hipSuccess) return W4_ERR_HIP;
+        }
+        a.Xq = ws_q;
+        if (M <= 64) {
+            g_last_path = "gemv_mfma";
+            return hip_status(launch_gemv_mfma(a, st));
+        }
+        g_last_path = "gemm_mfma";
+        return hip_status(launch_gemm_mfma(a, st));
+    }
+    // Anything else: natural layout, one thread per output.
+    if (src == Src::FP32) {
+        e = launch_quant_act(X, M, K, ws_q, ws_s, false, st);
+        if (e != hipSuccess) return W4_ERR_HIP;
+        a.Xq = ws_q;
+        a.sx = ws_s;
+    }
+    g_last_path = "w4a8_generic";
+    return hip_status(launch_w4a8_generic(a, st));
+}
+
+int check_workspace(int64_t M, int64_t K, void *workspace, size_t bytes) {
+    const size_t need = ws_bytes(M, K);
+    if (need == 0) return W4_OK;
+    if (!workspace || bytes < need) return W4_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return W4_ERR_ALIGN;
+    return W4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *w4_status_string(int status) {
+    switch (status) {
+        case W4_OK: return "ok";
+        case W4_ERR_NULL: return "a required pointer is NULL";
+        case W4_ERR_SHAPE: return "invalid shape";
+        case W4_ERR_ALIGN: return "misaligned pointer";
+        case W4_ERR_SCHEME: return "unknown quantization scheme";
+        case W4_ERR_WORKSPACE: return "workspace missing or too small";
+        case W4_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *w4_last_path(void) { return g_last_path; }
+
+int w4_quantize_weight(const float *W, int64_t K, int64_t N, int scheme, int64_t group_size,
+                       uint8_t *packed, float *scales, float *zeros, void *stream) {
+    if (!W || !packed || !scales) return W4_ERR_NULL;
+    if (!shape_ok(1, K, N)) return W4_ERR_SHAPE;
+    if (!aligned(W, 4) || !aligned(scales, 4)) return W4_ERR_ALIGN;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (scheme == W4_SYM_PER_CHANNEL) {
+        if (group_size != 0 || zeros) return W4_ERR_SHAPE;
+        g_last_path = "quant_weight_sym";
+        return hip_status(w4::launch_quant_weight_sym(W, K, N, packed, scales, st));
+    }
+    if (scheme == W4_ASYM_GROUP) {
+        if (!zeros) return W4_ERR_NULL;
+        if (!aligned(zeros, 4)) return W4_ERR_ALIGN;
+        if (group_size < 2 || group_size % 2 != 0 || K % group_size != 0) return W4_ERR_SHAPE;
+        if (K / group_size > 65535) return W4_ERR_SHAPE;
+        g_last_path = "quant_weight_asym";
+        return hip_status(
+            w4::launch_quant_weight_asym(W, K, N, group_size, packed, scales, zeros, st));
+    }
+    return W4_ERR_SCHEME;
+}
+
+int a8_quantize_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx, void *stream) {
+    if (!X || !Xq || !sx) return W4_ERR_NULL;
+    if (M < 1 || K < 1 || M > 0x7FFFFFFF || K > ((int64_t)1 << 40) / M) return W4_ERR_SHAPE;
+    if (!aligned(X, 4) || !aligned(sx, 4)) return W4_ERR_ALIGN;
+    g_last_path = "quant_act";
+    return hip_status(
+        w4::launch_quant_act(X, M, K, Xq, sx, false, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t w4a8_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (!shape_ok(M, K, N)) return 0;
+    return ws_bytes(M, K);
+}
+
+int w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N, const uint8_t *packed,
+                const float *sw, const float *bias, float *Y, void *workspace,
+                size_t workspace_bytes, void *stream) {
+    if (!X || !packed || !sw || !Y) return W4_ERR_NULL;
+    if (!shape_ok(M, K, N)) return W4_ERR_SHAPE;
+    if (!aligned(X, 4) || !aligned(sw, 4) || !aligned(Y, 4) || (bias && !aligned(bias, 4)))
+        return W4_ERR_ALIGN;
+    int rc = check_workspace(M, K, workspace, workspace_bytes);
+    if (rc != W4_OK) return rc;
+    return w4a8_dispatch(Src::FP32, X, nullptr, nullptr, packed, sw, bias, M, K, N, Y, nullptr,
+                         workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+int w4a8_linear_q(const int8_t *Xq, const float *sx, const uint8_t *packed, const float *sw,
+                  const float *bias, int64_t M, int64_t K, int64_t N, float *Y, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    if (!Xq || !sx || !packed || !sw || !Y) return W4_ERR_NULL;
+    if (!shape_ok(M, K, N)) return W4_ERR_SHAPE;
+    if (!aligned(sx, 4) || !aligned(sw, 4) || !aligned(Y, 4) || (bias && !aligned(bias, 4)))
+        return W4_ERR_ALIGN;
+    int rc = check_workspace(M, K, workspace, workspace_bytes);
+    if (rc != W4_OK) return rc;
+    return w4a8_dispatch(Src::Q, nullptr, Xq, sx, packed, sw, bias, M, K, N, Y, nullptr,
+                         workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+int w4a8_matmul_i32(const int8_t *Xq, const uint8_t *packed, int64_t M, int64_t K, int64_t N,
+                    int32_t *acc, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!Xq || !packed || !acc) return W4_ERR_NULL;
+    if (!shape_ok(M, K, N)) return W4_ERR_SHAPE;
+    if (!aligned(acc, 4)) return W4_ERR_ALIGN;
+    int rc = check_workspace(M, K, workspace, workspace_bytes);
+    if (rc != W4_OK) return rc;
+    return w4a8_dispatch(Src::Q, nullptr, Xq, nullptr, packed, nullptr, nullptr, M, K, N,
+                         nullptr, acc, workspace, workspace_bytes,
+                         reinterpret_cast<hipStream_t>(stream));
+}
+
+int w4a16_linear(const uint16_t *X_bf16, int64_t M, int64_t K, int64_t N, const uint8_t *packed,
+                 const float *scales, const float *zeros, int64_t group_size, float *Y,
+                 void *stream) {
+    if (!X_bf16 || !packed || !scales || !zeros || !Y) return W4_ERR_NULL;
+    if (!shape_ok(M, K, N)) return W4_ERR_SHAPE;
+    if (group_size < 2 || group_size % 2 != 0 || K % group_size != 0) return W4_ERR_SHAPE;
+    if (!aligned(X_bf16, 2) || !aligned(scales, 4) || !aligned(zeros, 4) || !aligned(Y, 4))
+        return W4_ERR_ALIGN;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (w4::w4a16_fast_ok(M, K, N, group_size) && aligned(X_bf16, 16) && aligned(packed, 16)) {
+        g_last_path = "w4a16_mfma";
+        return hip_status(
+            w4::launch_w4a16_mfma(X_bf16, M, K, N, packed, scales, zeros, group_size, Y, st));
+    }
+    g_last_path = "w4a16_generic";
+    return hip_status(
+        w4::launch_w4a16_generic(X_bf16, M, K, N, packed, scales, zeros, group_size, Y, st));
+}
+
+}  // extern "C"

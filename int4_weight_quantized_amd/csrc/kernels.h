@@ -1,0 +1,58 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+// Shapes and pointers are validated by the C ABI layer before any launcher
+// runs; each launcher only enqueues work on `st` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+// Which accumulation product a W4A8 kernel writes.
+enum class Out { Y, I32 };
+
+struct W4A8Args {
+    const float *X;       // fp32 activations [M][K] (fused quantization) or NULL
+    const int8_t *Xq;     // int8 activations, natural or P8 layout, or NULL
+    const float *sx;      // [M] activation scales (with Xq)
+    const uint8_t *packed;
+    const float *sw;
+    const float *bias;
+    float *Y;
+    int32_t *acc;
+    int64_t M, K, N;
+    Out out;
+};
+
+hipError_t launch_quant_weight_sym(const float *W, int64_t K, int64_t N, uint8_t *packed,
+                                   float *sw, hipStream_t st);
+hipError_t launch_quant_weight_asym(const float *W, int64_t K, int64_t N, int64_t group,
+                                    uint8_t *packed, float *scales, float *zeros, hipStream_t st);
+hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx, bool p8,
+                            hipStream_t st);
+hipError_t launch_to_p8(const int8_t *Xq, int64_t M, int64_t K, int8_t *out, hipStream_t st);
+
+// M <= 4, K % 32 == 0, 16-byte aligned: VALU dot4 GEMV.  Uses a.X (fused
+// quantization prologue) when non-NULL, else a.Xq (natural layout) + a.sx.
+bool gemv_dot4_ok(int64_t M, int64_t K);
+hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st);
+
+// M <= 64, K % 128 == 0: MFMA GEMV; a.Xq in P8 layout.
+hipError_t launch_gemv_mfma(const W4A8Args &a, hipStream_t st);
+
+// Any M, K % 128 == 0: LDS-tiled MFMA GEMM; a.Xq in P8 layout.
+hipError_t launch_gemm_mfma(const W4A8Args &a, hipStream_t st);
+
+// Any shape: one thread per output, natural-layout a.Xq.
+hipError_t launch_w4a8_generic(const W4A8Args &a, hipStream_t st);
+
+// W4A16.
+bool w4a16_fast_ok(int64_t M, int64_t K, int64_t N, int64_t group);
+hipError_t launch_w4a16_mfma(const uint16_t *X, int64_t M, int64_t K, int64_t N,
+                             const uint8_t *packed, const float *scales, const float *zeros,
+                             int64_t group, float *Y, hipStream_t st);
+hipError_t launch_w4a16_generic(const uint16_t *X, int64_t M, int64_t K, int64_t N,
+                                const uint8_t *packed, const float *scales, const float *zeros,
+                                int64_t group, float *Y, hipStream_t st);
+
+}  // namespace w4

@@ -1,0 +1,280 @@
+// Quantization kernels: symmetric per-channel int4 weights, asymmetric
+// group-wise int4 weights and per-row dynamic int8 activations.
+//
+// Symmetric weights (Keras INT4 guide, "How it works", steps 1-2):
+//   scale[n] = fl(max_k |W[k][n]| / 7), code = clamp(rne(fl(W / scale)), -8, 7).
+// Asymmetric groups ("4-bit Integer Quantization for LLMs", quantization
+// principle; "INT4" concept entry 4.1-4.2):
+//   scale = fl(fl(max - min) / 15), zero = 0 - rne(fl(min / scale)),
+//   code = clamp(rne(fl(W / scale)) + zero, 0, 15).
+// Activations (Keras guide step 3): sx[m] = fl(max_k |X[m][k]| / 127),
+//   Xq = clamp(rne(fl(X / sx)), -128, 127).
+#include "common.h"
+#include "kernels.h"
+
+namespace w4 {
+
+// ------------------------------------------------------------------ helpers
+__global__ void k_fill_u32(uint32_t *p, int64_t n, uint32_t v) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// ---------------------------------------------------- symmetric int4 weights
+// Pass 1: per-column absmax of a [krows x 64] slab, merged with an atomic max
+// on the fp32 bit pattern (valid because every value is >= +0).
+// Block: 256 threads = 64 columns x 4 row phases.
+__global__ __launch_bounds__(256) void k_absmax_cols(const float *__restrict__ W, int64_t K,
+                                                     int64_t N, int64_t krows,
+                                                     uint32_t *__restrict__ amax) {
+    __shared__ float red[4][64];
+    const int c = threadIdx.x % 64, ph = threadIdx.x / 64;
+    const int64_t col = (int64_t)blockIdx.x * 64 + c;
+    const int64_t k0 = (int64_t)blockIdx.y * krows;
+    const int64_t k1 = min(K, k0 + krows);
+    float m = 0.0f;
+    if (col < N) {
+        for (int64_t k = k0 + ph; k < k1; k += 4) m = fmaxf(m, fabsf(W[k * N + col]));
+    }
+    red[ph][c] = m;
+    __syncthreads();
+    if (ph == 0 && col < N) {
+        m = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
+        atomicMax(&amax[col], __float_as_uint(m));
+    }
+}
+
+// Pass 2: codes of a [128 x 64] tile.  Thread (c, part) owns column c and the
+// 16 bytes (32 k) part*16 .. part*16+15 of the tile; loads are coalesced over
+// the 64 columns of a wave.  `amax` still holds absmax bits here.
+__global__ __launch_bounds__(256) void k_quant_sym_tile(const float *__restrict__ W, int64_t K,
+                                                        int64_t N,
+                                                        const uint32_t *__restrict__ amax,
+                                                        uint8_t *__restrict__ packed) {
+    const int c = threadIdx.x % 64, part = threadIdx.x / 64;
+    const int64_t col = (int64_t)blockIdx.x * 64 + c;
+    if (col >= N) return;
+    const int64_t KB = (K + 1) / 2;
+    const float a = __uint_as_float(amax[col]);
+    const float s = (a == 0.0f) ? 0.0f : a / 7.0f;
+    const int64_t kbeg = (int64_t)blockIdx.y * 128 + part * 32;  // even
+    uint8_t bytes[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int64_t k = kbeg + 2 * j;
+        int q0 = 0, q1 = 0;
+        if (k < K) q0 = quant_code(W[k * N + col], s, -8.0f, 7.0f);
+        if (k + 1 < K) q1 = quant_code(W[(k + 1) * N + col], s, -8.0f, 7.0f);
+        bytes[j] = (uint8_t)((q0 & 0xF) | ((q1 & 0xF) << 4));
+    }
+    const int64_t b0 = kbeg / 2;
+    uint8_t *dst = packed + col * KB + b0;
+    if ((KB % 16) == 0 && b0 + 16 <= KB) {
+        uint4 v;
+        v.x = bytes[0] | (bytes[1] << 8) | (bytes[2] << 16) | ((uint32_t)bytes[3] << 24);
+        v.y = bytes[4] | (bytes[5] << 8) | (bytes[6] << 16) | ((uint32_t)bytes[7] << 24);
+        v.z = bytes[8] | (bytes[9] << 8) | (bytes[10] << 16) | ((uint32_t)bytes[11] << 24);
+        v.w = bytes[12] | (bytes[13] << 8) | (bytes[14] << 16) | ((uint32_t)bytes[15] << 24);
+        *reinterpret_cast<uint4 *>(dst) = v;
+    } else {
+        for (int j = 0; j < 16; ++j)
+            if (b0 + j < KB) dst[j] = bytes[j];
+    }
+}
+
+// Pass 3: absmax bits -> scale, in place.
+__global__ void k_finalize_sym_scales(uint32_t *__restrict__ amax_to_scale, int64_t N) {
+    int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= N) return;
+    float a = __uint_as_float(amax_to_scale[n]);
+    float s = (a == 0.0f) ? 0.0f : a / 7.0f;
+    reinterpret_cast<float *>(amax_to_scale)[n] = s;
+}
+
+hipError_t launch_quant_weight_sym(const float *W, int64_t K, int64_t N, uint8_t *packed,
+                                   float *sw, hipStream_t st) {
+    uint32_t *amax = reinterpret_cast<uint32_t *>(sw);
+    hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, amax, N,
+                       0u);
+    const int64_t krows = 256;
+    dim3 g1((unsigned)((N + 63) / 64), (unsigned)((K + krows - 1) / krows));
+    hipLaunchKernelGGL(k_absmax_cols, g1, dim3(256), 0, st, W, K, N, krows, amax);
+    dim3 g2((unsigned)((N + 63) / 64), (unsigned)((K + 127) / 128));
+    hipLaunchKernelGGL(k_quant_sym_tile, g2, dim3(256), 0, st, W, K, N, amax, packed);
+    hipLaunchKernelGGL(k_finalize_sym_scales, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st,
+                       amax, N);
+    return hipGetLastError();
+}
+
+// --------------------------------------------------- asymmetric group int4
+// One block per (64 columns, one group).  Thread (c, part): column c, a
+// contiguous quarter of the group's byte pairs.  The group size is even.
+__global__ __launch_bounds__(256) void k_quant_asym(const float *__restrict__ W, int64_t K,
+                                                    int64_t N, int64_t group,
+                                                    uint8_t *__restrict__ packed,
+                                                    float *__restrict__ scales,
+                                                    float *__restrict__ zeros) {
+    __shared__ float rlo[4][64], rhi[4][64];
+    const int c = threadIdx.x % 64, part = threadIdx.x / 64;
+    const int64_t col = (int64_t)blockIdx.x * 64 + c;
+    const int64_t g = blockIdx.y;
+    const int64_t G = K / group;
+    const int64_t k0 = g * group;
+    float lo = 0.0f, hi = 0.0f;
+    if (col < N) {
+        lo = hi = W[k0 * N + col];
+        for (int64_t k = k0 + part; k < k0 + group; k += 4) {
+            float w = W[k * N + col];
+            lo = fminf(lo, w);
+            hi = fmaxf(hi, w);
+        }
+    }
+    rlo[part][c] = lo;
+    rhi[part][c] = hi;
+    __syncthreads();
+    if (col >= N) return;
+    lo = fminf(fminf(rlo[0][c], rlo[1][c]), fminf(rlo[2][c], rlo[3][c]));
+    hi = fmaxf(fmaxf(rhi[0][c], rhi[1][c]), fmaxf(rhi[2][c], rhi[3][c]));
+    float s;
+    if (hi > lo) {
+        float range = hi - lo;
+        s = range / 15.0f;
+    } else {
+        s = (lo != 0.0f) ? fabsf(lo) : 1.0f;
+    }
+    const float zp = 0.0f - rintf(lo / s);
+    if (part == 0) {
+        scales[col * G + g] = s;
+        zeros[col * G + g] = zp;
+    }
+    const int64_t KB = (K + 1) / 2;
+    const int64_t npairs = group / 2;
+    const int64_t per = (npairs + 3) / 4;
+    const int64_t p0 = part * per, p1 = min(npairs, p0 + per);
+    uint8_t *dst = packed + col * KB + k0 / 2;
+    const bool vec = (per % 16 == 0) && (KB % 16 == 0) && ((k0 / 2) % 16 == 0);
+    for (int64_t p = p0; p < p1; p += 16) {
+        uint8_t bytes[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int64_t pp = p + j;
+            uint8_t b = 0;
+            if (pp < p1) {
+                const int64_t k = k0 + 2 * pp;
+                float r0 = rintf(W[k * N + col] / s) + zp;
+                float r1 = rintf(W[(k + 1) * N + col] / s) + zp;
+                int q0 = (int)fminf(fmaxf(r0, 0.0f), 15.0f);
+                int q1 = (int)fminf(fmaxf(r1, 0.0f), 15.0f);
+                b = (uint8_t)(q0 | (q1 << 4));
+            }
+            bytes[j] = b;
+        }
+        if (vec && p + 16 <= p1) {
+            uint4 v;
+            v.x = bytes[0] | (bytes[1] << 8) | (bytes[2] << 16) | ((uint32_t)bytes[3] << 24);
+            v.y = bytes[4] | (bytes[5] << 8) | (bytes[6] << 16) | ((uint32_t)bytes[7] << 24);
+            v.z = bytes[8] | (bytes[9] << 8) | (bytes[10] << 16) | ((uint32_t)bytes[11] << 24);
+            v.w = bytes[12] | (bytes[13] << 8) | (bytes[14] << 16) | ((uint32_t)bytes[15] << 24);
+            *reinterpret_cast<uint4 *>(dst + p) = v;
+        } else {
+            for (int j = 0; j < 16 && p + j < p1; ++j) dst[p + j] = bytes[j];
+        }
+    }
+}
+
+hipError_t launch_quant_weight_asym(const float *W, int64_t K, int64_t N, int64_t group,
+                                    uint8_t *packed, float *scales, float *zeros, hipStream_t st) {
+    dim3 g((unsigned)((N + 63) / 64), (unsigned)(K / group));
+    hipLaunchKernelGGL(k_quant_asym, g, dim3(256), 0, st, W, K, N, group, packed, scales, zeros);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------ int8 activations
+// One block (256 threads) per row.  Pass 1: absmax; pass 2: codes, 8 per
+// thread-step (re-reading the row from cache).  P8 = true writes the P8 layout
+// (requires K % 8 == 0), otherwise the natural layout.
+template <bool P8>
+__global__ __launch_bounds__(256) void k_quant_act(const float *__restrict__ X, int64_t K,
+                                                   int8_t *__restrict__ Xq,
+                                                   float *__restrict__ sx) {
+    __shared__ float red[4];
+    const int64_t m = blockIdx.x;
+    const float *row = X + m * K;
+    const bool vec = ((K % 4) == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+    float a = 0.0f;
+    if (vec) {
+        const float4 *r4 = reinterpret_cast<const float4 *>(row);
+        for (int64_t i = threadIdx.x; i < K / 4; i += 256) {
+            float4 v = r4[i];
+            a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+    } else {
+        for (int64_t i = threadIdx.x; i < K; i += 256) a = fmaxf(a, fabsf(row[i]));
+    }
+    a = block_max(a, red);
+    const float s = (a == 0.0f) ? 0.0f : a / 127.0f;
+    if (threadIdx.x == 0) sx[m] = s;
+    int8_t *out = Xq + m * K;
+    const int64_t ng = (K + 7) / 8;
+    for (int64_t g = threadIdx.x; g < ng; g += 256) {
+        const int64_t k0 = g * 8;
+        int q[8];
+        if (vec && k0 + 8 <= K) {
+            const float4 v0 = reinterpret_cast<const float4 *>(row + k0)[0];
+            const float4 v1 = reinterpret_cast<const float4 *>(row + k0)[1];
+            q[0] = quant_code(v0.x, s, -128.f, 127.f);
+            q[1] = quant_code(v0.y, s, -128.f, 127.f);
+            q[2] = quant_code(v0.z, s, -128.f, 127.f);
+            q[3] = quant_code(v0.w, s, -128.f, 127.f);
+            q[4] = quant_code(v1.x, s, -128.f, 127.f);
+            q[5] = quant_code(v1.y, s, -128.f, 127.f);
+            q[6] = quant_code(v1.z, s, -128.f, 127.f);
+            q[7] = quant_code(v1.w, s, -128.f, 127.f);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                q[j] = (k0 + j < K) ? quant_code(row[k0 + j], s, -128.f, 127.f) : 0;
+        }
+        if (P8) {
+            uint2 v;
+            v.x = pack4_i8(q[0], q[2], q[4], q[6]);
+            v.y = pack4_i8(q[1], q[3], q[5], q[7]);
+            *reinterpret_cast<uint2 *>(out + k0) = v;
+        } else if ((K % 8) == 0 && (reinterpret_cast<uintptr_t>(Xq) & 7) == 0) {
+            uint2 v;
+            v.x = pack4_i8(q[0], q[1], q[2], q[3]);
+            v.y = pack4_i8(q[4], q[5], q[6], q[7]);
+            *reinterpret_cast<uint2 *>(out + k0) = v;
+        } else {
+            for (int j = 0; j < 8 && k0 + j < K; ++j) out[k0 + j] = (int8_t)q[j];
+        }
+    }
+}
+
+hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx, bool p8,
+                            hipStream_t st) {
+    if (p8)
+        hipLaunchKernelGGL(k_quant_act<true>, dim3((unsigned)M), dim3(256), 0, st, X, K, Xq, sx);
+    else
+        hipLaunchKernelGGL(k_quant_act<false>, dim3((unsigned)M), dim3(256), 0, st, X, K, Xq, sx);
+    return hipGetLastError();
+}
+
+// Natural int8 [M][K] -> P8 layout (K % 8 == 0, 8-byte aligned input).
+__global__ void k_to_p8(const int8_t *__restrict__ in, int64_t total8, int8_t *__restrict__ out) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total8) return;
+    uint2 v = reinterpret_cast<const uint2 *>(in)[i];
+    uint2 r;
+    natural_to_p8(v.x, v.y, r.x, r.y);
+    reinterpret_cast<uint2 *>(out)[i] = r;
+}
+
+hipError_t launch_to_p8(const int8_t *Xq, int64_t M, int64_t K, int8_t *out, hipStream_t st) {
+    const int64_t total8 = M * K / 8;
+    hipLaunchKernelGGL(k_to_p8, dim3((unsigned)((total8 + 255) / 256)), dim3(256), 0, st, Xq,
+                       total8, out);
+    return hipGetLastError();
+}
+
+}  // namespace w4

@@ -1,0 +1,182 @@
+// Weight-only W4A16 product: unsigned int4 codes with a scale and zero point
+// per group of K ("4-bit Integer Quantization for LLMs": activations stay
+// 16-bit, weights are dequantized at compute time; "INT4" concept entry 4.5,
+// schemes A and C).  Each weight is dequantized in registers to
+//   w' = bf16_rne(fl((q - zero) * scale))
+// and fed to v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
+//
+// Block = 4 waves that split K into quarters and cover 16*NB output channels
+// for 16 activation rows.  Per 128-k step a lane loads 16 packed bytes of one
+// channel (codes k = 128*s + 32*(l/16) + [0, 32)) and the matching 32 bf16
+// activations of row l%16; the 32 codes feed four MFMAs of 8 codes each.
+//
+// Dequantization in 25 VALU operations per 8 codes: for a zero point z in
+// [-112, 128] the byte 128 + q - z never leaves [0, 255], so one integer add
+// per 4 codes forms it in place, v_cvt_f32_ubyte turns it into a float v, and
+//   fma(v, s, -128*s) = fl((v - 128) * s) = fl((q - z) * s)
+// exactly (one rounding of the exact product; 128*s is exact).  Other groups
+// take the direct fl(fl(q - z) * s).
+#include "common.h"
+#include "kernels.h"
+
+namespace w4 {
+
+bool w4a16_fast_ok(int64_t M, int64_t K, int64_t N, int64_t group) {
+    (void)M;
+    (void)N;
+    return K % 128 == 0 && group % 32 == 0;
+}
+
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+    const bf16x2 v = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// 8 codes of one packed dword -> 4 dwords of bf16 pairs in natural k order.
+__device__ __forceinline__ v4i dequant8(uint32_t w, float s, float zp, uint32_t cadd, float nbias,
+                                        bool fast) {
+    const uint32_t lo = w & 0x0F0F0F0Fu;         // codes k = 0, 2, 4, 6
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes k = 1, 3, 5, 7
+    float fl[4], fh[4];
+    if (fast) {
+        const uint32_t lb = lo + cadd, hb = hi + cadd;  // bytes 128 + q - z
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            fl[i] = fmaf((float)((lb >> (8 * i)) & 0xFFu), s, nbias);
+            fh[i] = fmaf((float)((hb >> (8 * i)) & 0xFFu), s, nbias);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float dl = (float)((lo >> (8 * i)) & 0xFFu) - zp;
+            const float dh = (float)((hi >> (8 * i)) & 0xFFu) - zp;
+            fl[i] = dl * s;
+            fh[i] = dh * s;
+        }
+    }
+    return v4i{(int)pk_bf16(fl[0], fh[0]), (int)pk_bf16(fl[1], fh[1]), (int)pk_bf16(fl[2], fh[2]),
+               (int)pk_bf16(fl[3], fh[3])};
+}
+
+template <int NB, int D>
+__global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t *__restrict__ X,
+                                                    const uint8_t *__restrict__ packed,
+                                                    const float *__restrict__ scales,
+                                                    const float *__restrict__ zeros,
+                                                    float *__restrict__ Y, int64_t M, int64_t K,
+                                                    int64_t N, int64_t group) {
+    __shared__ v4f red[3][NB][kWave];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int r16 = lane % 16, kq = lane / 16;
+    const int64_t KB = K / 2, G = K / group;
+    const int64_t S = K / 128;
+    const int64_t s0 = S * wave / 4, s1 = S * (wave + 1) / 4;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * NB;
+    const int64_t m0 = (int64_t)blockIdx.y * 16;
+
+    const uint8_t *bp[NB];
+    const float *sp[NB], *zpp[NB];
+    bool bv[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t col = n0 + 16 * nb + r16;
+        bv[nb] = col < N;
+        const int64_t c = bv[nb] ? col : 0;
+        bp[nb] = packed + c * KB + kq * 16;
+        sp[nb] = scales + c * G;
+        zpp[nb] = zeros + c * G;
+    }
+    const int64_t row = m0 + r16;
+    const bool xv = row < M;
+    const uint16_t *xp = X + (xv ? row : 0) * K + kq * 32;
+
+    v4f acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    uint4 wbuf[D][NB];
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            wbuf[d][nb] = (s0 + d < s1 && bv[nb])
+                              ? *reinterpret_cast<const uint4 *>(bp[nb] + (s0 + d) * 64)
+                              : make_uint4(0, 0, 0, 0);
+
+    for (int64_t s = s0; s < s1; s += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int64_t ss = s + d;
+            if (ss < s1) {
+                uint4 xa[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    xa[q] = xv ? reinterpret_cast<const uint4 *>(xp + ss * 128)[q]
+                               : make_uint4(0, 0, 0, 0);
+                const int64_t g = (ss * 128 + kq * 32) / group;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const uint4 w = wbuf[d][nb];
+                    const int64_t sn = ss + D;
+                    wbuf[d][nb] = (sn < s1 && bv[nb])
+                                      ? *reinterpret_cast<const uint4 *>(bp[nb] + sn * 64)
+                                      : make_uint4(0, 0, 0, 0);
+                    const float sc = sp[nb][g];
+                    const float zp = zpp[nb][g];
+                    const bool ok = (zp >= -112.0f) && (zp <= 128.0f) && (fabsf(sc) < 0x1p100f);
+                    // wave-uniform choice, so only one of the two paths executes
+                    const bool fast = __all(ok) != 0;
+                    const uint32_t cb = ok ? (uint32_t)(128 - (int)zp) : 0u;
+                    const uint32_t cadd = cb * 0x01010101u;
+                    const float nbias = -128.0f * sc;
+                    const v4i b0 = dequant8(w.x, sc, zp, cadd, nbias, fast);
+                    const v4i b1 = dequant8(w.y, sc, zp, cadd, nbias, fast);
+                    const v4i b2 = dequant8(w.z, sc, zp, cadd, nbias, fast);
+                    const v4i b3 = dequant8(w.w, sc, zp, cadd, nbias, fast);
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(v8bf, xa[0]), __builtin_bit_cast(v8bf, b0), acc[nb], 0, 0, 0);
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(v8bf, xa[1]), __builtin_bit_cast(v8bf, b1), acc[nb], 0, 0, 0);
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(v8bf, xa[2]), __builtin_bit_cast(v8bf, b2), acc[nb], 0, 0, 0);
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(v8bf, xa[3]), __builtin_bit_cast(v8bf, b3), acc[nb], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    if (wave > 0) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) red[wave - 1][nb][lane] = acc[nb];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const v4f t = acc[nb] + red[0][nb][lane] + red[1][nb][lane] + red[2][nb][lane];
+        const int64_t col = n0 + 16 * nb + r16;
+        if (col >= N) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t r = m0 + 4 * kq + i;
+            if (r < M) Y[r * N + col] = t[i];
+        }
+    }
+}
+
+hipError_t launch_w4a16_mfma(const uint16_t *X, int64_t M, int64_t K, int64_t N,
+                             const uint8_t *packed, const float *scales, const float *zeros,
+                             int64_t group, float *Y, hipStream_t st) {
+    constexpr int NB = 4, D = 2;
+    const int64_t mblocks = (M + 15) / 16;
+    for (int64_t mb0 = 0; mb0 < mblocks; mb0 += 65535) {
+        const int64_t cnt = (mblocks - mb0) < 65535 ? (mblocks - mb0) : 65535;
+        dim3 grid((unsigned)((N + 16 * NB - 1) / (16 * NB)), (unsigned)cnt);
+        hipLaunchKernelGGL((k_w4a16_mfma<NB, D>), grid, dim3(256), 0, st, X + mb0 * 16 * K, packed,
+                           scales, zeros, Y + mb0 * 16 * N, M - mb0 * 16, K, N, group);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace w4

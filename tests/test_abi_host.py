@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+* libw4.so loads and exports every function include/w4.h declares;
+* every argument check returns its documented status before any launch
+  (NULL pointers, bad sizes, unknown scheme, misaligned pointers, missing or
+  short workspace);
+* the workspace size formula.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4.h")
+
+W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_SCHEME, W4_ERR_WORKSPACE, W4_ERR_HIP = (
+    0, -1, -2, -3, -4, -5, -6)
+FAKE = 1 << 20  # a non-NULL, 256-aligned address; never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s*([a-z][a-z0-9_]*)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def w4():
+    import int4_weight_quantized_amd as pkg
+    if not os.path.exists(pkg.LIB_PATH):
+        pkg_build = __import__("int4_weight_quantized_amd.build", fromlist=["build"])
+        pkg_build.build()
+    return pkg
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["w4_quantize_weight", "a8_quantize_act", "w4a8_linear", "w4a16_linear",
+                 "w4a8_linear_q", "w4a8_matmul_i32", "w4a8_workspace_bytes",
+                 "w4_status_string", "w4_last_path"]:
+        assert want in names, names
+
+
+def test_library_exports_every_declared_symbol(w4):
+    lib = w4.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libw4.so does not export {name}"
+
+
+def test_status_strings(w4):
+    for st in range(-6, 1):
+        assert w4.w4_status_string(st) and w4.w4_status_string(st) != "unknown status"
+    assert w4.w4_status_string(-99) == "unknown status"
+
+
+def test_workspace_formula(w4):
+    assert w4.w4a8_workspace_bytes(1, 1152, 6912) == 1280 + 256
+    assert w4.w4a8_workspace_bytes(4096, 4096, 4096) == 4096 * 4096 + 16384
+    assert w4.w4a8_workspace_bytes(0, 4096, 4096) == 0
+    assert w4.w4a8_workspace_bytes(1, w4.W4_MAX_K + 1, 1) == 0
+
+
+def test_quantize_weight_checks(w4):
+    f = w4.lib().w4_quantize_weight
+    assert f(None, 4, 4, 0, 0, FAKE, FAKE, None, None) == W4_ERR_NULL
+    assert f(FAKE, 4, 4, 0, 0, None, FAKE, None, None) == W4_ERR_NULL
+    assert f(FAKE, 0, 4, 0, 0, FAKE, FAKE, None, None) == W4_ERR_SHAPE
+    assert f(FAKE, 4, -1, 0, 0, FAKE, FAKE, None, None) == W4_ERR_SHAPE
+    assert f(FAKE, w4.W4_MAX_K + 1, 4, 0, 0, FAKE, FAKE, None, None) == W4_ERR_SHAPE
+    assert f(FAKE + 2, 4, 4, 0, 0, FAKE, FAKE, None, None) == W4_ERR_ALIGN
+    assert f(FAKE, 4, 4, 7, 0, FAKE, FAKE, None, None) == W4_ERR_SCHEME
+    assert f(FAKE, 4, 4, 0, 128, FAKE, FAKE, None, None) == W4_ERR_SHAPE    # sym takes no group
+    assert f(FAKE, 4, 4, 0, 0, FAKE, FAKE, FAKE, None) == W4_ERR_SHAPE      # sym takes no zeros
+    assert f(FAKE, 256, 4, 1, 128, FAKE, FAKE, None, None) == W4_ERR_NULL   # asym needs zeros
+    assert f(FAKE, 200, 4, 1, 128, FAKE, FAKE, FAKE, None) == W4_ERR_SHAPE  # K % group
+    assert f(FAKE, 9, 4, 1, 3, FAKE, FAKE, FAKE, None) == W4_ERR_SHAPE      # odd group
+    assert f(FAKE, 256, 4, 1, 128, FAKE, FAKE, FAKE + 1, None) == W4_ERR_ALIGN
+
+
+def test_act_checks(w4):
+    f = w4.lib().a8_quantize_act
+    assert f(None, 1, 4, FAKE, FAKE, None) == W4_ERR_NULL
+    assert f(FAKE, 0, 4, FAKE, FAKE, None) == W4_ERR_SHAPE
+    assert f(FAKE, 2, 0, FAKE, FAKE, None) == W4_ERR_SHAPE
+    assert f(FAKE + 1, 2, 4, FAKE, FAKE, None) == W4_ERR_ALIGN
+
+
+def test_linear_checks(w4):
+    f = w4.lib().w4a8_linear
+    ws = w4.w4a8_workspace_bytes(2, 64, 8)
+    assert f(None, 2, 64, 8, FAKE, FAKE, None, FAKE, FAKE, ws, None) == W4_ERR_NULL
+    assert f(FAKE, 2, 64, 8, FAKE, None, None, FAKE, FAKE, ws, None) == W4_ERR_NULL
+    assert f(FAKE, 2, 0, 8, FAKE, FAKE, None, FAKE, FAKE, ws, None) == W4_ERR_SHAPE
+    assert f(FAKE, 2, 64, 8, FAKE, FAKE, None, FAKE + 2, FAKE, ws, None) == W4_ERR_ALIGN
+    assert f(FAKE, 2, 64, 8, FAKE, FAKE, FAKE + 1, FAKE, FAKE, ws, None) == W4_ERR_ALIGN
+    assert f(FAKE, 2, 64, 8, FAKE, FAKE, None, FAKE, None, 0, None) == W4_ERR_WORKSPACE
+    assert f(FAKE, 2, 64, 8, FAKE, FAKE, None, FAKE, FAKE, ws - 1, None) == W4_ERR_WORKSPACE
+    assert f(FAKE, 2, 64, 8, FAKE, FAKE, None, FAKE, FAKE + 16, ws, None) == W4_ERR_ALIGN
+    g = w4.lib().w4a8_linear_q
+    assert g(FAKE, None, FAKE, FAKE, None, 2, 64, 8, FAKE, FAKE, ws, None) == W4_ERR_NULL
+    assert g(FAKE, FAKE, FAKE, FAKE, None, 2, 64, -8, FAKE, FAKE, ws, None) == W4_ERR_SHAPE
+    h = w4.lib().w4a8_matmul_i32
+    assert h(FAKE, FAKE, 2, 64, 8, None, FAKE, ws, None) == W4_ERR_NULL
+    assert h(FAKE, FAKE, 2, 64, 8, FAKE + 2, FAKE, ws, None) == W4_ERR_ALIGN
+    assert h(FAKE, FAKE, 2, 64, 8, FAKE, FAKE, 3, None) == W4_ERR_WORKSPACE
+
+
+def test_w4a16_checks(w4):
+    f = w4.lib().w4a16_linear
+    assert f(None, 1, 256, 8, FAKE, FAKE, FAKE, 128, FAKE, None) == W4_ERR_NULL
+    assert f(FAKE, 1, 256, 8, FAKE, FAKE, None, 128, FAKE, None) == W4_ERR_NULL
+    assert f(FAKE, 1, 200, 8, FAKE, FAKE, FAKE, 128, FAKE, None) == W4_ERR_SHAPE
+    assert f(FAKE, 1, 256, 8, FAKE, FAKE, FAKE, 0, FAKE, None) == W4_ERR_SHAPE
+    assert f(FAKE + 1, 1, 256, 8, FAKE, FAKE, FAKE, 128, FAKE, None) == W4_ERR_ALIGN
+
+
+def test_binding_refuses_cpu_tensors(w4):
+    import torch
+    with pytest.raises(ValueError):
+        w4.a8_quantize_act(torch.zeros(2, 8))

@@ -1,0 +1,322 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar: bit-exact on codes, packed bytes, scales, zero points, int8 activations,
+int32 accumulators and W4A8 outputs (the W4A8 output is a fixed sequence of
+fp32 roundings, so it must match bit for bit, which is stricter than the
+1e-5 relative bound).  W4A16 outputs: fp32 accumulation in hardware order is
+one of several correct results, so they are checked norm-wise
+(||y - y_ref||_2 <= 1e-5 ||y_ref||_2) and element-wise against the fp32
+summation bound |y - y_ref| <= gamma_K * sum_k |x_k w'_k| with
+gamma_K = K u / (1 - K u), u = 2^-24.
+
+Small cases run the oracle on the whole problem; full-size workloads run the
+HIP path on the whole problem (in the launch configuration the benchmark
+uses) and compare sampled rows / channels the oracle computes one by one
+(rows of the W4A8 layer and channels of both layers are independent).
+Output buffers sit between canary guard regions.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+W4 = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def w4():
+    global W4
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import int4_weight_quantized_amd as pkg
+    pkg.lib()
+    W4 = pkg
+    return pkg
+
+
+DEV = "cuda"
+CANARY = {torch.uint8: 0xA5, torch.int8: -91, torch.float32: -12345.5, torch.int32: -0x5A5A5A5A}
+
+
+def guarded(shape, dtype):
+    """A contiguous output tensor with 256-byte canary regions on both sides."""
+    n = int(np.prod(shape))
+    pad = 256 // torch.tensor([], dtype=dtype).element_size()
+    buf = torch.full((pad + n + pad,), CANARY[dtype], dtype=dtype, device=DEV)
+    return buf, buf[pad:pad + n].view(*shape), pad
+
+
+def guards_intact(buf, pad):
+    c = CANARY[buf.dtype]
+    head, tail = buf[:pad].cpu(), buf[-pad:].cpu()
+    return bool((head == c).all()) and bool((tail == c).all())
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def bits_equal(a: np.ndarray, b: np.ndarray) -> bool:
+    a, b = np.ascontiguousarray(a), np.ascontiguousarray(b)
+    if a.dtype == np.float32:
+        return np.array_equal(a.view(np.uint32), b.astype(np.float32).view(np.uint32))
+    return np.array_equal(a, b)
+
+
+def report(name, got, want):
+    bad = np.argwhere(~(got == want))
+    return f"{name}: {len(bad)} mismatches, first {bad[:5].tolist()}"
+
+
+# ---------------------------------------------------------- weight quantization
+SYM_SHAPES = [(1, 1), (10, 32), (32, 1), (7, 5), (33, 70), (128, 64), (300, 129), (1152, 6912)]
+
+
+@pytest.mark.parametrize("K,N", SYM_SHAPES)
+def test_quantize_weight_sym(K, N):
+    d = workloads.random_case(K * 13 + N, 1, K, N, sigma=0.02)
+    W = d["W"]
+    if N > 3:
+        W[:, 3] = 0.0                            # all-zero channel
+    if K >= 7 and N > 1:                         # exact ties at scale 1
+        W[:7, 1] = [7, 2.5, -2.5, 0.5, -0.5, 1.5, -3.5]
+        W[7:, 1] = 0
+    pref, sref = oracle.quantize_weight_sym(W)
+    bufp, packed, pp = guarded((N, (K + 1) // 2), torch.uint8)
+    bufs, sw, ps = guarded((N,), torch.float32)
+    W4.w4_quantize_weight(dev(W), "sym", 0, packed=packed, scales=sw)
+    assert bits_equal(host(sw), sref)
+    assert np.array_equal(host(packed), pref), report("packed", host(packed), pref)
+    assert guards_intact(bufp, pp) and guards_intact(bufs, ps)
+
+
+def test_quantize_weight_sym_full_7b():
+    d = workloads.generate("mlp7b", M=1)
+    pref, sref = oracle.quantize_weight_sym(d["W"])
+    packed, sw, _ = W4.w4_quantize_weight(dev(d["W"]), "sym")
+    assert bits_equal(host(sw), sref)
+    assert np.array_equal(host(packed), pref)
+
+
+ASYM_CASES = [(8, 3, 4), (64, 9, 32), (256, 70, 128), (384, 5, 128), (512, 33, 256), (1024, 130, 64)]
+
+
+@pytest.mark.parametrize("K,N,g", ASYM_CASES)
+def test_quantize_weight_asym(K, N, g):
+    rng = np.random.default_rng(K + N + g)
+    W = (rng.standard_normal((K, N)) * 0.015).astype(np.float32)
+    W[:, 0] += 0.05                              # all-positive channel: zero point < 0
+    if N > 2:
+        W[:g, 2] = 0.25                          # degenerate (constant) group
+    pref, sref, zref = oracle.quantize_weight_asym(W, g)
+    bufp, packed, pp = guarded((N, K // 2), torch.uint8)
+    packed_, s, z = W4.w4_quantize_weight(dev(W), "asym", g, packed=packed)
+    assert np.array_equal(host(packed), pref), report("packed", host(packed), pref)
+    assert bits_equal(host(s), sref) and bits_equal(host(z), zref)
+    assert guards_intact(bufp, pp)
+
+
+def test_quantize_weight_asym_full_70b_slice():
+    """The 70B-class layer's weights, first 2048 channels (all of K)."""
+    d = workloads.w4a16_inputs(N=2048)
+    pref, sref, zref = oracle.quantize_weight_asym(d["W"], d["group"])
+    packed, s, z = W4.w4_quantize_weight(dev(d["W"]), "asym", d["group"])
+    assert np.array_equal(host(packed), pref)
+    assert bits_equal(host(s), sref) and bits_equal(host(z), zref)
+
+
+# ------------------------------------------------------------ activations
+ACT_SHAPES = [(1, 1), (32, 10), (3, 33), (1, 1152), (8, 1152), (16, 4096), (64, 4096), (5, 1000)]
+
+
+@pytest.mark.parametrize("M,K", ACT_SHAPES)
+def test_quantize_act(M, K):
+    d = workloads.random_case(M * 7 + K, M, K, 1, outliers=min(6, K))
+    X = d["x"]
+    if M > 2:
+        X[1] = 0.0                               # all-zero row
+        X[2, : min(K, 6)] = [127, 0.5, 1.5, -2.5, -0.5, 126.5][: min(K, 6)]
+    xq_ref, sx_ref = oracle.quantize_act(X)
+    bufq, xq, pq = guarded((M, K), torch.int8)
+    xq_, sx = W4.a8_quantize_act(dev(X), Xq=xq)
+    assert np.array_equal(host(xq), xq_ref), report("xq", host(xq), xq_ref)
+    assert bits_equal(host(sx), sx_ref)
+    assert guards_intact(bufq, pq)
+
+
+def test_quantize_act_prefill_full():
+    d = workloads.generate("prefill", with_w=False)
+    xq_ref, sx_ref = oracle.quantize_act(d["x"])
+    xq, sx = W4.a8_quantize_act(dev(d["x"]))
+    assert np.array_equal(host(xq), xq_ref)
+    assert bits_equal(host(sx), sx_ref)
+
+
+# ------------------------------------------------------- integer products
+# (M, K, N): dot4 GEMV (M<=4, K%32==0), MFMA GEMV (M<=64, K%128==0),
+# MFMA GEMM (M>64, K%128==0) and the generic kernel, with ragged edges.
+I32_CASES = [
+    (1, 128, 16), (1, 1152, 100), (2, 4096, 33), (3, 96, 17), (4, 1152, 257),
+    (5, 128, 16), (8, 1152, 130), (16, 4096, 96), (17, 256, 65), (33, 512, 31), (64, 1152, 200),
+    (65, 128, 130), (130, 256, 129), (256, 1152, 384), (300, 512, 1000),
+    (1, 10, 32), (32, 10, 32), (32, 32, 1), (6, 96, 20), (3, 7, 5), (70, 200, 9),
+]
+
+
+@pytest.mark.parametrize("M,K,N", I32_CASES)
+def test_matmul_i32(M, K, N):
+    xq = workloads.random_int8(M * 31 + K, (M, K))
+    packed = workloads.random_bytes(K * 17 + N, (N, (K + 1) // 2))  # every nibble incl. -8
+    if K % 2:
+        packed[:, -1] &= 0x0F
+    ref = oracle.matmul_i32(xq, packed, K)
+    bufa, acc, pa = guarded((M, N), torch.int32)
+    W4.w4a8_matmul_i32(dev(xq), dev(packed), acc=acc)
+    got = host(acc)
+    assert np.array_equal(got, ref), report(f"acc path={W4.w4_last_path()}", got, ref)
+    assert guards_intact(bufa, pa)
+
+
+def test_matmul_i32_extremes():
+    """Code -8 times -128 everywhere: the largest accumulator magnitude."""
+    for M in (1, 8, 128):
+        K, N = 4096, 48
+        xq = np.full((M, K), -128, np.int8)
+        packed = np.full((N, K // 2), 0x88, np.uint8)
+        acc = W4.w4a8_matmul_i32(dev(xq), dev(packed))
+        assert np.all(host(acc) == 1024 * K), W4.w4_last_path()
+
+
+# ----------------------------------------------------------- W4A8 linear
+LIN_CASES = [(1, 1152, 200), (4, 256, 70), (8, 1152, 130), (16, 512, 64), (64, 256, 33),
+             (100, 384, 260), (32, 10, 32), (9, 40, 7)]
+
+
+@pytest.mark.parametrize("M,K,N", LIN_CASES)
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_linear(M, K, N, with_bias):
+    d = workloads.random_case(M + K + N, M, K, N, outliers=min(6, K), bias=with_bias)
+    pref, sref = oracle.quantize_weight_sym(d["W"])
+    b = d.get("bias")
+    yref = oracle.w4a8_linear(d["x"], pref, sref, b)
+    packed, sw, _ = W4.w4_quantize_weight(dev(d["W"]), "sym")
+    bufy, y, py = guarded((M, N), torch.float32)
+    W4.w4a8_linear(dev(d["x"]), packed, sw, bias=None if b is None else dev(b), Y=y)
+    got = host(y)
+    assert bits_equal(got, yref), report(f"y path={W4.w4_last_path()}", got, yref)
+    assert np.all(np.abs(got - yref) <= 1e-5 * np.abs(yref))
+    assert guards_intact(bufy, py)
+    # same product from pre-quantized activations
+    xq, sx = oracle.quantize_act(d["x"])
+    y2 = W4.w4a8_linear_q(dev(xq), dev(sx), packed, sw, bias=None if b is None else dev(b))
+    assert bits_equal(host(y2), yref), W4.w4_last_path()
+
+
+def _sample(n, k, seed):
+    if n <= k:
+        return np.arange(n)
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], rng.choice(n, min(n, k) - 2, replace=False)]))
+
+
+@pytest.mark.parametrize("name,M", [("gemma", 1), ("gemma", 8), ("mlp7b", 1), ("mlp7b", 16),
+                                    ("mlp7b", 64), ("prefill", None)])
+def test_linear_full_workloads(name, M):
+    """Full-size layers as benchmarked; sampled rows x channels against the oracle."""
+    d = workloads.generate(name, M=M)
+    W, X = d["W"], d["x"]
+    packed, sw, _ = W4.w4_quantize_weight(dev(W), "sym")
+    y = W4.w4a8_linear(dev(X), packed, sw)
+    path = W4.w4_last_path()
+    got = host(y)
+    rows = _sample(X.shape[0], 64, 1)
+    cols = _sample(W.shape[1], 256, 2)
+    pref, sref = oracle.quantize_weight_sym(np.ascontiguousarray(W[:, cols]))
+    assert np.array_equal(host(packed)[cols], pref) and bits_equal(host(sw)[cols], sref)
+    yref = oracle.w4a8_linear(np.ascontiguousarray(X[rows]), pref, sref)
+    sub = got[np.ix_(rows, cols)]
+    assert bits_equal(sub, yref), report(f"{name} M={M} path={path}", sub, yref)
+    assert np.all(np.isfinite(got))
+
+
+def test_toy_model_end_to_end():
+    """The Keras guide's toy model: Dense 10->32 (ReLU) -> Dense 32->1, W4A8."""
+    t = workloads.toy_model()
+    p1, s1 = oracle.quantize_weight_sym(t["W1"])
+    p2, s2 = oracle.quantize_weight_sym(t["W2"])
+    h = np.maximum(oracle.w4a8_linear(t["x"], p1, s1, t["b1"]), 0).astype(np.float32)
+    yref = oracle.w4a8_linear(h, p2, s2, t["b2"])
+    gp1, gs1, _ = W4.w4_quantize_weight(dev(t["W1"]), "sym")
+    gp2, gs2, _ = W4.w4_quantize_weight(dev(t["W2"]), "sym")
+    gh = torch.relu(W4.w4a8_linear(dev(t["x"]), gp1, gs1, bias=dev(t["b1"])))
+    gy = W4.w4a8_linear(gh.contiguous(), gp2, gs2, bias=dev(t["b2"]))
+    assert bits_equal(host(gy), yref)
+
+
+# ----------------------------------------------------------------- W4A16
+def _w4a16_check(got, yref, absy, K):
+    u = 2.0 ** -24
+    gamma = K * u / (1 - K * u)
+    diff = np.abs(got.astype(np.float64) - yref)
+    assert np.linalg.norm(diff) <= 1e-5 * np.linalg.norm(yref)
+    assert np.all(diff <= gamma * absy + 1e-30)
+
+
+W4A16_CASES = [(1, 128, 16, 128), (16, 256, 70, 128), (5, 512, 33, 64), (16, 1024, 130, 32),
+               (20, 384, 48, 128), (3, 96, 10, 32), (2, 40, 6, 4), (64, 256, 64, 128)]
+
+
+@pytest.mark.parametrize("M,K,N,g", W4A16_CASES)
+def test_w4a16_linear(M, K, N, g):
+    rng = np.random.default_rng(M * K + N + g)
+    W = (rng.standard_normal((K, N)) * 0.015).astype(np.float32)
+    W[:, 0] += 0.05
+    xb = workloads.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    pref, sref, zref = oracle.quantize_weight_asym(W, g)
+    yref, absy = oracle.w4a16_linear(xb, pref, sref, zref, g)
+    packed, s, z = W4.w4_quantize_weight(dev(W), "asym", g)
+    bufy, y, py = guarded((M, N), torch.float32)
+    W4.w4a16_linear(dev(xb.view(np.int16)), packed, s, z, g, Y=y)
+    _w4a16_check(host(y), yref, absy, K)
+    assert guards_intact(bufy, py)
+
+
+def test_w4a16_zero_point_outside_fast_range():
+    """Groups whose zero point leaves [-112, 128] take the direct dequantization."""
+    K, N, M, g = 256, 32, 4, 128
+    rng = np.random.default_rng(77)
+    W = (rng.standard_normal((K, N)) * 0.01).astype(np.float32)
+    W[:, :8] += 3.0       # far-positive groups: zero point about -4000
+    W[:, 8:12] -= 3.0     # far-negative groups: zero point about +4000
+    xb = workloads.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    pref, sref, zref = oracle.quantize_weight_asym(W, g)
+    assert zref.min() < -112 and zref.max() > 128
+    yref, absy = oracle.w4a16_linear(xb, pref, sref, zref, g)
+    packed, s, z = W4.w4_quantize_weight(dev(W), "asym", g)
+    assert np.array_equal(host(packed), pref)
+    y = W4.w4a16_linear(dev(xb.view(np.int16)), packed, s, z, g)
+    _w4a16_check(host(y), yref, absy, K)
+
+
+def test_w4a16_full_workload():
+    """The 70B-class layer (16 x 8192 x 28672, group 128), sampled channels."""
+    d = workloads.w4a16_inputs()
+    W, xb, g = d["W"], d["x_bf16"], d["group"]
+    packed, s, z = W4.w4_quantize_weight(dev(W), "asym", g)
+    y = W4.w4a16_linear(dev(xb.view(np.int16)), packed, s, z, g)
+    assert W4.w4_last_path() == "w4a16_mfma"
+    got = host(y)
+    cols = _sample(W.shape[1], 384, 3)
+    pref, sref, zref = oracle.quantize_weight_asym(np.ascontiguousarray(W[:, cols]), g)
+    assert np.array_equal(host(packed)[cols], pref)
+    yref, absy = oracle.w4a16_linear(xb, pref, sref, zref, g)
+    _w4a16_check(got[:, cols], yref, absy, W.shape[0])
