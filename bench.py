@@ -1,0 +1,372 @@
+#!/usr/bin/env python3
+"""Throughput of the INT4 weight-quantized linear layer on one MI355X.
+
+Headline (one JSON line on stdout): W4A8 decode GEMV, Gemma3-1B-like MLP
+up-projection, x [1, 1152] fp32 ~ N(0,1), W [1152, 6912] ~ N(0, 0.02)
+quantized to symmetric per-channel int4.  One step = one ``w4a8_linear``
+call = the whole forward of the layer (per-row int8 activation quantization,
+int4 unpack, int8 x int8 -> int32 product, dequantization), launched from a
+captured HIP graph.  ``value`` = algorithmic bytes per step (packed weights +
+scales + x + y) x steps / wall time.  The packed weights rotate over enough
+copies (> 512 MB) that every step reads them from HBM, not from the 256 MB
+Infinity Cache.  Weights are quantized once, before timing (post-training
+quantization is a one-shot offline step).
+
+Also reported in the same line:
+  roofline      the dominant kernel's achieved GB/s (algorithmic bytes per
+                launch / average kernel duration from HIP events attached to
+                the kernel's dispatch) against the 8 TB/s HBM peak;
+  parts         the other workloads (Gemma M=8, 7B-class M=1/16/64, the
+                4096^3 prefill in int8 TOPS, the 70B-class W4A16 layer) and
+                the weight quantizers, each with per-kernel durations;
+  cpu_baseline  the CPU oracle on a bounded sample of the headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-parts]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0      # dense int8 MFMA
+BF16_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA
+ROTATE_BYTES = 640 << 20     # > 2 x the 256 MB Infinity Cache
+METRIC = "W4A8 linear: GB/s (M=1 GEMV) and int8 TOPS (M=4096), % of roofline"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------- HIP events
+class Hip:
+    """Raw hipEvent_t handles from the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so.7")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        maps = open("/proc/self/maps").read()
+        libs = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+        assert len(libs) == 1, f"more than one HIP runtime mapped: {libs}"
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        rc = self.h.hipEventCreate(ctypes.byref(ev))
+        assert rc == 0, rc
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        assert self.h.hipEventSynchronize(b) == 0
+        f = ctypes.c_float()
+        rc = self.h.hipEventElapsedTime(ctypes.byref(f), a, b)
+        assert rc == 0, rc
+        return float(f.value)
+
+    def destroy(self, ev):
+        self.h.hipEventDestroy(ev)
+
+
+# ------------------------------------------------------------- workloads
+def w4a8_bytes(M, K, N):
+    """Algorithmic bytes of one W4A8 forward: packed int4 weights, fp32 channel
+    scales, fp32 activations in, fp32 outputs out."""
+    return N * ((K + 1) // 2) + 4 * N + 4 * M * K + 4 * M * N
+
+
+def w4a16_bytes(M, K, N, g):
+    """Packed int4 weights, fp32 scale + zero point per group, bf16 x, fp32 y."""
+    return N * ((K + 1) // 2) + 8 * N * (K // g) + 2 * M * K + 4 * M * N
+
+
+class W4A8Case:
+    def __init__(self, w4, torch, name, shape_name, M, rotate=True):
+        import workloads
+        d = workloads.generate(shape_name, M=M)
+        self.name, self.M, self.K, self.N = name, M if M else d["M"], d["K"], d["N"]
+        self.torch, self.w4 = torch, w4
+        dev = torch.device("cuda")
+        self.x = torch.from_numpy(d["x"]).to(dev)
+        W = torch.from_numpy(d["W"]).to(dev)
+        t0 = time.perf_counter()
+        p, s, _ = w4.w4_quantize_weight(W, "sym")
+        torch.cuda.synchronize()
+        self.quant_s = time.perf_counter() - t0
+        del W
+        wbytes = p.numel() + 4 * s.numel()
+        self.copies = max(1, math.ceil(ROTATE_BYTES / wbytes)) if rotate else 2
+        self.P = [p] + [p.clone() for _ in range(self.copies - 1)]
+        self.S = [s] + [s.clone() for _ in range(self.copies - 1)]
+        self.y = torch.empty((self.M, self.N), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(max(1, w4.w4a8_workspace_bytes(self.M, self.K, self.N)),
+                              dtype=torch.uint8, device=dev)
+        self.bytes = w4a8_bytes(self.M, self.K, self.N)
+        self.ops = 2 * self.M * self.N * self.K
+        self.host_x, self.host_W = d["x"], d["W"]
+
+    def step(self, i):
+        c = i % self.copies
+        self.w4.w4a8_linear(self.x, self.P[c], self.S[c], Y=self.y, workspace=self.ws)
+
+
+class W4A16Case:
+    def __init__(self, w4, torch):
+        import numpy as np
+        import workloads
+        d = workloads.w4a16_inputs()
+        self.name = "w4a16_70b_m16"
+        self.M, self.K, self.N, self.g = d["M"], d["K"], d["N"], d["group"]
+        self.torch, self.w4 = torch, w4
+        dev = torch.device("cuda")
+        self.x = torch.from_numpy(d["x_bf16"].view(np.int16)).to(dev)
+        W = torch.from_numpy(d["W"]).to(dev)
+        t0 = time.perf_counter()
+        p, s, z = w4.w4_quantize_weight(W, "asym", self.g)
+        torch.cuda.synchronize()
+        self.quant_s = time.perf_counter() - t0
+        del W
+        wbytes = p.numel() + 8 * s.numel()
+        self.copies = max(1, math.ceil(ROTATE_BYTES / wbytes))
+        self.P = [p] + [p.clone() for _ in range(self.copies - 1)]
+        self.Sc = [s] + [s.clone() for _ in range(self.copies - 1)]
+        self.Z = [z] + [z.clone() for _ in range(self.copies - 1)]
+        self.y = torch.empty((self.M, self.N), dtype=torch.float32, device=dev)
+        self.bytes = w4a16_bytes(self.M, self.K, self.N, self.g)
+        self.ops = 2 * self.M * self.N * self.K
+
+    def step(self, i):
+        c = i % self.copies
+        self.w4.w4a16_linear(self.x, self.P[c], self.Sc[c], self.Z[c], self.g, Y=self.y)
+
+
+def graph_step_time(torch, case, steps, warmup):
+    """Wall time per step of `steps` steps replayed from one captured graph."""
+    for i in range(warmup):
+        case.step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                case.step(i)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()                      # untimed replay
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    del g
+    return dt / steps
+
+
+def kernel_time(torch, hip, w4, case, launches):
+    """Average duration (s) of the product kernel, from start/stop events
+    attached to each dispatch, over `launches` rotating launches."""
+    evs = [(hip.event(), hip.event()) for _ in range(launches)]
+    for i in range(min(10, launches)):
+        case.step(i)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        w4.w4_time_next_kernel(a, b)
+        case.step(i)
+    torch.cuda.synchronize()
+    ms = [hip.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    ms.sort()
+    return sum(ms) / len(ms) / 1e3, ms[len(ms) // 2] / 1e3
+
+
+def src_digest():
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "common.h"):
+        with open(os.path.join(ROOT, "int4_weight_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_digest):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "gemv_dot4_gemma_m1_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("src_digest") != kernel_digest:
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(case, seconds=10.0):
+    """The CPU oracle, as it is, on the headline workload: whole forward calls
+    repeated for about `seconds` on one host thread."""
+    import oracle
+    pref, sref = oracle.quantize_weight_sym(case.host_W)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.w4a8_linear(case.host_x, pref, sref)
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    per = dt / n
+    return {"value": round(case.bytes / per / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} calls of the oracle's w4a8_linear on the headline workload "
+                      f"({case.M}x{case.K}x{case.N}), {dt:.1f} s, {per * 1e3:.2f} ms per call"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-parts", action="store_true", help="headline workload only")
+    ap.add_argument("--only", default=None,
+                    help="run one workload's product kernel (for profilers): gemma_m1, gemma_m8, "
+                         "mlp7b_m1, mlp7b_m16, mlp7b_m64, prefill, w4a16; or copy (a 64 MiB "
+                         "device copy, for counter calibration)")
+    ap.add_argument("--launches", type=int, default=200)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer shards over output channels with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import int4_weight_quantized_amd as w4
+    w4.lib()  # fails loudly when the HIP library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    hip = Hip()
+
+    if args.only == "copy":
+        # a plain device copy of known size (calibrates the HBM byte counters)
+        src = torch.ones(64 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy: {args.warmup + args.steps} copies of {src.numel()} bytes done")
+        return
+    if args.only:
+        specs = {"gemma_m1": ("gemma", 1), "gemma_m8": ("gemma", 8), "mlp7b_m1": ("mlp7b", 1),
+                 "mlp7b_m16": ("mlp7b", 16), "mlp7b_m64": ("mlp7b", 64),
+                 "prefill": ("prefill", None)}
+        case = (W4A16Case(w4, torch) if args.only == "w4a16"
+                else W4A8Case(w4, torch, args.only, *specs[args.only]))
+        for i in range(args.warmup + args.steps):
+            case.step(i)
+        torch.cuda.synchronize()
+        log(f"{args.only}: {args.warmup + args.steps} launches done ({w4.w4_last_path()})")
+        return
+
+    log("headline: gemma3-1b up-projection, W4A8, M=1")
+    head = W4A8Case(w4, torch, "gemma_m1", "gemma", 1)
+    step_s = graph_step_time(torch, head, args.steps, args.warmup)
+    path = w4.w4_last_path()
+    k_avg, k_med = kernel_time(torch, hip, w4, head, args.launches)
+    value = head.bytes / step_s / 1e9
+    achieved = head.bytes / k_avg / 1e9
+    digest = src_digest()
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "Gemma3-1B-like MLP up-projection, W4A8 decode GEMV",
+                   "M": 1, "K": head.K, "N": head.N, "weights": "int4 symmetric per-channel",
+                   "activations": "int8 per-row dynamic", "launch": "hipGraph of all steps",
+                   "rotating_weight_copies": head.copies, "product_kernel": path},
+        "roofline": {"bound": "hbm", "kernel": "k_gemv_dot4<1,fused>",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(digest),
+                     "algorithmic_bytes_per_launch": head.bytes,
+                     "kernel_us_avg": round(k_avg * 1e6, 3), "kernel_us_median": round(k_med * 1e6, 3),
+                     "src_digest": digest},
+    }
+    log(f"headline: step {step_s * 1e6:.2f} us, kernel {k_avg * 1e6:.2f} us, {value:.0f} GB/s")
+
+    parts = []
+    if not args.no_parts:
+        def w4a8_part(name, shape, M, bound, rotate=True):
+            log(f"part: {name}")
+            c = W4A8Case(w4, torch, name, shape, M, rotate=rotate)
+            st = graph_step_time(torch, c, min(args.steps, 200), 10)
+            p = w4.w4_last_path()
+            ka, km = kernel_time(torch, hip, w4, c, min(args.launches, 100))
+            r = {"workload": name, "M": c.M, "K": c.K, "N": c.N, "product_kernel": p,
+                 "step_us": round(st * 1e6, 3), "kernel_us_avg": round(ka * 1e6, 3),
+                 "algorithmic_bytes": c.bytes, "int_ops": c.ops,
+                 "rotating_weight_copies": c.copies,
+                 "weight_quantize_ms": round(c.quant_s * 1e3, 3)}
+            if bound == "hbm":
+                r["GBps_kernel"] = round(c.bytes / ka / 1e9, 1)
+                r["GBps_step"] = round(c.bytes / st / 1e9, 1)
+                r["frac_hbm_kernel"] = round(c.bytes / ka / 1e9 / HBM_PEAK_GBS, 4)
+            else:
+                r["TOPS_kernel"] = round(c.ops / ka / 1e12, 1)
+                r["TOPS_step"] = round(c.ops / st / 1e12, 1)
+                r["frac_int8_mfma_kernel"] = round(c.ops / ka / 1e12 / INT8_PEAK_TOPS, 4)
+                r["frac_int8_mfma_step"] = round(c.ops / st / 1e12 / INT8_PEAK_TOPS, 4)
+            parts.append(r)
+            del c
+            torch.cuda.empty_cache()
+
+        w4a8_part("gemma_m8", "gemma", 8, "hbm")
+        w4a8_part("mlp7b_m1", "mlp7b", 1, "hbm")
+        w4a8_part("mlp7b_m16", "mlp7b", 16, "hbm")
+        w4a8_part("mlp7b_m64", "mlp7b", 64, "hbm")
+        w4a8_part("prefill_4096", "prefill", None, "mfma", rotate=False)
+        log("part: w4a16_70b_m16")
+        c = W4A16Case(w4, torch)
+        st = graph_step_time(torch, c, 50, 5)
+        p = w4.w4_last_path()
+        ka, km = kernel_time(torch, hip, w4, c, 50)
+        parts.append({"workload": c.name, "M": c.M, "K": c.K, "N": c.N, "group": c.g,
+                      "product_kernel": p, "step_us": round(st * 1e6, 3),
+                      "kernel_us_avg": round(ka * 1e6, 3), "algorithmic_bytes": c.bytes,
+                      "GBps_kernel": round(c.bytes / ka / 1e9, 1),
+                      "GBps_step": round(c.bytes / st / 1e9, 1),
+                      "frac_hbm_kernel": round(c.bytes / ka / 1e9 / HBM_PEAK_GBS, 4),
+                      "TFLOPS_kernel": round(c.ops / ka / 1e12, 2),
+                      "rotating_weight_copies": c.copies,
+                      "weight_quantize_ms": round(c.quant_s * 1e3, 3)})
+        del c
+        torch.cuda.empty_cache()
+        pre = [p for p in parts if p["workload"] == "prefill_4096"][0]
+        out["prefill_int8"] = {"metric": "int8 TOPS (M=4096 prefill GEMM)",
+                               "TOPS_kernel": pre["TOPS_kernel"], "TOPS_step": pre["TOPS_step"],
+                               "peak": INT8_PEAK_TOPS,
+                               "frac_kernel": pre["frac_int8_mfma_kernel"]}
+    out["parts"] = parts
+    out["headline_weight_quantize_ms"] = round(head.quant_s * 1e3, 3)
+    if not args.no_cpu:
+        log("cpu baseline: oracle")
+        out["cpu_baseline"] = cpu_baseline(head)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

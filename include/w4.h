@@ -145,6 +145,15 @@ int w4a16_linear(const uint16_t *X_bf16, int64_t M, int64_t K, int64_t N,
 /* Static description of a status code (never NULL). */
 const char *w4_status_string(int status);
 
+/* Per-kernel timing for benchmarks and profiling: the next product kernel
+ * (the GEMV / GEMM / W4A16 kernel, not the activation or weight quantizers
+ * of a multi-kernel call) that an entry point launches from this host thread
+ * records `start_event` when it begins executing and `stop_event` when it
+ * completes.  Both are hipEvent_t handles created by the caller (either may
+ * be NULL; NULL and NULL cancels).  Consumed by that one launch.  Not for
+ * use while a stream is being captured into a graph.  Returns W4_OK. */
+int w4_time_next_kernel(void *start_event, void *stop_event);
+
 /* Name of the kernel variant the last successful call on this thread launched
  * for its main product (for tests and profiling; never NULL). */
 const char *w4_last_path(void);

@@ -62,6 +62,7 @@ def lib():
             "w4a16_linear": ([_P, _I, _I, _I, _P, _P, _P, _I, _P, _P], ctypes.c_int),
             "w4_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "w4_last_path": ([], ctypes.c_char_p),
+            "w4_time_next_kernel": ([_P, _P], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
             f = getattr(L, name)
@@ -78,6 +79,12 @@ def w4_status_string(status: int) -> str:
 def w4_last_path() -> str:
     """Kernel variant of the last call's main product (e.g. "gemv_dot4")."""
     return lib().w4_last_path().decode()
+
+
+def w4_time_next_kernel(start_event: int | None, stop_event: int | None) -> None:
+    """Attach raw hipEvent_t handles to the next product kernel launched
+    from this thread (recorded when it starts and when it completes)."""
+    _check("w4_time_next_kernel", lib().w4_time_next_kernel(start_event, stop_event))
 
 
 def w4a8_workspace_bytes(M: int, K: int, N: int) -> int:

@@ -11,6 +11,7 @@
 namespace {
 
 thread_local const char *g_last_path = "none";
+thread_local hipEvent_t g_time_start = nullptr, g_time_stop = nullptr;
 
 inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -105,7 +106,19 @@ int check_workspace(int64_t M, int64_t K, void *workspace, size_t bytes) {
 
 }  // namespace
 
+w4::TimingEvents w4::take_timing_events() {
+    TimingEvents ev{g_time_start, g_time_stop};
+    g_time_start = g_time_stop = nullptr;
+    return ev;
+}
+
 extern "C" {
+
+int w4_time_next_kernel(void *start_event, void *stop_event) {
+    g_time_start = reinterpret_cast<hipEvent_t>(start_event);
+    g_time_stop = reinterpret_cast<hipEvent_t>(stop_event);
+    return W4_OK;
+}
 
 const char *w4_status_string(int status) {
     switch (status) {

@@ -14,6 +14,83 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// ------------------------------------------------------------ buffer loads
+// Raw buffer loads: the descriptor carries the byte range, and a load whose
+// offset lies outside it returns zeros without touching memory.  This gives
+// branch-free predication (no exec-mask branches between loads, so the loads
+// of a lane issue back to back).
+constexpr int kBufFlags = 0x00020000;  // gfx9 raw-buffer descriptor word 3
+constexpr int kMaxRange = 0x7F000000;  // descriptor ranges are capped here
+constexpr int kOOB = 0x7FFF0000;       // an offset beyond every range (plus room for +16 .. +48)
+
+// Callers keep every in-range offset below kMaxRange (the kernels rebase the
+// descriptor on the rows a block touches).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int n = bytes > kMaxRange ? kMaxRange : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, kBufFlags);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+__device__ __forceinline__ float4 bloadf4(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ float bloadf(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// ------------------------------------------------------------ DPP reductions
+// Cross-lane moves inside a row of 16 lanes (no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Sum over each row of 16 lanes; every lane of the row gets the sum.
+__device__ __forceinline__ int sum16(int v) {
+    v += dpp<kQuadSwap1>(v);
+    v += dpp<kQuadSwap2>(v);
+    v += dpp<kRowHalfMirror>(v);
+    v += dpp<kRowMirror>(v);
+    return v;
+}
+
+__device__ __forceinline__ float fdpp_max(float v, int which) {
+    int b = __builtin_bit_cast(int, v), o;
+    switch (which) {
+        case 0: o = dpp<kQuadSwap1>(b); break;
+        case 1: o = dpp<kQuadSwap2>(b); break;
+        case 2: o = dpp<kRowHalfMirror>(b); break;
+        default: o = dpp<kRowMirror>(b); break;
+    }
+    return fmaxf(v, __builtin_bit_cast(float, o));
+}
+
+// Max over the 64 lanes of a wave (inputs >= 0 or any finite values); the
+// result is wave-uniform.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = fdpp_max(v, 0);
+    v = fdpp_max(v, 1);
+    v = fdpp_max(v, 2);
+    v = fdpp_max(v, 3);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -36,49 +36,43 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(W4A8Args a) {
     const int r16 = lane % 16, kq = lane / 16;
     const int wm = wave / 2, wn = wave % 2;
 
-    // Global -> register staging assignment.
+    // Global -> register staging assignment (raw buffer loads; the
+    // descriptors cover this tile's rows / channels, so rows past M and
+    // channels past N read zeros and their outputs are not stored).
     // A: 1024 16-byte pieces: piece p = t + 256*i -> row p/8, column (p%8)*16.
     // B: 512 pieces: piece p = t + 256*i -> channel p/4, bytes (p%4)*16.
-    const int8_t *ag[4];
-    bool avalid[4];
+    const int Ki = (int)K, KBi = (int)KB;
+    const auto ra = make_rsrc(a.Xq + m0 * K, min((int64_t)kBM, M - m0) * K);
+    const auto rbs = make_rsrc(a.packed + n0 * KB, min((int64_t)kBN, N - n0) * KB);
+    int aoff[4], boff[2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int p = t + 256 * i;
-        const int64_t row = m0 + p / 8;
-        avalid[i] = row < M;
-        ag[i] = a.Xq + (avalid[i] ? row : 0) * K + (p % 8) * 16;
+        aoff[i] = (p / 8) * Ki + (p % 8) * 16;
     }
-    const uint8_t *bg[2];
-    bool bvalid[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int p = t + 256 * i;
-        const int64_t col = n0 + p / 4;
-        bvalid[i] = col < N;
-        bg[i] = a.packed + (bvalid[i] ? col : 0) * KB + (p % 4) * 16;
+        boff[i] = (p / 4) * KBi + (p % 4) * 16;
     }
 
-    uint4 ra[4], rb[2];
-    auto fetch = [&](int64_t kt) {
+    uint4 ra_[4], rb_[2];
+    auto fetch = [&](int kt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            ra[i] = avalid[i] ? *reinterpret_cast<const uint4 *>(ag[i] + kt * kBK)
-                              : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < 4; ++i) ra_[i] = bload16(ra, aoff[i] + kt * kBK);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            rb[i] = bvalid[i] ? *reinterpret_cast<const uint4 *>(bg[i] + kt * (kBK / 2))
-                              : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < 2; ++i) rb_[i] = bload16(rbs, boff[i] + kt * (kBK / 2));
     };
     auto stash = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int p = t + 256 * i;
-            *reinterpret_cast<uint4 *>(&As[buf][(p / 8) * kAP + (p % 8) * 16]) = ra[i];
+            *reinterpret_cast<uint4 *>(&As[buf][(p / 8) * kAP + (p % 8) * 16]) = ra_[i];
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int p = t + 256 * i;
-            *reinterpret_cast<uint4 *>(&Bs[buf][(p / 4) * kBP + (p % 4) * 16]) = rb[i];
+            *reinterpret_cast<uint4 *>(&Bs[buf][(p / 4) * kBP + (p % 4) * 16]) = rb_[i];
         }
     };
 
@@ -88,12 +82,12 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(W4A8Args a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-    const int64_t KT = K / kBK;
+    const int KT = (int)(K / kBK);
     fetch(0);
     stash(0);
     __syncthreads();
 
-    for (int64_t kt = 0; kt < KT; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
         const int buf = (int)(kt & 1);
         if (kt + 1 < KT) fetch(kt + 1);
 
@@ -146,9 +140,9 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(W4A8Args a) {
 hipError_t launch_gemm_mfma(const W4A8Args &a, hipStream_t st) {
     const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
     if (a.out == Out::I32)
-        hipLaunchKernelGGL(k_gemm_mfma<Out::I32>, dim3((unsigned)tiles), dim3(256), 0, st, a);
+        launch_main(k_gemm_mfma<Out::I32>, dim3((unsigned)tiles), dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL(k_gemm_mfma<Out::Y>, dim3((unsigned)tiles), dim3(256), 0, st, a);
+        launch_main(k_gemm_mfma<Out::Y>, dim3((unsigned)tiles), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

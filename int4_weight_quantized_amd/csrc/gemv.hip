@@ -7,6 +7,10 @@
 //    launch runs steps 3-6.
 //  * k_gemv_mfma  (M <= 64): int8 MFMA 16x16x64 with the weight operand
 //    unpacked in registers; the activations come pre-quantized in P8 layout.
+//
+// All global loads are raw buffer loads: out-of-range lanes get zeros from
+// the descriptor's range check instead of an exec-mask branch, so a lane's
+// loads issue back to back and the vmcnt waits stay in program order.
 #include "common.h"
 #include "kernels.h"
 
@@ -14,80 +18,124 @@ namespace w4 {
 
 // ------------------------------------------------------------------ dot4
 // Block = 256 threads = 16 output channels x 16 lanes.  Lane j of a channel
-// streams the 16-byte chunks j, j+16, j+32, ... of that channel's packed row
-// (one chunk = 32 codes), so a wave reads 4 rows x 256 contiguous bytes per
-// load.  The quantized activations (P8 layout) sit in LDS.
+// streams the 16-byte chunks j, j+16, ..., of that channel's packed row (one
+// chunk = 32 codes), so a wave reads 4 rows x 256 contiguous bytes per load.
+// Order of work: (1) issue the activation loads, (2) issue up to 8 weight
+// chunks per lane, (3) quantize the activations into LDS (P8 layout) while the
+// weights are in flight, (4) dot products, (5) 16-lane DPP sum and epilogue.
 constexpr int kDot4Rows = 16;
-constexpr int kDot4Batch = 8;  // chunks in flight per lane
+constexpr int kDot4Batch = 8;  // chunks per lane per batch = 4096 codes per row
 
 bool gemv_dot4_ok(int64_t M, int64_t K) {
-    return M >= 1 && M <= 4 && K % 32 == 0 && M * K <= 48 * 1024;
+    return M >= 1 && M <= 4 && K % 32 == 0 && K <= 8192;
 }
 
-template <int M, bool FUSED, Out OUT>
+template <int M, int NG, bool FUSED, Out OUT>
 __global__ __launch_bounds__(256) void k_gemv_dot4(W4A8Args a) {
     extern __shared__ __align__(16) uint8_t smem[];
-    __shared__ float red[4];
-    __shared__ float sxs[4];
+    __shared__ float red[4][M];
     int8_t *xs = reinterpret_cast<int8_t *>(smem);
-    const int K = (int)a.K;
-    const int64_t KB = a.K / 2;
-    const int C = K / 32;  // chunks per row
-    const int j = threadIdx.x & 15;
-    const int64_t n = (int64_t)blockIdx.x * kDot4Rows + threadIdx.x / 16;
-    const bool valid = n < a.N;
-    const uint4 *prow = reinterpret_cast<const uint4 *>(a.packed + (valid ? n : 0) * KB);
+    const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+    const int K = (int)a.K, KB = K / 2, C = K / 32, G8 = K / 8;
+    const int j = t & 15, r = t >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * kDot4Rows;
+    const int rows = (int)min((int64_t)kDot4Rows, a.N - n0);
 
-    // Issue the first batch of weight loads before the prologue so their
-    // latency overlaps the activation quantization.
+    // (1) activations: group g = t + 256*i holds k = 8g .. 8g+7 of each row.
+    float4 xa[M][NG], xb[M][NG];
+    uint2 xn[M][NG];
+    if (FUSED) {
+        const auto rx = make_rsrc(a.X, (int64_t)M * K * 4);
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                const int g = t + 256 * i;
+                const int off = g < G8 ? (m * K + 8 * g) * 4 : kOOB;
+                xa[m][i] = bloadf4(rx, off);
+                xb[m][i] = bloadf4(rx, off + 16);
+            }
+    } else {
+        const auto rq = make_rsrc(a.Xq, (int64_t)M * K);
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                const int g = t + 256 * i;
+                xn[m][i] = bload8(rq, g < G8 ? m * K + 8 * g : kOOB);
+            }
+    }
+
+    // (2) weights of this block's rows.
+    const auto rw = make_rsrc(a.packed + n0 * KB, (int64_t)rows * KB);
+    const int rowoff = r * KB;
     uint4 wb[kDot4Batch];
 #pragma unroll
     for (int u = 0; u < kDot4Batch; ++u) {
         const int c = j + 16 * u;
-        wb[u] = (valid && c < C) ? prow[c] : make_uint4(0, 0, 0, 0);
+        wb[u] = bload16(rw, c < C ? rowoff + 16 * c : kOOB);
     }
+    // Keep the scheduler from interleaving the activation math (which waits
+    // for the activation loads) with the weight loads above.
+    __builtin_amdgcn_sched_barrier(0);
 
-    // Prologue: activations -> LDS in P8 layout, plus their row scales.
-    const int ng = K / 8;
+    // (3) activations -> int8 P8 layout in LDS, scales in registers.
+    float sxm[M];
     if (FUSED) {
+#pragma unroll
         for (int m = 0; m < M; ++m) {
-            const float *row = a.X + (int64_t)m * K;
-            const float4 *r4 = reinterpret_cast<const float4 *>(row);
-            float amax = 0.0f;
-            for (int i = threadIdx.x; i < K / 4; i += 256) {
-                float4 v = r4[i];
-                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            float am = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                am = fmaxf(am, fmaxf(fmaxf(fabsf(xa[m][i].x), fabsf(xa[m][i].y)),
+                                     fmaxf(fabsf(xa[m][i].z), fabsf(xa[m][i].w))));
+                am = fmaxf(am, fmaxf(fmaxf(fabsf(xb[m][i].x), fabsf(xb[m][i].y)),
+                                     fmaxf(fabsf(xb[m][i].z), fabsf(xb[m][i].w))));
             }
-            amax = block_max(amax, red);
-            const float s = (amax == 0.0f) ? 0.0f : amax / 127.0f;
-            if (threadIdx.x == 0) sxs[m] = s;
-            for (int g = threadIdx.x; g < ng; g += 256) {
-                const float4 v0 = r4[2 * g], v1 = r4[2 * g + 1];
-                uint2 p;
-                p.x = pack4_i8(quant_code(v0.x, s, -128.f, 127.f), quant_code(v0.z, s, -128.f, 127.f),
-                               quant_code(v1.x, s, -128.f, 127.f), quant_code(v1.z, s, -128.f, 127.f));
-                p.y = pack4_i8(quant_code(v0.y, s, -128.f, 127.f), quant_code(v0.w, s, -128.f, 127.f),
-                               quant_code(v1.y, s, -128.f, 127.f), quant_code(v1.w, s, -128.f, 127.f));
-                *reinterpret_cast<uint2 *>(xs + m * K + 8 * g) = p;
+            am = wave_max_dpp(am);
+            if (lane == 0) red[wave][m] = am;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float am = fmaxf(fmaxf(red[0][m], red[1][m]), fmaxf(red[2][m], red[3][m]));
+            const float s = (am == 0.0f) ? 0.0f : am / 127.0f;
+            sxm[m] = s;
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                const int g = t + 256 * i;
+                if (g < G8) {
+                    const float4 v0 = xa[m][i], v1 = xb[m][i];
+                    uint2 p;
+                    p.x = pack4_i8(quant_code(v0.x, s, -128.f, 127.f), quant_code(v0.z, s, -128.f, 127.f),
+                                   quant_code(v1.x, s, -128.f, 127.f), quant_code(v1.z, s, -128.f, 127.f));
+                    p.y = pack4_i8(quant_code(v0.y, s, -128.f, 127.f), quant_code(v0.w, s, -128.f, 127.f),
+                                   quant_code(v1.y, s, -128.f, 127.f), quant_code(v1.w, s, -128.f, 127.f));
+                    *reinterpret_cast<uint2 *>(xs + m * K + 8 * g) = p;
+                }
             }
         }
     } else {
+#pragma unroll
         for (int m = 0; m < M; ++m) {
-            const uint2 *src = reinterpret_cast<const uint2 *>(a.Xq + (int64_t)m * K);
-            for (int g = threadIdx.x; g < ng; g += 256) {
-                uint2 v = src[g], p;
-                natural_to_p8(v.x, v.y, p.x, p.y);
-                *reinterpret_cast<uint2 *>(xs + m * K + 8 * g) = p;
+            sxm[m] = (OUT == Out::Y) ? a.sx[m] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                const int g = t + 256 * i;
+                if (g < G8) {
+                    uint2 p;
+                    natural_to_p8(xn[m][i].x, xn[m][i].y, p.x, p.y);
+                    *reinterpret_cast<uint2 *>(xs + m * K + 8 * g) = p;
+                }
             }
-            if (threadIdx.x == 0) sxs[m] = (OUT == Out::Y) ? a.sx[m] : 0.0f;
         }
     }
     __syncthreads();
 
+    // (4) int8 dot products of 16*code with the P8 activations.
     int acc[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[m] = 0;
-
     for (int base = 0; base < C; base += 16 * kDot4Batch) {
         uint4 cur[kDot4Batch];
 #pragma unroll
@@ -96,70 +144,71 @@ __global__ __launch_bounds__(256) void k_gemv_dot4(W4A8Args a) {
 #pragma unroll
             for (int u = 0; u < kDot4Batch; ++u) {
                 const int c = base + 16 * kDot4Batch + j + 16 * u;
-                wb[u] = (valid && c < C) ? prow[c] : make_uint4(0, 0, 0, 0);
+                wb[u] = bload16(rw, c < C ? rowoff + 16 * c : kOOB);
             }
         }
 #pragma unroll
         for (int u = 0; u < kDot4Batch; ++u) {
-            const int c = base + j + 16 * u;
-            if (c < C) {
-                const uint32_t l0 = lo16(cur[u].x), h0 = hi16(cur[u].x);
-                const uint32_t l1 = lo16(cur[u].y), h1 = hi16(cur[u].y);
-                const uint32_t l2 = lo16(cur[u].z), h2 = hi16(cur[u].z);
-                const uint32_t l3 = lo16(cur[u].w), h3 = hi16(cur[u].w);
+            // Past the end of the row the weights are zero; clamp the LDS read.
+            const int cx = min(base + j + 16 * u, C - 1);
+            const uint32_t l0 = lo16(cur[u].x), h0 = hi16(cur[u].x);
+            const uint32_t l1 = lo16(cur[u].y), h1 = hi16(cur[u].y);
+            const uint32_t l2 = lo16(cur[u].z), h2 = hi16(cur[u].z);
+            const uint32_t l3 = lo16(cur[u].w), h3 = hi16(cur[u].w);
 #pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    const uint4 *xp = reinterpret_cast<const uint4 *>(xs + m * K + c * 32);
-                    const uint4 x0 = xp[0], x1 = xp[1];
-                    int t = acc[m];
-                    t = __builtin_amdgcn_sdot4((int)l0, (int)x0.x, t, false);
-                    t = __builtin_amdgcn_sdot4((int)h0, (int)x0.y, t, false);
-                    t = __builtin_amdgcn_sdot4((int)l1, (int)x0.z, t, false);
-                    t = __builtin_amdgcn_sdot4((int)h1, (int)x0.w, t, false);
-                    t = __builtin_amdgcn_sdot4((int)l2, (int)x1.x, t, false);
-                    t = __builtin_amdgcn_sdot4((int)h2, (int)x1.y, t, false);
-                    t = __builtin_amdgcn_sdot4((int)l3, (int)x1.z, t, false);
-                    t = __builtin_amdgcn_sdot4((int)h3, (int)x1.w, t, false);
-                    acc[m] = t;
-                }
+            for (int m = 0; m < M; ++m) {
+                const uint4 *xp = reinterpret_cast<const uint4 *>(xs + m * K + cx * 32);
+                const uint4 x0 = xp[0], x1 = xp[1];
+                int s = acc[m];
+                s = __builtin_amdgcn_sdot4((int)l0, (int)x0.x, s, false);
+                s = __builtin_amdgcn_sdot4((int)h0, (int)x0.y, s, false);
+                s = __builtin_amdgcn_sdot4((int)l1, (int)x0.z, s, false);
+                s = __builtin_amdgcn_sdot4((int)h1, (int)x0.w, s, false);
+                s = __builtin_amdgcn_sdot4((int)l2, (int)x1.x, s, false);
+                s = __builtin_amdgcn_sdot4((int)h2, (int)x1.y, s, false);
+                s = __builtin_amdgcn_sdot4((int)l3, (int)x1.z, s, false);
+                s = __builtin_amdgcn_sdot4((int)h3, (int)x1.w, s, false);
+                acc[m] = s;
             }
         }
     }
 
+    // (5) sum the 16 lanes of each channel; divide out the 16 of the codes.
+    const int64_t n = n0 + r;
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-        int t = acc[m];
-        t += __shfl_xor(t, 8, kWave);
-        t += __shfl_xor(t, 4, kWave);
-        t += __shfl_xor(t, 2, kWave);
-        t += __shfl_xor(t, 1, kWave);
-        acc[m] = t >> 4;  // undo the x16 of the unpacked weights (exact)
-    }
-    if (j == 0 && valid) {
+    for (int m = 0; m < M; ++m) acc[m] = sum16(acc[m]) >> 4;
+    if (j == 0 && r < rows) {
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             if (OUT == Out::I32)
                 a.acc[(int64_t)m * a.N + n] = acc[m];
             else
-                a.Y[(int64_t)m * a.N + n] = dequant(acc[m], sxs[m], a.sw[n], a.bias, (int)n);
+                a.Y[(int64_t)m * a.N + n] = dequant(acc[m], sxm[m], a.sw[n], a.bias, (int)n);
         }
     }
 }
 
-template <int M, bool FUSED, Out OUT>
+template <int M, int NG>
 static void go_dot4(const W4A8Args &a, hipStream_t st) {
     dim3 grid((unsigned)((a.N + kDot4Rows - 1) / kDot4Rows));
-    hipLaunchKernelGGL((k_gemv_dot4<M, FUSED, OUT>), grid, dim3(256), (size_t)(M * a.K), st, a);
+    const uint32_t shm = (uint32_t)(M * a.K);
+    if (a.out == Out::I32)
+        launch_main(k_gemv_dot4<M, NG, false, Out::I32>, grid, dim3(256), shm, st, a);
+    else if (a.X)
+        launch_main(k_gemv_dot4<M, NG, true, Out::Y>, grid, dim3(256), shm, st, a);
+    else
+        launch_main(k_gemv_dot4<M, NG, false, Out::Y>, grid, dim3(256), shm, st, a);
 }
 
 template <int M>
 static void go_dot4_m(const W4A8Args &a, hipStream_t st) {
-    if (a.out == Out::I32)
-        go_dot4<M, false, Out::I32>(a, st);
-    else if (a.X)
-        go_dot4<M, true, Out::Y>(a, st);
+    const int64_t g8 = a.K / 8;
+    if (g8 <= 256)
+        go_dot4<M, 1>(a, st);
+    else if (g8 <= 512)
+        go_dot4<M, 2>(a, st);
     else
-        go_dot4<M, false, Out::Y>(a, st);
+        go_dot4<M, 4>(a, st);
 }
 
 hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st) {
@@ -182,32 +231,30 @@ hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st) {
 // lane).  The weight and activation operands use identical k slots per lane,
 // so the order in which the MFMA consumes the slots does not matter.
 // Accumulator layout (16x16 i32): lane l holds rows 4*(l/16)+i, column l%16.
+// Weights and activations of the next D steps are in flight in a register
+// ring while the current step multiplies.  Rows past M and channels past N
+// read zeros (their outputs are not stored).
 template <int MB, int NB, int D, Out OUT>
 __global__ __launch_bounds__(256) void k_gemv_mfma(W4A8Args a) {
     __shared__ v4i red[3][MB * NB][kWave];
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    // wave-uniform (scalar) so the K-range loop branches are scalar branches
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
     const int r16 = lane % 16, kq = lane / 16;
-    const int64_t K = a.K, KB = a.K / 2, N = a.N, M = a.M;
-    const int64_t S = K / 128;
-    const int64_t s0 = S * wave / 4, s1 = S * (wave + 1) / 4;
+    const int K = (int)a.K, KB = K / 2;
+    const int64_t N = a.N, M = a.M;
+    const int S = K / 128;
+    const int s0 = S * wave / 4, s1 = S * (wave + 1) / 4;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * NB;
+    const int cols = (int)min((int64_t)(16 * NB), N - n0);
 
-    const uint8_t *bp[NB];
-    bool bv[NB];
+    const auto rb = make_rsrc(a.packed + n0 * KB, (int64_t)cols * KB);
+    const auto ra = make_rsrc(a.Xq, M * K);
+    int boff[NB], aoff[MB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int64_t col = n0 + 16 * nb + r16;
-        bv[nb] = col < N;
-        bp[nb] = a.packed + (bv[nb] ? col : 0) * KB + kq * 16;
-    }
-    const int8_t *ap[MB];
-    bool av[MB];
+    for (int nb = 0; nb < NB; ++nb) boff[nb] = (16 * nb + r16) * KB + kq * 16;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int64_t row = 16 * mb + r16;
-        av[mb] = row < M;
-        ap[mb] = a.Xq + (av[mb] ? row : 0) * K + kq * 32;
-    }
+    for (int mb = 0; mb < MB; ++mb) aoff[mb] = (16 * mb + r16) * K + kq * 32;
 
     v4i acc[MB][NB];
 #pragma unroll
@@ -215,54 +262,53 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(W4A8Args a) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = v4i{0, 0, 0, 0};
 
-    uint4 wbuf[D][NB];
+    uint4 wr[D][NB], xr0[D][MB], xr1[D][MB];
+    auto fetch = [&](int d, int ss) {
+        const bool ok = ss < s1;
 #pragma unroll
-    for (int d = 0; d < D; ++d)
+        for (int nb = 0; nb < NB; ++nb) wr[d][nb] = bload16(rb, ok ? boff[nb] + 64 * ss : kOOB);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            wbuf[d][nb] = (s0 + d < s1 && bv[nb])
-                              ? *reinterpret_cast<const uint4 *>(bp[nb] + (s0 + d) * 64)
-                              : make_uint4(0, 0, 0, 0);
+        for (int mb = 0; mb < MB; ++mb) {
+            const int o = ok ? aoff[mb] + 128 * ss : kOOB;
+            xr0[d][mb] = bload16(ra, o);
+            xr1[d][mb] = bload16(ra, o + 16);
+        }
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        fetch(d, s0 + d);
+        __builtin_amdgcn_sched_barrier(0);  // slot 0 oldest, as in the loop below
+    }
 
-    for (int64_t s = s0; s < s1; s += D) {
+    // Each ring slot keeps its registers: its data is consumed (unpacked /
+    // fed to the MFMAs) before the slot is refilled with the step D ahead.
+    // The body has no per-step branch: steps past s1 hold zeros (out-of-range
+    // loads) and add nothing, which keeps the vmcnt bookkeeping exact.
+    for (int s = s0; s < s1; s += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const int64_t ss = s + d;
-            if (ss < s1) {
-                uint4 x0[MB], x1[MB];
+            {
+                v4i b0[NB], b1[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const uint4 w = wr[d][nb];
+                    b0[nb] = v4i{(int)lo16(w.x), (int)hi16(w.x), (int)lo16(w.y), (int)hi16(w.y)};
+                    b1[nb] = v4i{(int)lo16(w.z), (int)hi16(w.z), (int)lo16(w.w), (int)hi16(w.w)};
+                }
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
-                    if (av[mb]) {
-                        const uint4 *xp = reinterpret_cast<const uint4 *>(ap[mb] + ss * 128);
-                        x0[mb] = xp[0];
-                        x1[mb] = xp[1];
-                    } else {
-                        x0[mb] = x1[mb] = make_uint4(0, 0, 0, 0);
+                    const uint4 x0 = xr0[d][mb], x1 = xr1[d][mb];
+                    const v4i a0 = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
+                    const v4i a1 = {(int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0[nb], acc[mb][nb], 0, 0, 0);
+                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1[nb], acc[mb][nb], 0, 0, 0);
                     }
                 }
-                uint4 w[NB];
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    w[nb] = wbuf[d][nb];
-                    const int64_t sn = ss + D;
-                    wbuf[d][nb] = (sn < s1 && bv[nb])
-                                      ? *reinterpret_cast<const uint4 *>(bp[nb] + sn * 64)
-                                      : make_uint4(0, 0, 0, 0);
-                }
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const v4i b0 = {(int)lo16(w[nb].x), (int)hi16(w[nb].x), (int)lo16(w[nb].y),
-                                    (int)hi16(w[nb].y)};
-                    const v4i b1 = {(int)lo16(w[nb].z), (int)hi16(w[nb].z), (int)lo16(w[nb].w),
-                                    (int)hi16(w[nb].w)};
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) {
-                        const v4i a0 = {(int)x0[mb].x, (int)x0[mb].y, (int)x0[mb].z, (int)x0[mb].w};
-                        const v4i a1 = {(int)x1[mb].x, (int)x1[mb].y, (int)x1[mb].z, (int)x1[mb].w};
-                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc[mb][nb], 0, 0, 0);
-                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc[mb][nb], 0, 0, 0);
-                    }
-                }
+                fetch(d, s + d + D);
+                // keep the refill of this slot ahead of the next slot's math
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -301,16 +347,16 @@ template <int MB, int NB, int D>
 static void go_mfma(const W4A8Args &a, hipStream_t st) {
     dim3 grid((unsigned)((a.N + 16 * NB - 1) / (16 * NB)));
     if (a.out == Out::I32)
-        hipLaunchKernelGGL((k_gemv_mfma<MB, NB, D, Out::I32>), grid, dim3(256), 0, st, a);
+        launch_main(k_gemv_mfma<MB, NB, D, Out::I32>, grid, dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((k_gemv_mfma<MB, NB, D, Out::Y>), grid, dim3(256), 0, st, a);
+        launch_main(k_gemv_mfma<MB, NB, D, Out::Y>, grid, dim3(256), 0, st, a);
 }
 
 hipError_t launch_gemv_mfma(const W4A8Args &a, hipStream_t st) {
     const int mb = (int)((a.M + 15) / 16);
     switch (mb) {
         case 1: go_mfma<1, 2, 4>(a, st); break;
-        case 2: go_mfma<2, 2, 4>(a, st); break;
+        case 2: go_mfma<2, 2, 3>(a, st); break;
         case 3: go_mfma<3, 2, 2>(a, st); break;
         default: go_mfma<4, 2, 2>(a, st); break;
     }

@@ -37,8 +37,8 @@ __global__ __launch_bounds__(256) void k_w4a8_generic(const int8_t *__restrict__
 
 hipError_t launch_w4a8_generic(const W4A8Args &a, hipStream_t st) {
     dim3 g((unsigned)((a.N + 255) / 256), (unsigned)(a.M < 65535 ? a.M : 65535));
-    hipLaunchKernelGGL(k_w4a8_generic, g, dim3(256), 0, st, a.Xq, a.sx, a.packed, a.sw, a.bias,
-                       a.Y, a.out == Out::I32 ? a.acc : nullptr, a.M, a.K, a.N);
+    launch_main(k_w4a8_generic, g, dim3(256), 0, st, a.Xq, a.sx, a.packed, a.sw, a.bias, a.Y,
+                a.out == Out::I32 ? a.acc : nullptr, a.M, a.K, a.N);
     return hipGetLastError();
 }
 
@@ -79,8 +79,7 @@ hipError_t launch_w4a16_generic(const uint16_t *X, int64_t M, int64_t K, int64_t
                                 const uint8_t *packed, const float *scales, const float *zeros,
                                 int64_t group, float *Y, hipStream_t st) {
     dim3 g((unsigned)((N + 255) / 256), (unsigned)(M < 65535 ? M : 65535));
-    hipLaunchKernelGGL(k_w4a16_generic, g, dim3(256), 0, st, X, packed, scales, zeros, Y, M, K,
-                       N, group);
+    launch_main(k_w4a16_generic, g, dim3(256), 0, st, X, packed, scales, zeros, Y, M, K, N, group);
     return hipGetLastError();
 }
 

@@ -3,10 +3,31 @@
 // runs; each launcher only enqueues work on `st` and returns hipGetLastError().
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace w4 {
+
+// Optional start/stop events for the next product kernel (per host thread);
+// taking them clears them.
+struct TimingEvents {
+    hipEvent_t start;
+    hipEvent_t stop;
+};
+TimingEvents take_timing_events();
+
+// Launch a product kernel; if timing events are pending they are attached to
+// this dispatch (recorded when the kernel starts and when it completes).
+template <typename... KArgs, typename... Args>
+inline void launch_main(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shm,
+                        hipStream_t st, Args... args) {
+    const TimingEvents ev = take_timing_events();
+    if (ev.start || ev.stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, shm, st, ev.start, ev.stop, 0u, KArgs(args)...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, shm, st, KArgs(args)...);
+}
 
 // Which accumulation product a W4A8 kernel writes.
 enum class Out { Y, I32 };

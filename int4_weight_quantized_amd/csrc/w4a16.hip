@@ -63,86 +63,90 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t *__restrict__
                                                     const uint8_t *__restrict__ packed,
                                                     const float *__restrict__ scales,
                                                     const float *__restrict__ zeros,
-                                                    float *__restrict__ Y, int64_t M, int64_t K,
+                                                    float *__restrict__ Y, int64_t M, int64_t K64,
                                                     int64_t N, int64_t group) {
     __shared__ v4f red[3][NB][kWave];
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
     const int r16 = lane % 16, kq = lane / 16;
-    const int64_t KB = K / 2, G = K / group;
-    const int64_t S = K / 128;
-    const int64_t s0 = S * wave / 4, s1 = S * (wave + 1) / 4;
+    const int K = (int)K64, KB = K / 2, G = (int)(K64 / group);
+    const int S = K / 128;
+    const int s0 = S * wave / 4, s1 = S * (wave + 1) / 4;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * NB;
     const int64_t m0 = (int64_t)blockIdx.y * 16;
+    const int cols = (int)min((int64_t)(16 * NB), N - n0);
+    const int rowsm = (int)min((int64_t)16, M - m0);
 
-    const uint8_t *bp[NB];
-    const float *sp[NB], *zpp[NB];
-    bool bv[NB];
+    // Descriptors cover exactly this block's channels / rows: channels past N
+    // and rows past M read zeros (their outputs are not stored).
+    const auto rb = make_rsrc(packed + n0 * KB, (int64_t)cols * KB);
+    const auto rs = make_rsrc(scales + n0 * G, (int64_t)cols * G * 4);
+    const auto rz = make_rsrc(zeros + n0 * G, (int64_t)cols * G * 4);
+    const auto rx = make_rsrc(X + m0 * K, (int64_t)rowsm * K * 2);
+    int boff[NB], goff[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        const int64_t col = n0 + 16 * nb + r16;
-        bv[nb] = col < N;
-        const int64_t c = bv[nb] ? col : 0;
-        bp[nb] = packed + c * KB + kq * 16;
-        sp[nb] = scales + c * G;
-        zpp[nb] = zeros + c * G;
+        boff[nb] = (16 * nb + r16) * KB + kq * 16;
+        goff[nb] = (16 * nb + r16) * G * 4;
     }
-    const int64_t row = m0 + r16;
-    const bool xv = row < M;
-    const uint16_t *xp = X + (xv ? row : 0) * K + kq * 32;
+    const int xoff = r16 * K * 2 + kq * 64;
 
     v4f acc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[nb] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    uint4 wbuf[D][NB];
+    uint4 wr[D][NB], xr[D][4];
+    float sr[D][NB], zr[D][NB];
+    auto fetch = [&](int d, int ss) {
+        const bool ok = ss < s1;
+        const int g = (ss * 128 + kq * 32) / (int)group;
 #pragma unroll
-    for (int d = 0; d < D; ++d)
+        for (int nb = 0; nb < NB; ++nb) {
+            wr[d][nb] = bload16(rb, ok ? boff[nb] + 64 * ss : kOOB);
+            sr[d][nb] = bloadf(rs, ok ? goff[nb] + 4 * g : kOOB);
+            zr[d][nb] = bloadf(rz, ok ? goff[nb] + 4 * g : kOOB);
+        }
+        const int xo = ok ? xoff + 256 * ss : kOOB;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            wbuf[d][nb] = (s0 + d < s1 && bv[nb])
-                              ? *reinterpret_cast<const uint4 *>(bp[nb] + (s0 + d) * 64)
-                              : make_uint4(0, 0, 0, 0);
+        for (int q = 0; q < 4; ++q) xr[d][q] = bload16(rx, xo + 16 * q);
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        fetch(d, s0 + d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
-    for (int64_t s = s0; s < s1; s += D) {
+    // No per-step branch: steps past s1 read zeros and add nothing.
+    for (int s = s0; s < s1; s += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const int64_t ss = s + d;
-            if (ss < s1) {
-                uint4 xa[4];
+            v4i b[NB][4];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const float sc = sr[d][nb], zp = zr[d][nb];
+                const bool ok = (zp >= -112.0f) && (zp <= 128.0f) && (fabsf(sc) < 0x1p100f);
+                // wave-uniform choice, so only one of the two paths executes
+                const bool fast = __all(ok) != 0;
+                const uint32_t cadd = (ok ? (uint32_t)(128 - (int)zp) : 0u) * 0x01010101u;
+                const float nbias = -128.0f * sc;
+                const uint4 w = wr[d][nb];
+                b[nb][0] = dequant8(w.x, sc, zp, cadd, nbias, fast);
+                b[nb][1] = dequant8(w.y, sc, zp, cadd, nbias, fast);
+                b[nb][2] = dequant8(w.z, sc, zp, cadd, nbias, fast);
+                b[nb][3] = dequant8(w.w, sc, zp, cadd, nbias, fast);
+            }
+            uint4 x[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x[q] = xr[d][q];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    xa[q] = xv ? reinterpret_cast<const uint4 *>(xp + ss * 128)[q]
-                               : make_uint4(0, 0, 0, 0);
-                const int64_t g = (ss * 128 + kq * 32) / group;
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const uint4 w = wbuf[d][nb];
-                    const int64_t sn = ss + D;
-                    wbuf[d][nb] = (sn < s1 && bv[nb])
-                                      ? *reinterpret_cast<const uint4 *>(bp[nb] + sn * 64)
-                                      : make_uint4(0, 0, 0, 0);
-                    const float sc = sp[nb][g];
-                    const float zp = zpp[nb][g];
-                    const bool ok = (zp >= -112.0f) && (zp <= 128.0f) && (fabsf(sc) < 0x1p100f);
-                    // wave-uniform choice, so only one of the two paths executes
-                    const bool fast = __all(ok) != 0;
-                    const uint32_t cb = ok ? (uint32_t)(128 - (int)zp) : 0u;
-                    const uint32_t cadd = cb * 0x01010101u;
-                    const float nbias = -128.0f * sc;
-                    const v4i b0 = dequant8(w.x, sc, zp, cadd, nbias, fast);
-                    const v4i b1 = dequant8(w.y, sc, zp, cadd, nbias, fast);
-                    const v4i b2 = dequant8(w.z, sc, zp, cadd, nbias, fast);
-                    const v4i b3 = dequant8(w.w, sc, zp, cadd, nbias, fast);
                     acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(v8bf, xa[0]), __builtin_bit_cast(v8bf, b0), acc[nb], 0, 0, 0);
-                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(v8bf, xa[1]), __builtin_bit_cast(v8bf, b1), acc[nb], 0, 0, 0);
-                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(v8bf, xa[2]), __builtin_bit_cast(v8bf, b2), acc[nb], 0, 0, 0);
-                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(v8bf, xa[3]), __builtin_bit_cast(v8bf, b3), acc[nb], 0, 0, 0);
-                }
-            }
+                        __builtin_bit_cast(v8bf, x[q]), __builtin_bit_cast(v8bf, b[nb][q]), acc[nb], 0,
+                        0, 0);
+            fetch(d, s + d + D);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -173,8 +177,8 @@ hipError_t launch_w4a16_mfma(const uint16_t *X, int64_t M, int64_t K, int64_t N,
     for (int64_t mb0 = 0; mb0 < mblocks; mb0 += 65535) {
         const int64_t cnt = (mblocks - mb0) < 65535 ? (mblocks - mb0) : 65535;
         dim3 grid((unsigned)((N + 16 * NB - 1) / (16 * NB)), (unsigned)cnt);
-        hipLaunchKernelGGL((k_w4a16_mfma<NB, D>), grid, dim3(256), 0, st, X + mb0 * 16 * K, packed,
-                           scales, zeros, Y + mb0 * 16 * N, M - mb0 * 16, K, N, group);
+        launch_main(k_w4a16_mfma<NB, D>, grid, dim3(256), 0, st, X + mb0 * 16 * K, packed, scales,
+                    zeros, Y + mb0 * 16 * N, M - mb0 * 16, K, N, group);
     }
     return hipGetLastError();
 }
