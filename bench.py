@@ -94,7 +94,7 @@ def w4a16_bytes(M, K, N, g):
 
 
 class W4A8Case:
-    def __init__(self, w4, torch, name, shape_name, M, rotate=True):
+    def __init__(self, w4, torch, name, shape_name, M, rotate=True, copies=None):
         import workloads
         d = workloads.generate(shape_name, M=M)
         self.name, self.M, self.K, self.N = name, M if M else d["M"], d["K"], d["N"]
@@ -109,6 +109,8 @@ class W4A8Case:
         del W
         wbytes = p.numel() + 4 * s.numel()
         self.copies = max(1, math.ceil(ROTATE_BYTES / wbytes)) if rotate else 2
+        if copies:
+            self.copies = copies
         self.P = [p] + [p.clone() for _ in range(self.copies - 1)]
         self.S = [s] + [s.clone() for _ in range(self.copies - 1)]
         self.y = torch.empty((self.M, self.N), dtype=torch.float32, device=dev)
@@ -124,7 +126,7 @@ class W4A8Case:
 
 
 class W4A16Case:
-    def __init__(self, w4, torch):
+    def __init__(self, w4, torch, copies=None):
         import numpy as np
         import workloads
         d = workloads.w4a16_inputs()
@@ -140,7 +142,7 @@ class W4A16Case:
         self.quant_s = time.perf_counter() - t0
         del W
         wbytes = p.numel() + 8 * s.numel()
-        self.copies = max(1, math.ceil(ROTATE_BYTES / wbytes))
+        self.copies = copies or max(1, math.ceil(ROTATE_BYTES / wbytes))
         self.P = [p] + [p.clone() for _ in range(self.copies - 1)]
         self.Sc = [s] + [s.clone() for _ in range(self.copies - 1)]
         self.Z = [z] + [z.clone() for _ in range(self.copies - 1)]
@@ -247,6 +249,9 @@ def main():
                          "mlp7b_m1, mlp7b_m16, mlp7b_m64, prefill, w4a16; or copy (a 64 MiB "
                          "device copy, for counter calibration)")
     ap.add_argument("--launches", type=int, default=200)
+    ap.add_argument("--copies", type=int, default=0,
+                    help="with --only: number of rotating weight copies (0 = enough to exceed "
+                         "the Infinity Cache)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -273,8 +278,8 @@ def main():
         specs = {"gemma_m1": ("gemma", 1), "gemma_m8": ("gemma", 8), "mlp7b_m1": ("mlp7b", 1),
                  "mlp7b_m16": ("mlp7b", 16), "mlp7b_m64": ("mlp7b", 64),
                  "prefill": ("prefill", None)}
-        case = (W4A16Case(w4, torch) if args.only == "w4a16"
-                else W4A8Case(w4, torch, args.only, *specs[args.only]))
+        case = (W4A16Case(w4, torch, copies=args.copies) if args.only == "w4a16"
+                else W4A8Case(w4, torch, args.only, *specs[args.only], copies=args.copies))
         for i in range(args.warmup + args.steps):
             case.step(i)
         torch.cuda.synchronize()

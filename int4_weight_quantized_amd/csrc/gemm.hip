@@ -1,137 +1,179 @@
 // Prefill-shaped W4A8 product (many activation rows): int8 MFMA GEMM with
 // LDS-staged tiles (Keras INT4 guide, "How it works", steps 4-6).
 //
-// Block tile 128 (rows) x 128 (output channels) x 128 (k); 4 waves in a 2x2
-// arrangement, each owning a 64x64 sub-tile = 4x4 blocks of
-// v_mfma_i32_16x16x64_i8.  Per k-tile the block stages
-//   A: 128 rows x 128 int8 activations (P8 layout)  -> LDS, row pitch 144 B
-//   B: 128 channels x 64 packed bytes (128 codes)   -> LDS, row pitch 80 B
-// (the pitches keep the 16-byte LDS reads of 8 consecutive lanes on distinct
-// banks).  Each wave unpacks its B fragments in registers; the next k-tile is
-// fetched into registers while the current one is multiplied (two LDS
-// buffers, one barrier per k-tile).
+// Block tile 256 (rows) x 256 (output channels) x 128 (k), 8 waves in a 2x4
+// arrangement, each owning a 128x64 sub-tile = 8x4 blocks of
+// v_mfma_i32_16x16x64_i8 (accumulators in AGPRs).
+//
+// Per k-tile the block stages
+//   A: 256 rows x 128 int8 activations (P8 layout)  = 32 KB
+//   B: 256 channels x 64 packed bytes (128 codes)   = 16 KB
+// in one stage of a 3-stage LDS ring, using direct global->LDS loads
+// (global_load_lds_dwordx4: lane L of a wave writes LDS[base + 16 L]), so the
+// tile after next is in flight while the current one is multiplied.  Rows
+// are stored without padding; the 16-byte chunk position inside each row is
+// XOR-swizzled so that the fragment reads of 8 consecutive lanes hit 8
+// distinct bank groups.  Each wave unpacks its packed B fragments in
+// registers (16 * code as int8) and the int32 sums are divided by 16 in the
+// epilogue, which also applies the dequantization.
 #include "common.h"
 #include "kernels.h"
 
 namespace w4 {
 
-constexpr int kBM = 128, kBN = 128, kBK = 128;
-constexpr int kAP = kBK + 16;      // A row pitch (bytes)
-constexpr int kBP = kBK / 2 + 16;  // B row pitch (bytes)
+constexpr int kBM = 256, kBN = 256, kBK = 128, kStages = 3;
+constexpr int kABytes = kBM * kBK;       // 32 KB
+constexpr int kBBytes = kBN * kBK / 2;   // 16 KB
+constexpr int kStageBytes = kABytes + kBBytes;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until at most N of this wave's vector-memory operations (here: the
+// direct global->LDS loads) are outstanding and all its LDS operations are
+// done, then join the workgroup barrier.  The "memory" clobber keeps the
+// compiler from moving LDS accesses across it.  (The fences of
+// __syncthreads would instead drain every outstanding direct load.)
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+    static_assert(N >= 0 && N < 16, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 template <Out OUT>
-__global__ __launch_bounds__(256) void k_gemm_mfma(W4A8Args a) {
-    __shared__ __align__(16) uint8_t As[2][kBM * kAP];
-    __shared__ __align__(16) uint8_t Bs[2][kBN * kBP];
+__global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
+    // One array per ring stage: each unrolled iteration below names its
+    // stages statically, so the compiler can tell the stage being read from
+    // the stages being filled.
+    __shared__ __align__(16) uint8_t stage0[kStageBytes];
+    __shared__ __align__(16) uint8_t stage1[kStageBytes];
+    __shared__ __align__(16) uint8_t stage2[kStageBytes];
 
     const int64_t M = a.M, N = a.N, K = a.K, KB = a.K / 2;
     const int tiles_n = (int)((N + kBN - 1) / kBN);
-    const int nblk = gridDim.x;
-    const int tile = xcd_swizzle(blockIdx.x, nblk);
+    const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
     const int64_t m0 = (int64_t)(tile / tiles_n) * kBM;
     const int64_t n0 = (int64_t)(tile % tiles_n) * kBN;
 
     const int t = threadIdx.x;
-    const int wave = t / kWave, lane = t % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+    const int lane = t % kWave;
     const int r16 = lane % 16, kq = lane / 16;
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / 4, wn = wave % 4;
 
-    // Global -> register staging assignment (raw buffer loads; the
-    // descriptors cover this tile's rows / channels, so rows past M and
-    // channels past N read zeros and their outputs are not stored).
-    // A: 1024 16-byte pieces: piece p = t + 256*i -> row p/8, column (p%8)*16.
-    // B: 512 pieces: piece p = t + 256*i -> channel p/4, bytes (p%4)*16.
-    const int Ki = (int)K, KBi = (int)KB;
+    // ---- direct-load sources (buffer loads that write LDS; rows past M and
+    // channels past N are outside the descriptors and read as zeros).
+    // A: 32 wave-loads of 8 rows x 128 B; this wave issues q = 4*wave + i, i.e.
+    // rows 32*wave + 8*i + lane/8.  Stored chunk position lane%8 of a row holds
+    // the row's global chunk (lane%8) ^ (lane/8).
     const auto ra = make_rsrc(a.Xq + m0 * K, min((int64_t)kBM, M - m0) * K);
+    const int a_voff = (32 * wave + lane / 8) * (int)K + (((lane % 8) ^ (lane / 8)) * 16);
+    // B: 16 wave-loads of 16 channels x 64 B; this wave issues q = 2*wave + i,
+    // i.e. channels 32*wave + 16*i + lane/4.  Stored position lane%4 holds the
+    // channel's global chunk (lane%4) ^ ((lane/8)%4).
     const auto rbs = make_rsrc(a.packed + n0 * KB, min((int64_t)kBN, N - n0) * KB);
-    int aoff[4], boff[2];
+    const int b_voff = (32 * wave + lane / 4) * (int)KB + (((lane % 4) ^ ((lane / 8) % 4)) * 16);
+    auto issue = [&](uint8_t *st, int kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = t + 256 * i;
-        aoff[i] = (p / 8) * Ki + (p % 8) * 16;
-    }
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (lds_void *)(st + (4 * wave + i) * 1024), 16, a_voff,
+                8 * i * (int)K + kt * kBK, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int p = t + 256 * i;
-        boff[i] = (p / 4) * KBi + (p % 4) * 16;
-    }
-
-    uint4 ra_[4], rb_[2];
-    auto fetch = [&](int kt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ra_[i] = bload16(ra, aoff[i] + kt * kBK);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) rb_[i] = bload16(rbs, boff[i] + kt * (kBK / 2));
-    };
-    auto stash = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int p = t + 256 * i;
-            *reinterpret_cast<uint4 *>(&As[buf][(p / 8) * kAP + (p % 8) * 16]) = ra_[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int p = t + 256 * i;
-            *reinterpret_cast<uint4 *>(&Bs[buf][(p / 4) * kBP + (p % 4) * 16]) = rb_[i];
-        }
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rbs, (lds_void *)(st + kABytes + (2 * wave + i) * 1024), 16, b_voff,
+                16 * i * (int)KB + kt * (kBK / 2), 0, 0);
     };
 
-    v4i acc[4][4];
+    // ---- fragment read offsets inside a stage (row block rb adds rb*2048,
+    // channel block nb adds nb*1024).
+    int aoff[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int h = 0; h < 2; ++h)
+        aoff[h] = (wm * 128 + r16) * 128 + (((2 * kq + h) ^ (r16 % 8)) * 16);
+    const int boff = kABytes + (wn * 64 + r16) * 64 + ((kq ^ ((r16 / 2) % 4)) * 16);
+
+    v4i acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-    const int KT = (int)(K / kBK);
-    fetch(0);
-    stash(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = (int)(kt & 1);
-        if (kt + 1 < KT) fetch(kt + 1);
-
-        // B fragments of this wave: 4 channel blocks, 16 packed bytes each.
+    auto compute = [&](const uint8_t *st) {
         v4i b0[4], b1[4];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-            const int c = wn * 64 + nb * 16 + r16;
-            const uint4 w = *reinterpret_cast<const uint4 *>(&Bs[buf][c * kBP + kq * 16]);
+            const uint4 w = *reinterpret_cast<const uint4 *>(st + boff + nb * 1024);
             b0[nb] = v4i{(int)lo16(w.x), (int)hi16(w.x), (int)lo16(w.y), (int)hi16(w.y)};
             b1[nb] = v4i{(int)lo16(w.z), (int)hi16(w.z), (int)lo16(w.w), (int)hi16(w.w)};
         }
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            const int r = wm * 64 + mb * 16 + r16;
-            const uint4 x0 = *reinterpret_cast<const uint4 *>(&As[buf][r * kAP + kq * 32]);
-            const uint4 x1 = *reinterpret_cast<const uint4 *>(&As[buf][r * kAP + kq * 32 + 16]);
-            const v4i a0 = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
-            const v4i a1 = {(int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0[nb], acc[mb][nb], 0, 0, 0);
-                acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1[nb], acc[mb][nb], 0, 0, 0);
+            for (int rb = 0; rb < 8; ++rb) {
+                const uint4 x = *reinterpret_cast<const uint4 *>(st + aoff[h] + rb * 2048);
+                const v4i av = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+                    acc[rb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, h ? b1[nb] : b0[nb],
+                                                                        acc[rb][nb], 0, 0, 0);
             }
         }
-        if (kt + 1 < KT) stash(buf ^ 1);
-        __syncthreads();
-    }
+    };
+    // One ring step: tile kt sits in `cur`; the tile two ahead goes into
+    // `nxt2` (the stage read in the previous step).  Before the barrier this
+    // thread's loads of tile kt must be complete: at most the 6 loads of tile
+    // kt+1 may remain outstanding.  The barrier also guarantees that no wave
+    // still reads `nxt2`.
+    auto step = [&](int kt, int KT, const uint8_t *cur, uint8_t *nxt2) {
+        if (kt + 1 < KT)
+            wait_and_barrier<6>();
+        else
+            wait_and_barrier<0>();
+        if (kt + 2 < KT) issue(nxt2, kt + 2);
+        compute(cur);
+    };
 
+    const int KT = (int)(K / kBK);
+    issue(stage0, 0);
+    if (KT > 1) issue(stage1, 1);
+    int kt = 0;
+    for (; kt + 3 <= KT; kt += 3) {
+        step(kt, KT, stage0, stage2);
+        step(kt + 1, KT, stage1, stage0);
+        step(kt + 2, KT, stage2, stage1);
+    }
+    if (kt < KT) step(kt, KT, stage0, stage2);
+    if (kt + 1 < KT) step(kt + 1, KT, stage1, stage0);
+
+    // ---- epilogue: rows 4*(lane/16)+i of each 16x16 block, column lane%16.
+    float swc[4], bc[4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int nb = 0; nb < 4; ++nb) {
+        const int64_t col = min(n0 + wn * 64 + nb * 16 + r16, N - 1);
+        swc[nb] = (OUT == Out::Y) ? a.sw[col] : 0.0f;
+        bc[nb] = (OUT == Out::Y && a.bias) ? a.bias[col] : 0.0f;
+    }
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const int64_t col = n0 + wn * 64 + nb * 16 + r16;
-            if (col >= N) continue;
+    for (int rb = 0; rb < 8; ++rb) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = m0 + wm * 64 + mb * 16 + 4 * kq + i;
-                if (row >= M) continue;
-                const int v = acc[mb][nb][i] >> 4;
-                if (OUT == Out::I32)
+        for (int i = 0; i < 4; ++i) {
+            const int64_t row = m0 + wm * 128 + rb * 16 + 4 * kq + i;
+            if (row >= M) continue;
+            const float sxr = (OUT == Out::Y) ? a.sx[row] : 0.0f;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                const int64_t col = n0 + wn * 64 + nb * 16 + r16;
+                if (col >= N) continue;
+                const int v = acc[rb][nb][i] >> 4;
+                if (OUT == Out::I32) {
                     a.acc[row * N + col] = v;
-                else
-                    a.Y[row * N + col] = dequant(v, a.sx[row], a.sw[col], a.bias, (int)col);
+                } else {
+                    const float s = sxr * swc[nb];
+                    float y = (float)v * s;
+                    if (a.bias) y = y + bc[nb];
+                    a.Y[row * N + col] = y;
+                }
             }
         }
     }
@@ -140,9 +182,9 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(W4A8Args a) {
 hipError_t launch_gemm_mfma(const W4A8Args &a, hipStream_t st) {
     const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
     if (a.out == Out::I32)
-        launch_main(k_gemm_mfma<Out::I32>, dim3((unsigned)tiles), dim3(256), 0, st, a);
+        launch_main(k_gemm_mfma<Out::I32>, dim3((unsigned)tiles), dim3(512), 0, st, a);
     else
-        launch_main(k_gemm_mfma<Out::Y>, dim3((unsigned)tiles), dim3(256), 0, st, a);
+        launch_main(k_gemm_mfma<Out::Y>, dim3((unsigned)tiles), dim3(512), 0, st, a);
     return hipGetLastError();
 }
 

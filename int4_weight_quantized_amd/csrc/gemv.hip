@@ -66,6 +66,12 @@ __global__ __launch_bounds__(256) void k_gemv_dot4(W4A8Args a) {
             }
     }
 
+    // Epilogue operands early, so their latency hides behind the main loop.
+    const int64_t n = n0 + r;
+    const int64_t nc = r < rows ? n : n0;
+    const float swn = (OUT == Out::Y) ? a.sw[nc] : 0.0f;
+    const float bn = (OUT == Out::Y && a.bias) ? a.bias[nc] : 0.0f;
+
     // (2) weights of this block's rows.
     const auto rw = make_rsrc(a.packed + n0 * KB, (int64_t)rows * KB);
     const int rowoff = r * KB;
@@ -174,16 +180,19 @@ __global__ __launch_bounds__(256) void k_gemv_dot4(W4A8Args a) {
     }
 
     // (5) sum the 16 lanes of each channel; divide out the 16 of the codes.
-    const int64_t n = n0 + r;
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[m] = sum16(acc[m]) >> 4;
     if (j == 0 && r < rows) {
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            if (OUT == Out::I32)
+            if (OUT == Out::I32) {
                 a.acc[(int64_t)m * a.N + n] = acc[m];
-            else
-                a.Y[(int64_t)m * a.N + n] = dequant(acc[m], sxm[m], a.sw[n], a.bias, (int)n);
+            } else {
+                const float s = sxm[m] * swn;
+                float y = (float)acc[m] * s;
+                if (a.bias) y = y + bn;
+                a.Y[(int64_t)m * a.N + n] = y;
+            }
         }
     }
 }
@@ -262,6 +271,22 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(W4A8Args a) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = v4i{0, 0, 0, 0};
 
+    // Epilogue operands early (wave 0 stores): channel scales / bias of this
+    // lane's columns and the row scales of its 4 rows per row block.
+    float swc[NB], bc[NB], sxr[MB][4];
+    if (OUT == Out::Y && wave == 0) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int64_t col = min(n0 + 16 * nb + r16, N - 1);
+            swc[nb] = a.sw[col];
+            bc[nb] = a.bias ? a.bias[col] : 0.0f;
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sxr[mb][i] = a.sx[min((int64_t)(16 * mb + 4 * kq + i), M - 1)];
+    }
+
     uint4 wr[D][NB], xr0[D][MB], xr1[D][MB];
     auto fetch = [&](int d, int ss) {
         const bool ok = ss < s1;
@@ -334,10 +359,14 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(W4A8Args a) {
                 const int64_t row = 16 * mb + 4 * kq + i;
                 if (row >= M) continue;
                 const int v = t[i] >> 4;
-                if (OUT == Out::I32)
+                if (OUT == Out::I32) {
                     a.acc[row * N + col] = v;
-                else
-                    a.Y[row * N + col] = dequant(v, a.sx[row], a.sw[col], a.bias, (int)col);
+                } else {
+                    const float sc = sxr[mb][i] * swc[nb];
+                    float y = (float)v * sc;
+                    if (a.bias) y = y + bc[nb];
+                    a.Y[row * N + col] = y;
+                }
             }
         }
     }
@@ -355,8 +384,8 @@ static void go_mfma(const W4A8Args &a, hipStream_t st) {
 hipError_t launch_gemv_mfma(const W4A8Args &a, hipStream_t st) {
     const int mb = (int)((a.M + 15) / 16);
     switch (mb) {
-        case 1: go_mfma<1, 2, 4>(a, st); break;
-        case 2: go_mfma<2, 2, 3>(a, st); break;
+        case 1: go_mfma<1, 2, 8>(a, st); break;
+        case 2: go_mfma<2, 2, 4>(a, st); break;
         case 3: go_mfma<3, 2, 2>(a, st); break;
         default: go_mfma<4, 2, 2>(a, st); break;
     }

@@ -33,29 +33,39 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
 }
 
 // 8 codes of one packed dword -> 4 dwords of bf16 pairs in natural k order.
-__device__ __forceinline__ v4i dequant8(uint32_t w, float s, float zp, uint32_t cadd, float nbias,
-                                        bool fast) {
-    const uint32_t lo = w & 0x0F0F0F0Fu;         // codes k = 0, 2, 4, 6
-    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes k = 1, 3, 5, 7
+// Fast form (zero point in [-112, 128], see above): bytes 128 + q - z, one
+// fma per code.
+__device__ __forceinline__ v4i dequant8_fast(uint32_t w, float s, uint32_t cadd, float nbias) {
+    const uint32_t lb = (w & 0x0F0F0F0Fu) + cadd;          // k = 0, 2, 4, 6
+    const uint32_t hb = ((w >> 4) & 0x0F0F0F0Fu) + cadd;   // k = 1, 3, 5, 7
     float fl[4], fh[4];
-    if (fast) {
-        const uint32_t lb = lo + cadd, hb = hi + cadd;  // bytes 128 + q - z
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            fl[i] = fmaf((float)((lb >> (8 * i)) & 0xFFu), s, nbias);
-            fh[i] = fmaf((float)((hb >> (8 * i)) & 0xFFu), s, nbias);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float dl = (float)((lo >> (8 * i)) & 0xFFu) - zp;
-            const float dh = (float)((hi >> (8 * i)) & 0xFFu) - zp;
-            fl[i] = dl * s;
-            fh[i] = dh * s;
-        }
+    for (int i = 0; i < 4; ++i) {
+        fl[i] = fmaf((float)((lb >> (8 * i)) & 0xFFu), s, nbias);
+        fh[i] = fmaf((float)((hb >> (8 * i)) & 0xFFu), s, nbias);
     }
     return v4i{(int)pk_bf16(fl[0], fh[0]), (int)pk_bf16(fl[1], fh[1]), (int)pk_bf16(fl[2], fh[2]),
                (int)pk_bf16(fl[3], fh[3])};
+}
+
+// Direct form for any zero point: fl(fl(q - z) * s).
+__device__ __forceinline__ v4i dequant8_direct(uint32_t w, float s, float zp) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    float fl[4], fh[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float dl = (float)((lo >> (8 * i)) & 0xFFu) - zp;
+        const float dh = (float)((hi >> (8 * i)) & 0xFFu) - zp;
+        fl[i] = dl * s;
+        fh[i] = dh * s;
+    }
+    return v4i{(int)pk_bf16(fl[0], fh[0]), (int)pk_bf16(fl[1], fh[1]), (int)pk_bf16(fl[2], fh[2]),
+               (int)pk_bf16(fl[3], fh[3])};
+}
+
+__device__ __forceinline__ v4f mfma_bf16(uint4 a, v4i b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
+                                                   __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
 template <int NB, int D>
@@ -116,35 +126,49 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t *__restrict__
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // No per-step branch: steps past s1 read zeros and add nothing.
+    // No per-step branch: steps past s1 read zeros and add nothing.  One
+    // wave-uniform vote per step picks the dequantization path for all NB
+    // channel blocks; each block is dequantized right before its 4 MFMAs so
+    // only 16 dequantized registers are live at a time.
     for (int s = s0; s < s1; s += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            v4i b[NB][4];
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const float sc = sr[d][nb], zp = zr[d][nb];
-                const bool ok = (zp >= -112.0f) && (zp <= 128.0f) && (fabsf(sc) < 0x1p100f);
-                // wave-uniform choice, so only one of the two paths executes
-                const bool fast = __all(ok) != 0;
-                const uint32_t cadd = (ok ? (uint32_t)(128 - (int)zp) : 0u) * 0x01010101u;
-                const float nbias = -128.0f * sc;
-                const uint4 w = wr[d][nb];
-                b[nb][0] = dequant8(w.x, sc, zp, cadd, nbias, fast);
-                b[nb][1] = dequant8(w.y, sc, zp, cadd, nbias, fast);
-                b[nb][2] = dequant8(w.z, sc, zp, cadd, nbias, fast);
-                b[nb][3] = dequant8(w.w, sc, zp, cadd, nbias, fast);
-            }
-            uint4 x[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) x[q] = xr[d][q];
+            bool ok = true;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
+                ok = ok && (zr[d][nb] >= -112.0f) && (zr[d][nb] <= 128.0f) &&
+                     (fabsf(sr[d][nb]) < 0x1p100f);
+            if (__all(ok)) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(v8bf, x[q]), __builtin_bit_cast(v8bf, b[nb][q]), acc[nb], 0,
-                        0, 0);
+                for (int nb = 0; nb < NB; ++nb) {
+                    const float sc = sr[d][nb];
+                    const uint32_t cadd = (uint32_t)(128 - (int)zr[d][nb]) * 0x01010101u;
+                    const float nbias = -128.0f * sc;
+                    const uint4 w = wr[d][nb];
+                    const v4i b0 = dequant8_fast(w.x, sc, cadd, nbias);
+                    const v4i b1 = dequant8_fast(w.y, sc, cadd, nbias);
+                    const v4i b2 = dequant8_fast(w.z, sc, cadd, nbias);
+                    const v4i b3 = dequant8_fast(w.w, sc, cadd, nbias);
+                    acc[nb] = mfma_bf16(xr[d][0], b0, acc[nb]);
+                    acc[nb] = mfma_bf16(xr[d][1], b1, acc[nb]);
+                    acc[nb] = mfma_bf16(xr[d][2], b2, acc[nb]);
+                    acc[nb] = mfma_bf16(xr[d][3], b3, acc[nb]);
+                }
+            } else {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const float sc = sr[d][nb], zp = zr[d][nb];
+                    const uint4 w = wr[d][nb];
+                    const v4i b0 = dequant8_direct(w.x, sc, zp);
+                    const v4i b1 = dequant8_direct(w.y, sc, zp);
+                    const v4i b2 = dequant8_direct(w.z, sc, zp);
+                    const v4i b3 = dequant8_direct(w.w, sc, zp);
+                    acc[nb] = mfma_bf16(xr[d][0], b0, acc[nb]);
+                    acc[nb] = mfma_bf16(xr[d][1], b1, acc[nb]);
+                    acc[nb] = mfma_bf16(xr[d][2], b2, acc[nb]);
+                    acc[nb] = mfma_bf16(xr[d][3], b3, acc[nb]);
+                }
+            }
             fetch(d, s + d + D);
             __builtin_amdgcn_sched_barrier(0);
         }
