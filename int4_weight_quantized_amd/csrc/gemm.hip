@@ -11,9 +11,8 @@
 // in one stage of a 3-stage LDS ring, using direct global->LDS loads
 // (global_load_lds_dwordx4: lane L of a wave writes LDS[base + 16 L]), so the
 // tile after next is in flight while the current one is multiplied.  Rows
-// are stored without padding; the 16-byte chunk position inside each row is
-// XOR-swizzled so that the fragment reads of 8 consecutive lanes hit 8
-// distinct bank groups.  Each wave unpacks its packed B fragments in
+// are stored without padding, with XOR-swizzled 16-byte chunk positions so
+// that the fragment reads are free of LDS bank conflicts.  Each wave unpacks its packed B fragments in
 // registers (16 * code as int8) and the int32 sums are divided by 16 in the
 // epilogue, which also applies the dequantization.
 #include "common.h"
@@ -62,11 +61,21 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
 
     // ---- direct-load sources (buffer loads that write LDS; rows past M and
     // channels past N are outside the descriptors and read as zeros).
-    // A: 32 wave-loads of 8 rows x 128 B; this wave issues q = 4*wave + i, i.e.
-    // rows 32*wave + 8*i + lane/8.  Stored chunk position lane%8 of a row holds
-    // the row's global chunk (lane%8) ^ (lane/8).
+    // LDS A layout: rows r, r+1 (r even) form a 256-byte super-row; the 16
+    // chunks (row parity p, chunk c) sit at slot ((8p + c) ^ ((r/2) % 8)).  A
+    // 128-bit LDS read is conflict-free when each 16 consecutive lanes use 16
+    // distinct 16-byte slots modulo 256 bytes; the fragment reads (16 rows, one
+    // chunk) do.  A: 32 wave-loads of 4 super-rows (1 KB); this wave issues
+    // q = 4*wave + i.  Lane s fills slot s%16 of super-row 4q + s/16, i.e.
+    // global row 8q + 2(s/16) + (v>>3), chunk v&7, with v = (s%16) ^ ((s/16 + 4q) % 8)
+    // = (s%16) ^ (s/16 + 4*(q%2)) since 4q % 8 = 4*(q%2).
     const auto ra = make_rsrc(a.Xq + m0 * K, min((int64_t)kBM, M - m0) * K);
-    const int a_voff = (32 * wave + lane / 8) * (int)K + (((lane % 8) ^ (lane / 8)) * 16);
+    int a_voff[2];
+#pragma unroll
+    for (int qp = 0; qp < 2; ++qp) {
+        const int v = (lane % 16) ^ (lane / 16 + 4 * qp);
+        a_voff[qp] = (32 * wave + 2 * (lane / 16) + (v >> 3)) * (int)K + (v & 7) * 16;
+    }
     // B: 16 wave-loads of 16 channels x 64 B; this wave issues q = 2*wave + i,
     // i.e. channels 32*wave + 16*i + lane/4.  Stored position lane%4 holds the
     // channel's global chunk (lane%4) ^ ((lane/8)%4).
@@ -76,7 +85,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (lds_void *)(st + (4 * wave + i) * 1024), 16, a_voff,
+                ra, (lds_void *)(st + (4 * wave + i) * 1024), 16, a_voff[i % 2],
                 8 * i * (int)K + kt * kBK, 0, 0);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -86,11 +95,12 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
     };
 
     // ---- fragment read offsets inside a stage (row block rb adds rb*2048,
-    // channel block nb adds nb*1024).
+    // channel block nb adds nb*1024).  A: row r = wm*128 + rb*16 + r16, chunk
+    // 2*kq + h -> super-row r/2, slot (8*(r16%2) + 2kq + h) ^ ((r16/2) % 8).
     int aoff[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-        aoff[h] = (wm * 128 + r16) * 128 + (((2 * kq + h) ^ (r16 % 8)) * 16);
+        aoff[h] = (wm * 64 + r16 / 2) * 256 + (((8 * (r16 % 2) + 2 * kq + h) ^ ((r16 / 2) % 8)) * 16);
     const int boff = kABytes + (wn * 64 + r16) * 64 + ((kq ^ ((r16 / 2) % 4)) * 16);
 
     v4i acc[8][4];
@@ -100,23 +110,28 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
         for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
     auto compute = [&](const uint8_t *st) {
-        v4i b0[4], b1[4];
+        uint4 wraw[4];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const uint4 w = *reinterpret_cast<const uint4 *>(st + boff + nb * 1024);
-            b0[nb] = v4i{(int)lo16(w.x), (int)hi16(w.x), (int)lo16(w.y), (int)hi16(w.y)};
-            b1[nb] = v4i{(int)lo16(w.z), (int)hi16(w.z), (int)lo16(w.w), (int)hi16(w.w)};
-        }
+        for (int nb = 0; nb < 4; ++nb)
+            wraw[nb] = *reinterpret_cast<const uint4 *>(st + boff + nb * 1024);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+            // this half's 16 codes of each channel block, unpacked (16 * code)
+            v4i bh[4];
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                const uint32_t p0 = h ? wraw[nb].z : wraw[nb].x;
+                const uint32_t p1 = h ? wraw[nb].w : wraw[nb].y;
+                bh[nb] = v4i{(int)lo16(p0), (int)hi16(p0), (int)lo16(p1), (int)hi16(p1)};
+            }
 #pragma unroll
             for (int rb = 0; rb < 8; ++rb) {
                 const uint4 x = *reinterpret_cast<const uint4 *>(st + aoff[h] + rb * 2048);
                 const v4i av = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb)
-                    acc[rb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, h ? b1[nb] : b0[nb],
-                                                                        acc[rb][nb], 0, 0, 0);
+                    acc[rb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bh[nb], acc[rb][nb],
+                                                                        0, 0, 0);
             }
         }
     };
@@ -146,7 +161,10 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
     if (kt < KT) step(kt, KT, stage0, stage2);
     if (kt + 1 < KT) step(kt + 1, KT, stage1, stage0);
 
-    // ---- epilogue: rows 4*(lane/16)+i of each 16x16 block, column lane%16.
+    // ---- epilogue.  Dequantize in registers (lane holds rows 4*(lane/16)+i
+    // of each 16x16 block, column lane%16), stage one 16-row block of each
+    // wave's sub-tile at a time in LDS (the ring is free now) and store rows
+    // back contiguously: one store instruction writes 4 rows x 256 bytes.
     float swc[4], bc[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
@@ -154,28 +172,59 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
         swc[nb] = (OUT == Out::Y) ? a.sw[col] : 0.0f;
         bc[nb] = (OUT == Out::Y && a.bias) ? a.bias[col] : 0.0f;
     }
+    constexpr int kPitch = 68;  // words per staged row (64 + 4 pad)
+    static_assert(8 * 16 * kPitch * 4 <= kStageBytes, "staging fits one ring stage");
+    uint32_t *stg = reinterpret_cast<uint32_t *>(stage0) + wave * (16 * kPitch);
+    wait_and_barrier<0>();  // every wave is done reading the ring
+    const int c4 = (lane % 16) * 4;
+    const int64_t col = n0 + wn * 64 + c4;
 #pragma unroll
     for (int rb = 0; rb < 8; ++rb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t row = m0 + wm * 128 + rb * 16 + 4 * kq + i;
-            if (row >= M) continue;
-            const float sxr = (OUT == Out::Y) ? a.sx[row] : 0.0f;
+            const int lr = 4 * kq + i;  // local row 0..15 of this row block
+            const int64_t row = m0 + wm * 128 + rb * 16 + lr;
+            const float sxr = (OUT == Out::Y) ? a.sx[min(row, M - 1)] : 0.0f;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
-                const int64_t col = n0 + wn * 64 + nb * 16 + r16;
-                if (col >= N) continue;
                 const int v = acc[rb][nb][i] >> 4;
+                uint32_t bits;
                 if (OUT == Out::I32) {
-                    a.acc[row * N + col] = v;
+                    bits = (uint32_t)v;
                 } else {
-                    const float s = sxr * swc[nb];
-                    float y = (float)v * s;
+                    const float sc = sxr * swc[nb];
+                    float y = (float)v * sc;
                     if (a.bias) y = y + bc[nb];
-                    a.Y[row * N + col] = y;
+                    bits = __float_as_uint(y);
                 }
+                stg[lr * kPitch + nb * 16 + r16] = bits;
             }
         }
+        // wave-local exchange through LDS: the writes complete before the reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int lr = 4 * it + lane / 16;
+            const int64_t row = m0 + wm * 128 + rb * 16 + lr;
+            const uint4 v = *reinterpret_cast<const uint4 *>(&stg[lr * kPitch + c4]);
+            if (row >= M) continue;
+            uint32_t *dst = (OUT == Out::I32) ? reinterpret_cast<uint32_t *>(a.acc + row * N + col)
+                                              : reinterpret_cast<uint32_t *>(a.Y + row * N + col);
+            if (col + 3 < N && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                *reinterpret_cast<uint4 *>(dst) = v;
+            } else {
+                if (col < N) dst[0] = v.x;
+                if (col + 1 < N) dst[1] = v.y;
+                if (col + 2 < N) dst[2] = v.z;
+                if (col + 3 < N) dst[3] = v.w;
+            }
+        }
+        // the reads above complete before the next row block overwrites
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
