@@ -38,6 +38,30 @@ __device__ __forceinline__ void wait_and_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Raw buffer descriptor (gfx9 layout): 48-bit base, stride 0, byte range,
+// raw-buffer flags.  Reads outside [0, bytes) return zeros.
+__device__ __forceinline__ v4i buffer_desc(const void *base, int64_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const int n = bytes > kMaxRange ? kMaxRange : (int)bytes;
+    return v4i{(int)(uint32_t)p, (int)(uint32_t)((p >> 32) & 0xFFFFu), n, kBufFlags};
+}
+
+// One 16-byte buffer load per lane that writes LDS (lane L of the wave writes
+// LDS[lds_base + 16 L]).  Written as inline asm so that the compiler's
+// wait-count pass, which cannot tell which ring stage such a load fills,
+// does not drain all outstanding loads before every LDS read; all waits for
+// these loads are explicit (wait_and_barrier).  The asm has no register
+// outputs; it sets M0 itself and declares it clobbered.
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds_base, int voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 ::"s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)p));
+}
+
 template <Out OUT>
 __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
     // One array per ring stage: each unrolled iteration below names its
@@ -69,7 +93,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
     // q = 4*wave + i.  Lane s fills slot s%16 of super-row 4q + s/16, i.e.
     // global row 8q + 2(s/16) + (v>>3), chunk v&7, with v = (s%16) ^ ((s/16 + 4q) % 8)
     // = (s%16) ^ (s/16 + 4*(q%2)) since 4q % 8 = 4*(q%2).
-    const auto ra = make_rsrc(a.Xq + m0 * K, min((int64_t)kBM, M - m0) * K);
+    const v4i ra = buffer_desc(a.Xq + m0 * K, min((int64_t)kBM, M - m0) * K);
     int a_voff[2];
 #pragma unroll
     for (int qp = 0; qp < 2; ++qp) {
@@ -79,19 +103,17 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
     // B: 16 wave-loads of 16 channels x 64 B; this wave issues q = 2*wave + i,
     // i.e. channels 32*wave + 16*i + lane/4.  Stored position lane%4 holds the
     // channel's global chunk (lane%4) ^ ((lane/8)%4).
-    const auto rbs = make_rsrc(a.packed + n0 * KB, min((int64_t)kBN, N - n0) * KB);
+    const v4i rbs = buffer_desc(a.packed + n0 * KB, min((int64_t)kBN, N - n0) * KB);
     const int b_voff = (32 * wave + lane / 4) * (int)KB + (((lane % 4) ^ ((lane / 8) % 4)) * 16);
     auto issue = [&](uint8_t *st, int kt) {
+        const uint32_t base = lds_addr(st);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (lds_void *)(st + (4 * wave + i) * 1024), 16, a_voff[i % 2],
-                8 * i * (int)K + kt * kBK, 0, 0);
+            dma16(ra, base + (4 * wave + i) * 1024, a_voff[i % 2], 8 * i * (int)K + kt * kBK);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rbs, (lds_void *)(st + kABytes + (2 * wave + i) * 1024), 16, b_voff,
-                16 * i * (int)KB + kt * (kBK / 2), 0, 0);
+            dma16(rbs, base + kABytes + (2 * wave + i) * 1024, b_voff,
+                  16 * i * (int)KB + kt * (kBK / 2));
     };
 
     // ---- fragment read offsets inside a stage (row block rb adds rb*2048,
