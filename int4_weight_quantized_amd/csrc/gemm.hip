@@ -8,8 +8,8 @@
 // Per k-tile the block stages
 //   A: 256 rows x 128 int8 activations (P8 layout)  = 32 KB
 //   B: 256 channels x 64 packed bytes (128 codes)   = 16 KB
-// in one stage of a 3-stage LDS ring, using direct global->LDS loads
-// (global_load_lds_dwordx4: lane L of a wave writes LDS[base + 16 L]), so the
+// in one stage of a 3-stage LDS ring, using direct buffer->LDS loads
+// (buffer_load_dwordx4 ... lds: lane L of a wave writes LDS[M0 + 16 L]), so the
 // tile after next is in flight while the current one is multiplied.  Rows
 // are stored without padding, with XOR-swizzled 16-byte chunk positions so
 // that the fragment reads are free of LDS bank conflicts.  Each wave unpacks its packed B fragments in
@@ -51,9 +51,10 @@ __device__ __forceinline__ v4i buffer_desc(const void *base, int64_t bytes) {
 // wait-count pass, which cannot tell which ring stage such a load fills,
 // does not drain all outstanding loads before every LDS read; all waits for
 // these loads are explicit (wait_and_barrier).  The asm has no register
-// outputs; it sets M0 itself and declares it clobbered.
+// outputs; it sets M0 itself and declares it clobbered.  On gfx9 an LDS
+// direct load needs one wait state after an SALU write of M0, hence the nop.
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds_base, int voff, int soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  ::"s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff)
                  : "memory", "m0");
 }
