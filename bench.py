@@ -303,7 +303,7 @@ def main():
                    "M": 1, "K": head.K, "N": head.N, "weights": "int4 symmetric per-channel",
                    "activations": "int8 per-row dynamic", "launch": "hipGraph of all steps",
                    "rotating_weight_copies": head.copies, "product_kernel": path},
-        "roofline": {"bound": "hbm", "kernel": "k_gemv_dot4<1,fused>",
+        "roofline": {"bound": "hbm", "kernel": "w4::k_gemv_dot4<1, 16, 3, true, Out::Y>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(digest),

@@ -91,6 +91,16 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
     return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// ----------------------------------------------------------------- barrier
+// Workgroup barrier that waits only for this wave's LDS operations: vector
+// memory loads issued before it stay in flight (the compiler still waits for
+// each loaded register before its first use).  __syncthreads would instead
+// drain every outstanding load at the barrier.  The "memory" clobber keeps
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -124,6 +134,26 @@ __device__ __forceinline__ int quant_code(float v, float s, float lo, float hi) 
     if (s == 0.0f) return 0;
     float t = v / s;  // IEEE division (no fast-math in this build)
     float r = rintf(t);
+    r = fminf(fmaxf(r, lo), hi);
+    return (int)r;
+}
+
+// The correctly rounded quotient fl(v / s) without a division: with
+// rs = fl(1 / s), q = fl(v * rs) lies within one ulp of v / s, the residual
+// v - s*q is exact in one fma and fl(q + residual * rs) is the correctly
+// rounded quotient (Markstein's theorem for round-to-nearest; it needs the
+// operands away from the subnormal range, hence kFastQuotientMinScale).
+constexpr float kFastQuotientMinScale = 0x1p-64f;
+
+__device__ __forceinline__ float quotient_rn(float v, float s, float rs) {
+    const float q = v * rs;
+    const float r = __builtin_fmaf(-q, s, v);
+    return __builtin_fmaf(r, rs, q);
+}
+
+// quant_code for a scale s >= kFastQuotientMinScale, with rs = fl(1 / s).
+__device__ __forceinline__ int quant_code_fast(float v, float s, float rs, float lo, float hi) {
+    float r = rintf(quotient_rn(v, s, rs));
     r = fminf(fmaxf(r, lo), hi);
     return (int)r;
 }

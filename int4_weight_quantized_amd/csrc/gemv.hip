@@ -17,31 +17,35 @@
 namespace w4 {
 
 // ------------------------------------------------------------------ dot4
-// Block = 256 threads = 16 output channels x 16 lanes.  Lane j of a channel
-// streams the 16-byte chunks j, j+16, ..., of that channel's packed row (one
-// chunk = 32 codes), so a wave reads 4 rows x 256 contiguous bytes per load.
-// Order of work: (1) issue the activation loads, (2) issue up to 8 weight
-// chunks per lane, (3) quantize the activations into LDS (P8 layout) while the
-// weights are in flight, (4) dot products, (5) 16-lane DPP sum and epilogue.
-constexpr int kDot4Rows = 16;
-constexpr int kDot4Batch = 8;  // chunks per lane per batch = 4096 codes per row
+// Block = ROWS output channels x 16 lanes.  Lane j of a channel streams the
+// 16-byte chunks j, j+16, ..., j+16*(UB-1) of that channel's packed row (one
+// chunk = 32 codes), so a wave reads 4 rows x 256 contiguous bytes per load
+// and every weight byte of the block is requested before any arithmetic.
+// Order of work: (1) issue the activation loads, (2) issue the weight chunks,
+// (3) quantize the activations into LDS (P8 layout) while the weights are in
+// flight (the barriers wait for LDS only, so the weight loads stay in
+// flight), (4) dot products, chunk by chunk as the loads land, (5) 16-lane
+// DPP sum and epilogue.
+constexpr int kDot4MaxK = 8192;
 
 bool gemv_dot4_ok(int64_t M, int64_t K) {
-    return M >= 1 && M <= 4 && K % 32 == 0 && K <= 8192;
+    return M >= 1 && M <= 4 && K % 32 == 0 && K <= kDot4MaxK;
 }
 
-template <int M, int NG, bool FUSED, Out OUT>
-__global__ __launch_bounds__(256) void k_gemv_dot4(W4A8Args a) {
+template <int M, int ROWS, int UB, bool FUSED, Out OUT>
+__global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
+    constexpr int T = 16 * ROWS;                   // threads
+    constexpr int NG = (4 * UB + ROWS - 1) / ROWS;  // 8-groups of k per thread (K <= 512*UB)
     extern __shared__ __align__(16) uint8_t smem[];
-    __shared__ float red[4][M];
+    __shared__ float red[T / kWave][M];
     int8_t *xs = reinterpret_cast<int8_t *>(smem);
     const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
     const int K = (int)a.K, KB = K / 2, C = K / 32, G8 = K / 8;
     const int j = t & 15, r = t >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * kDot4Rows;
-    const int rows = (int)min((int64_t)kDot4Rows, a.N - n0);
+    const int64_t n0 = (int64_t)blockIdx.x * ROWS;
+    const int rows = (int)min((int64_t)ROWS, a.N - n0);
 
-    // (1) activations: group g = t + 256*i holds k = 8g .. 8g+7 of each row.
+    // (1) activations: group g = t + T*i holds k = 8g .. 8g+7 of each row.
     float4 xa[M][NG], xb[M][NG];
     uint2 xn[M][NG];
     if (FUSED) {
@@ -50,7 +54,7 @@ __global__ __launch_bounds__(256) void k_gemv_dot4(W4A8Args a) {
         for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int i = 0; i < NG; ++i) {
-                const int g = t + 256 * i;
+                const int g = t + T * i;
                 const int off = g < G8 ? (m * K + 8 * g) * 4 : kOOB;
                 xa[m][i] = bloadf4(rx, off);
                 xb[m][i] = bloadf4(rx, off + 16);
@@ -61,28 +65,28 @@ __global__ __launch_bounds__(256) void k_gemv_dot4(W4A8Args a) {
         for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int i = 0; i < NG; ++i) {
-                const int g = t + 256 * i;
+                const int g = t + T * i;
                 xn[m][i] = bload8(rq, g < G8 ? m * K + 8 * g : kOOB);
             }
     }
 
-    // Epilogue operands early, so their latency hides behind the main loop.
+    // (2) weights of this block's rows: all UB chunks of the lane.
+    const auto rw = make_rsrc(a.packed + n0 * KB, (int64_t)rows * KB);
+    const int rowoff = r * KB;
+    uint4 wb[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+        const int c = j + 16 * u;
+        wb[u] = bload16(rw, c < C ? rowoff + 16 * c : kOOB);
+    }
+
+    // Epilogue operands, so their latency hides behind the main work.
     const int64_t n = n0 + r;
     const int64_t nc = r < rows ? n : n0;
     const float swn = (OUT == Out::Y) ? a.sw[nc] : 0.0f;
     const float bn = (OUT == Out::Y && a.bias) ? a.bias[nc] : 0.0f;
-
-    // (2) weights of this block's rows.
-    const auto rw = make_rsrc(a.packed + n0 * KB, (int64_t)rows * KB);
-    const int rowoff = r * KB;
-    uint4 wb[kDot4Batch];
-#pragma unroll
-    for (int u = 0; u < kDot4Batch; ++u) {
-        const int c = j + 16 * u;
-        wb[u] = bload16(rw, c < C ? rowoff + 16 * c : kOOB);
-    }
     // Keep the scheduler from interleaving the activation math (which waits
-    // for the activation loads) with the weight loads above.
+    // for the activation loads) with the loads above.
     __builtin_amdgcn_sched_barrier(0);
 
     // (3) activations -> int8 P8 layout in LDS, scales in registers.
@@ -101,24 +105,33 @@ __global__ __launch_bounds__(256) void k_gemv_dot4(W4A8Args a) {
             am = wave_max_dpp(am);
             if (lane == 0) red[wave][m] = am;
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            const float am = fmaxf(fmaxf(red[0][m], red[1][m]), fmaxf(red[2][m], red[3][m]));
+            float am = red[0][m];
+#pragma unroll
+            for (int w = 1; w < T / kWave; ++w) am = fmaxf(am, red[w][m]);
             const float s = (am == 0.0f) ? 0.0f : am / 127.0f;
             sxm[m] = s;
+            // codes of the thread's 8-groups, stored P8: [x0 x2 x4 x6 | x1 x3 x5 x7]
+            auto quantize = [&](auto code) {
 #pragma unroll
-            for (int i = 0; i < NG; ++i) {
-                const int g = t + 256 * i;
-                if (g < G8) {
-                    const float4 v0 = xa[m][i], v1 = xb[m][i];
-                    uint2 p;
-                    p.x = pack4_i8(quant_code(v0.x, s, -128.f, 127.f), quant_code(v0.z, s, -128.f, 127.f),
-                                   quant_code(v1.x, s, -128.f, 127.f), quant_code(v1.z, s, -128.f, 127.f));
-                    p.y = pack4_i8(quant_code(v0.y, s, -128.f, 127.f), quant_code(v0.w, s, -128.f, 127.f),
-                                   quant_code(v1.y, s, -128.f, 127.f), quant_code(v1.w, s, -128.f, 127.f));
-                    *reinterpret_cast<uint2 *>(xs + m * K + 8 * g) = p;
+                for (int i = 0; i < NG; ++i) {
+                    const int g = t + T * i;
+                    if (g < G8) {
+                        const float4 v0 = xa[m][i], v1 = xb[m][i];
+                        uint2 p;
+                        p.x = pack4_i8(code(v0.x), code(v0.z), code(v1.x), code(v1.z));
+                        p.y = pack4_i8(code(v0.y), code(v0.w), code(v1.y), code(v1.w));
+                        *reinterpret_cast<uint2 *>(xs + m * K + 8 * g) = p;
+                    }
                 }
+            };
+            if (s >= kFastQuotientMinScale) {  // row-uniform
+                const float rs = 1.0f / s;
+                quantize([&](float v) { return quant_code_fast(v, s, rs, -128.f, 127.f); });
+            } else {
+                quantize([&](float v) { return quant_code(v, s, -128.f, 127.f); });
             }
         }
     } else {
@@ -127,7 +140,7 @@ __global__ __launch_bounds__(256) void k_gemv_dot4(W4A8Args a) {
             sxm[m] = (OUT == Out::Y) ? a.sx[m] : 0.0f;
 #pragma unroll
             for (int i = 0; i < NG; ++i) {
-                const int g = t + 256 * i;
+                const int g = t + T * i;
                 if (g < G8) {
                     uint2 p;
                     natural_to_p8(xn[m][i].x, xn[m][i].y, p.x, p.y);
@@ -136,46 +149,33 @@ __global__ __launch_bounds__(256) void k_gemv_dot4(W4A8Args a) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // (4) int8 dot products of 16*code with the P8 activations.
     int acc[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[m] = 0;
-    for (int base = 0; base < C; base += 16 * kDot4Batch) {
-        uint4 cur[kDot4Batch];
 #pragma unroll
-        for (int u = 0; u < kDot4Batch; ++u) cur[u] = wb[u];
-        if (base + 16 * kDot4Batch < C) {
+    for (int u = 0; u < UB; ++u) {
+        // Past the end of the row the weights are zero; clamp the LDS read.
+        const int cx = min(j + 16 * u, C - 1);
+        const uint4 w = wb[u];
+        const uint32_t l0 = lo16(w.x), h0 = hi16(w.x), l1 = lo16(w.y), h1 = hi16(w.y);
+        const uint32_t l2 = lo16(w.z), h2 = hi16(w.z), l3 = lo16(w.w), h3 = hi16(w.w);
 #pragma unroll
-            for (int u = 0; u < kDot4Batch; ++u) {
-                const int c = base + 16 * kDot4Batch + j + 16 * u;
-                wb[u] = bload16(rw, c < C ? rowoff + 16 * c : kOOB);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kDot4Batch; ++u) {
-            // Past the end of the row the weights are zero; clamp the LDS read.
-            const int cx = min(base + j + 16 * u, C - 1);
-            const uint32_t l0 = lo16(cur[u].x), h0 = hi16(cur[u].x);
-            const uint32_t l1 = lo16(cur[u].y), h1 = hi16(cur[u].y);
-            const uint32_t l2 = lo16(cur[u].z), h2 = hi16(cur[u].z);
-            const uint32_t l3 = lo16(cur[u].w), h3 = hi16(cur[u].w);
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const uint4 *xp = reinterpret_cast<const uint4 *>(xs + m * K + cx * 32);
-                const uint4 x0 = xp[0], x1 = xp[1];
-                int s = acc[m];
-                s = __builtin_amdgcn_sdot4((int)l0, (int)x0.x, s, false);
-                s = __builtin_amdgcn_sdot4((int)h0, (int)x0.y, s, false);
-                s = __builtin_amdgcn_sdot4((int)l1, (int)x0.z, s, false);
-                s = __builtin_amdgcn_sdot4((int)h1, (int)x0.w, s, false);
-                s = __builtin_amdgcn_sdot4((int)l2, (int)x1.x, s, false);
-                s = __builtin_amdgcn_sdot4((int)h2, (int)x1.y, s, false);
-                s = __builtin_amdgcn_sdot4((int)l3, (int)x1.z, s, false);
-                s = __builtin_amdgcn_sdot4((int)h3, (int)x1.w, s, false);
-                acc[m] = s;
-            }
+        for (int m = 0; m < M; ++m) {
+            const uint4 *xp = reinterpret_cast<const uint4 *>(xs + m * K + cx * 32);
+            const uint4 x0 = xp[0], x1 = xp[1];
+            int s = acc[m];
+            s = __builtin_amdgcn_sdot4((int)l0, (int)x0.x, s, false);
+            s = __builtin_amdgcn_sdot4((int)h0, (int)x0.y, s, false);
+            s = __builtin_amdgcn_sdot4((int)l1, (int)x0.z, s, false);
+            s = __builtin_amdgcn_sdot4((int)h1, (int)x0.w, s, false);
+            s = __builtin_amdgcn_sdot4((int)l2, (int)x1.x, s, false);
+            s = __builtin_amdgcn_sdot4((int)h2, (int)x1.y, s, false);
+            s = __builtin_amdgcn_sdot4((int)l3, (int)x1.z, s, false);
+            s = __builtin_amdgcn_sdot4((int)h3, (int)x1.w, s, false);
+            acc[m] = s;
         }
     }
 
@@ -197,27 +197,32 @@ __global__ __launch_bounds__(256) void k_gemv_dot4(W4A8Args a) {
     }
 }
 
-template <int M, int NG>
+template <int M, int ROWS, int UB>
 static void go_dot4(const W4A8Args &a, hipStream_t st) {
-    dim3 grid((unsigned)((a.N + kDot4Rows - 1) / kDot4Rows));
+    dim3 grid((unsigned)((a.N + ROWS - 1) / ROWS));
     const uint32_t shm = (uint32_t)(M * a.K);
     if (a.out == Out::I32)
-        launch_main(k_gemv_dot4<M, NG, false, Out::I32>, grid, dim3(256), shm, st, a);
+        launch_main(k_gemv_dot4<M, ROWS, UB, false, Out::I32>, grid, dim3(16 * ROWS), shm, st, a);
     else if (a.X)
-        launch_main(k_gemv_dot4<M, NG, true, Out::Y>, grid, dim3(256), shm, st, a);
+        launch_main(k_gemv_dot4<M, ROWS, UB, true, Out::Y>, grid, dim3(16 * ROWS), shm, st, a);
     else
-        launch_main(k_gemv_dot4<M, NG, false, Out::Y>, grid, dim3(256), shm, st, a);
+        launch_main(k_gemv_dot4<M, ROWS, UB, false, Out::Y>, grid, dim3(16 * ROWS), shm, st, a);
 }
 
+// UB = chunks per lane, the smallest instantiated value >= ceil(K/32 / 16).
 template <int M>
 static void go_dot4_m(const W4A8Args &a, hipStream_t st) {
-    const int64_t g8 = a.K / 8;
-    if (g8 <= 256)
-        go_dot4<M, 1>(a, st);
-    else if (g8 <= 512)
-        go_dot4<M, 2>(a, st);
+    const int64_t ub = (a.K / 32 + 15) / 16;
+    if (ub <= 2)
+        go_dot4<M, 16, 2>(a, st);
+    else if (ub <= 3)
+        go_dot4<M, 16, 3>(a, st);
+    else if (ub <= 4)
+        go_dot4<M, 16, 4>(a, st);
+    else if (ub <= 8)
+        go_dot4<M, 16, 8>(a, st);
     else
-        go_dot4<M, 4>(a, st);
+        go_dot4<M, 16, 16>(a, st);
 }
 
 hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st) {
@@ -231,8 +236,11 @@ hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st) {
 }
 
 // ------------------------------------------------------------------ MFMA
-// Block = 4 waves that split K into quarters and cover the same 16*NB output
-// channels; the partial int32 sums are added through LDS at the end.
+// Block = W waves that split K into W slices and cover the same 16*NB output
+// channels for 16*MB activation rows; the partial int32 sums meet in LDS
+// (integer adds, so their order does not matter).  Many waves per block keep
+// enough weight bytes in flight to cover the HBM latency even though a
+// decode-batch layer has few output-channel blocks.
 // Per 128-k step a lane loads 16 packed bytes (32 codes) of one channel:
 //   lane l: channel n0 + 16*nb + l%16, codes k = 128*s + 32*(l/16) + [0, 32)
 // and the matching 2 x 16 P8 activation bytes of row 16*mb + l%16, which
@@ -243,9 +251,11 @@ hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st) {
 // Weights and activations of the next D steps are in flight in a register
 // ring while the current step multiplies.  Rows past M and channels past N
 // read zeros (their outputs are not stored).
-template <int MB, int NB, int D, Out OUT>
-__global__ __launch_bounds__(256) void k_gemv_mfma(W4A8Args a) {
-    __shared__ v4i red[3][MB * NB][kWave];
+template <int MB, int NB, int D, int W, Out OUT>
+__global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args a) {
+    constexpr int kPairs = MB * NB;                 // 16x16 output blocks
+    constexpr int kPerWave = (kPairs + W - 1) / W;  // epilogue blocks per wave
+    __shared__ int red[kPairs * 4 * kWave];         // [pair][i][lane]
     // wave-uniform (scalar) so the K-range loop branches are scalar branches
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
@@ -253,9 +263,12 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(W4A8Args a) {
     const int K = (int)a.K, KB = K / 2;
     const int64_t N = a.N, M = a.M;
     const int S = K / 128;
-    const int s0 = S * wave / 4, s1 = S * (wave + 1) / 4;
+    const int s0 = S * wave / W, s1 = S * (wave + 1) / W;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * NB;
     const int cols = (int)min((int64_t)(16 * NB), N - n0);
+
+    for (int t = threadIdx.x; t < kPairs * 4 * kWave; t += 64 * W) red[t] = 0;
+    __syncthreads();
 
     const auto rb = make_rsrc(a.packed + n0 * KB, (int64_t)cols * KB);
     const auto ra = make_rsrc(a.Xq, M * K);
@@ -270,22 +283,6 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(W4A8Args a) {
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = v4i{0, 0, 0, 0};
-
-    // Epilogue operands early (wave 0 stores): channel scales / bias of this
-    // lane's columns and the row scales of its 4 rows per row block.
-    float swc[NB], bc[NB], sxr[MB][4];
-    if (OUT == Out::Y && wave == 0) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const int64_t col = min(n0 + 16 * nb + r16, N - 1);
-            swc[nb] = a.sw[col];
-            bc[nb] = a.bias ? a.bias[col] : 0.0f;
-        }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sxr[mb][i] = a.sx[min((int64_t)(16 * mb + 4 * kq + i), M - 1)];
-    }
 
     uint4 wr[D][NB], xr0[D][MB], xr1[D][MB];
     auto fetch = [&](int d, int ss) {
@@ -303,6 +300,22 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(W4A8Args a) {
     for (int d = 0; d < D; ++d) {
         fetch(d, s0 + d);
         __builtin_amdgcn_sched_barrier(0);  // slot 0 oldest, as in the loop below
+    }
+
+    // Epilogue operands of the output blocks this wave stores, loaded early:
+    // channel scale and bias of this lane's column, row scales of its 4 rows.
+    float swc[kPerWave], bc[kPerWave], sxr[kPerWave][4];
+    if (OUT == Out::Y) {
+#pragma unroll
+        for (int j = 0; j < kPerWave; ++j) {
+            const int p = wave + j * W;
+            const int mb = min(p, kPairs - 1) / NB, nb = min(p, kPairs - 1) % NB;
+            const int64_t col = min(n0 + 16 * nb + r16, N - 1);
+            swc[j] = a.sw[col];
+            bc[j] = a.bias ? a.bias[col] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sxr[j][i] = a.sx[min((int64_t)(16 * mb + 4 * kq + i), M - 1)];
+        }
     }
 
     // Each ring slot keeps its registers: its data is consumed (unpacked /
@@ -338,56 +351,54 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(W4A8Args a) {
         }
     }
 
-    if (wave > 0) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) red[wave - 1][mb * NB + nb][lane] = acc[mb][nb];
-    }
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) atomicAdd(&red[((mb * NB + nb) * 4 + i) * kWave + lane], acc[mb][nb][i]);
     __syncthreads();
-    if (wave != 0) return;
+
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    for (int j = 0; j < kPerWave; ++j) {
+        const int p = wave + j * W;
+        if (p >= kPairs) break;
+        const int mb = p / NB, nb = p % NB;
+        const int64_t col = n0 + 16 * nb + r16;
+        if (col >= N) continue;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            v4i t = acc[mb][nb] + red[0][mb * NB + nb][lane] + red[1][mb * NB + nb][lane] +
-                    red[2][mb * NB + nb][lane];
-            const int64_t col = n0 + 16 * nb + r16;
-            if (col >= N) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = 16 * mb + 4 * kq + i;
-                if (row >= M) continue;
-                const int v = t[i] >> 4;
-                if (OUT == Out::I32) {
-                    a.acc[row * N + col] = v;
-                } else {
-                    const float sc = sxr[mb][i] * swc[nb];
-                    float y = (float)v * sc;
-                    if (a.bias) y = y + bc[nb];
-                    a.Y[row * N + col] = y;
-                }
+        for (int i = 0; i < 4; ++i) {
+            const int64_t row = 16 * mb + 4 * kq + i;
+            if (row >= M) continue;
+            const int v = red[(p * 4 + i) * kWave + lane] >> 4;
+            if (OUT == Out::I32) {
+                a.acc[row * N + col] = v;
+            } else {
+                const float sc = sxr[j][i] * swc[j];
+                float y = (float)v * sc;
+                if (a.bias) y = y + bc[j];
+                a.Y[row * N + col] = y;
             }
         }
     }
 }
 
-template <int MB, int NB, int D>
+template <int MB, int NB, int D, int W>
 static void go_mfma(const W4A8Args &a, hipStream_t st) {
     dim3 grid((unsigned)((a.N + 16 * NB - 1) / (16 * NB)));
     if (a.out == Out::I32)
-        launch_main(k_gemv_mfma<MB, NB, D, Out::I32>, grid, dim3(256), 0, st, a);
+        launch_main(k_gemv_mfma<MB, NB, D, W, Out::I32>, grid, dim3(64 * W), 0, st, a);
     else
-        launch_main(k_gemv_mfma<MB, NB, D, Out::Y>, grid, dim3(256), 0, st, a);
+        launch_main(k_gemv_mfma<MB, NB, D, W, Out::Y>, grid, dim3(64 * W), 0, st, a);
 }
 
 hipError_t launch_gemv_mfma(const W4A8Args &a, hipStream_t st) {
     const int mb = (int)((a.M + 15) / 16);
     switch (mb) {
-        case 1: go_mfma<1, 2, 8>(a, st); break;
-        case 2: go_mfma<2, 2, 4>(a, st); break;
-        case 3: go_mfma<3, 2, 2>(a, st); break;
-        default: go_mfma<4, 2, 2>(a, st); break;
+        case 1: go_mfma<1, 4, 2, 8>(a, st); break;
+        case 2: go_mfma<2, 4, 2, 8>(a, st); break;
+        case 3: go_mfma<3, 4, 1, 8>(a, st); break;
+        default: go_mfma<4, 4, 1, 8>(a, st); break;
     }
     return hipGetLastError();
 }

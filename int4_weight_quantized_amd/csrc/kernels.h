@@ -53,7 +53,7 @@ hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, fl
                             hipStream_t st);
 hipError_t launch_to_p8(const int8_t *Xq, int64_t M, int64_t K, int8_t *out, hipStream_t st);
 
-// M <= 4, K % 32 == 0, 16-byte aligned: VALU dot4 GEMV.  Uses a.X (fused
+// M <= 4, K % 32 == 0, K <= 8192, 16-byte aligned: VALU dot4 GEMV.  Uses a.X (fused
 // quantization prologue) when non-NULL, else a.Xq (natural layout) + a.sx.
 bool gemv_dot4_ok(int64_t M, int64_t K);
 hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st);

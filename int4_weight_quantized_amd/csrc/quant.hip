@@ -216,38 +216,45 @@ __global__ __launch_bounds__(256) void k_quant_act(const float *__restrict__ X, 
     if (threadIdx.x == 0) sx[m] = s;
     int8_t *out = Xq + m * K;
     const int64_t ng = (K + 7) / 8;
-    for (int64_t g = threadIdx.x; g < ng; g += 256) {
-        const int64_t k0 = g * 8;
-        int q[8];
-        if (vec && k0 + 8 <= K) {
-            const float4 v0 = reinterpret_cast<const float4 *>(row + k0)[0];
-            const float4 v1 = reinterpret_cast<const float4 *>(row + k0)[1];
-            q[0] = quant_code(v0.x, s, -128.f, 127.f);
-            q[1] = quant_code(v0.y, s, -128.f, 127.f);
-            q[2] = quant_code(v0.z, s, -128.f, 127.f);
-            q[3] = quant_code(v0.w, s, -128.f, 127.f);
-            q[4] = quant_code(v1.x, s, -128.f, 127.f);
-            q[5] = quant_code(v1.y, s, -128.f, 127.f);
-            q[6] = quant_code(v1.z, s, -128.f, 127.f);
-            q[7] = quant_code(v1.w, s, -128.f, 127.f);
-        } else {
+    auto quantize = [&](auto code) {
+        for (int64_t g = threadIdx.x; g < ng; g += 256) {
+            const int64_t k0 = g * 8;
+            int q[8];
+            if (vec && k0 + 8 <= K) {
+                const float4 v0 = reinterpret_cast<const float4 *>(row + k0)[0];
+                const float4 v1 = reinterpret_cast<const float4 *>(row + k0)[1];
+                q[0] = code(v0.x);
+                q[1] = code(v0.y);
+                q[2] = code(v0.z);
+                q[3] = code(v0.w);
+                q[4] = code(v1.x);
+                q[5] = code(v1.y);
+                q[6] = code(v1.z);
+                q[7] = code(v1.w);
+            } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                q[j] = (k0 + j < K) ? quant_code(row[k0 + j], s, -128.f, 127.f) : 0;
+                for (int j = 0; j < 8; ++j) q[j] = (k0 + j < K) ? code(row[k0 + j]) : 0;
+            }
+            if (P8) {
+                uint2 v;
+                v.x = pack4_i8(q[0], q[2], q[4], q[6]);
+                v.y = pack4_i8(q[1], q[3], q[5], q[7]);
+                *reinterpret_cast<uint2 *>(out + k0) = v;
+            } else if ((K % 8) == 0 && (reinterpret_cast<uintptr_t>(Xq) & 7) == 0) {
+                uint2 v;
+                v.x = pack4_i8(q[0], q[1], q[2], q[3]);
+                v.y = pack4_i8(q[4], q[5], q[6], q[7]);
+                *reinterpret_cast<uint2 *>(out + k0) = v;
+            } else {
+                for (int j = 0; j < 8 && k0 + j < K; ++j) out[k0 + j] = (int8_t)q[j];
+            }
         }
-        if (P8) {
-            uint2 v;
-            v.x = pack4_i8(q[0], q[2], q[4], q[6]);
-            v.y = pack4_i8(q[1], q[3], q[5], q[7]);
-            *reinterpret_cast<uint2 *>(out + k0) = v;
-        } else if ((K % 8) == 0 && (reinterpret_cast<uintptr_t>(Xq) & 7) == 0) {
-            uint2 v;
-            v.x = pack4_i8(q[0], q[1], q[2], q[3]);
-            v.y = pack4_i8(q[4], q[5], q[6], q[7]);
-            *reinterpret_cast<uint2 *>(out + k0) = v;
-        } else {
-            for (int j = 0; j < 8 && k0 + j < K; ++j) out[k0 + j] = (int8_t)q[j];
-        }
+    };
+    if (s >= kFastQuotientMinScale) {  // block-uniform
+        const float rs = 1.0f / s;
+        quantize([&](float v) { return quant_code_fast(v, s, rs, -128.f, 127.f); });
+    } else {
+        quantize([&](float v) { return quant_code(v, s, -128.f, 127.f); });
     }
 }
 

@@ -5,7 +5,7 @@
 //   w' = bf16_rne(fl((q - zero) * scale))
 // and fed to v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
 //
-// Block = 4 waves that split K into quarters and cover 16*NB output channels
+// Block = W waves that split K into W slices and cover 16*NB output channels
 // for 16 activation rows.  Per 128-k step a lane loads 16 packed bytes of one
 // channel (codes k = 128*s + 32*(l/16) + [0, 32)) and the matching 32 bf16
 // activations of row l%16; the 32 codes feed four MFMAs of 8 codes each.
@@ -68,20 +68,21 @@ __device__ __forceinline__ v4f mfma_bf16(uint4 a, v4i b, v4f c) {
                                                    __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
-template <int NB, int D>
-__global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t *__restrict__ X,
+template <int NB, int D, int W>
+__global__ __launch_bounds__(64 * W) void k_w4a16_mfma(const uint16_t *__restrict__ X,
                                                     const uint8_t *__restrict__ packed,
                                                     const float *__restrict__ scales,
                                                     const float *__restrict__ zeros,
                                                     float *__restrict__ Y, int64_t M, int64_t K64,
                                                     int64_t N, int64_t group) {
-    __shared__ v4f red[3][NB][kWave];
+    static_assert(W * NB * kWave * 16 <= 160 * 1024, "partial sums must fit in LDS");
+    __shared__ v4f red[W][NB][kWave];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
     const int r16 = lane % 16, kq = lane / 16;
     const int K = (int)K64, KB = K / 2, G = (int)(K64 / group);
     const int S = K / 128;
-    const int s0 = S * wave / 4, s1 = S * (wave + 1) / 4;
+    const int s0 = S * wave / W, s1 = S * (wave + 1) / W;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * NB;
     const int64_t m0 = (int64_t)blockIdx.y * 16;
     const int cols = (int)min((int64_t)(16 * NB), N - n0);
@@ -174,15 +175,14 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t *__restrict__
         }
     }
 
-    if (wave > 0) {
+    // Partial sums of the W waves meet in LDS; each channel block is summed
+    // over the waves in a fixed order (deterministic results).
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) red[wave - 1][nb][lane] = acc[nb];
-    }
+    for (int nb = 0; nb < NB; ++nb) red[wave][nb][lane] = acc[nb];
     __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const v4f t = acc[nb] + red[0][nb][lane] + red[1][nb][lane] + red[2][nb][lane];
+    for (int nb = wave; nb < NB; nb += W) {
+        v4f t = red[0][nb][lane];
+        for (int w = 1; w < W; ++w) t += red[w][nb][lane];
         const int64_t col = n0 + 16 * nb + r16;
         if (col >= N) continue;
 #pragma unroll
@@ -196,12 +196,12 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t *__restrict__
 hipError_t launch_w4a16_mfma(const uint16_t *X, int64_t M, int64_t K, int64_t N,
                              const uint8_t *packed, const float *scales, const float *zeros,
                              int64_t group, float *Y, hipStream_t st) {
-    constexpr int NB = 4, D = 2;
+    constexpr int NB = 8, D = 1, W = 4;
     const int64_t mblocks = (M + 15) / 16;
     for (int64_t mb0 = 0; mb0 < mblocks; mb0 += 65535) {
         const int64_t cnt = (mblocks - mb0) < 65535 ? (mblocks - mb0) : 65535;
         dim3 grid((unsigned)((N + 16 * NB - 1) / (16 * NB)), (unsigned)cnt);
-        launch_main(k_w4a16_mfma<NB, D>, grid, dim3(256), 0, st, X + mb0 * 16 * K, packed, scales,
+        launch_main(k_w4a16_mfma<NB, D, W>, grid, dim3(64 * W), 0, st, X + mb0 * 16 * K, packed, scales,
                     zeros, Y + mb0 * 16 * N, M - mb0 * 16, K, N, group);
     }
     return hipGetLastError();

@@ -153,6 +153,48 @@ def test_quantize_act(M, K):
     assert guards_intact(bufq, pq)
 
 
+def _tie_rows(M, K, seed):
+    """Activation rows whose values sit on, and one ulp either side of, the
+    rounding ties (k + 1/2) * sx of the int8 grid.  Even rows use a power-of-two
+    scale (exact ties); odd rows a random scale (ties rounded to fp32)."""
+    rng = np.random.default_rng(seed)
+    X = np.empty((M, K), np.float32)
+    for m in range(M):
+        if m % 2 == 0:
+            am = np.float32(127.0) * np.float32(2.0) ** np.float32(rng.integers(-8, 4))
+        else:
+            am = np.float32(rng.uniform(0.5, 60.0))
+        s = np.float32(am / np.float32(127.0))
+        k = rng.integers(-128, 127, K).astype(np.float32)
+        tie = (k + np.float32(0.5)) * s
+        kind = rng.integers(0, 3, K)
+        up = np.nextafter(tie, np.float32(np.inf), dtype=np.float32)
+        dn = np.nextafter(tie, np.float32(-np.inf), dtype=np.float32)
+        row = np.where(kind == 0, tie, np.where(kind == 1, up, dn)).astype(np.float32)
+        row = np.clip(row, -am, am)
+        row[rng.integers(0, K)] = am if m % 3 else -am
+        X[m] = row
+    return X
+
+
+@pytest.mark.parametrize("M,K", [(1, 1152), (2, 256), (4, 4096), (8, 1152), (1, 10), (100, 256)])
+def test_activation_ties(M, K):
+    """Values on and next to rounding ties: the standalone quantizer and the
+    linear layer (whose decode path quantizes inside the product kernel)."""
+    X = _tie_rows(M, K, M * 1000 + K)
+    xq_ref, sx_ref = oracle.quantize_act(X)
+    xq, sx = W4.a8_quantize_act(dev(X))
+    assert np.array_equal(host(xq), xq_ref), report("xq", host(xq), xq_ref)
+    assert bits_equal(host(sx), sx_ref)
+    N = 64
+    W = workloads.random_case(K, 1, K, N)["W"]
+    pref, sref = oracle.quantize_weight_sym(W)
+    yref = oracle.w4a8_linear(X, pref, sref)
+    y = W4.w4a8_linear(dev(X), dev(pref), dev(sref))
+    got = host(y)
+    assert bits_equal(got, yref), report(f"y path={W4.w4_last_path()}", got, yref)
+
+
 def test_quantize_act_prefill_full():
     d = workloads.generate("prefill", with_w=False)
     xq_ref, sx_ref = oracle.quantize_act(d["x"])
