@@ -68,7 +68,7 @@ __device__ __forceinline__ v4f mfma_bf16(uint4 a, v4i b, v4f c) {
                                                    __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
-template <int NB, int D, int W>
+template <int NB, int D, int W, bool G128>
 __global__ __launch_bounds__(64 * W) void k_w4a16_mfma(const uint16_t *__restrict__ X,
                                                     const uint8_t *__restrict__ packed,
                                                     const float *__restrict__ scales,
@@ -76,6 +76,7 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_mfma(const uint16_t *__restric
                                                     float *__restrict__ Y, int64_t M, int64_t K64,
                                                     int64_t N, int64_t group) {
     static_assert(W * NB * kWave * 16 <= 160 * 1024, "partial sums must fit in LDS");
+    static_assert(4 % D == 0, "ring depth divides the 4-step scale blocks");
     __shared__ v4f red[W][NB][kWave];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
@@ -106,72 +107,126 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_mfma(const uint16_t *__restric
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[nb] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // Register ring: weights and activations of the next D steps.
     uint4 wr[D][NB], xr[D][4];
-    float sr[D][NB], zr[D][NB];
     auto fetch = [&](int d, int ss) {
         const bool ok = ss < s1;
-        const int g = (ss * 128 + kq * 32) / (int)group;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            wr[d][nb] = bload16(rb, ok ? boff[nb] + 64 * ss : kOOB);
-            sr[d][nb] = bloadf(rs, ok ? goff[nb] + 4 * g : kOOB);
-            zr[d][nb] = bloadf(rz, ok ? goff[nb] + 4 * g : kOOB);
-        }
+        for (int nb = 0; nb < NB; ++nb) wr[d][nb] = bload16(rb, ok ? boff[nb] + 64 * ss : kOOB);
         const int xo = ok ? xoff + 256 * ss : kOOB;
 #pragma unroll
         for (int q = 0; q < 4; ++q) xr[d][q] = bload16(rx, xo + 16 * q);
     };
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-        fetch(d, s0 + d);
-        __builtin_amdgcn_sched_barrier(0);
-    }
 
-    // No per-step branch: steps past s1 read zeros and add nothing.  One
-    // wave-uniform vote per step picks the dequantization path for all NB
-    // channel blocks; each block is dequantized right before its 4 MFMAs so
-    // only 16 dequantized registers are live at a time.
-    for (int s = s0; s < s1; s += D) {
+    // One step: one wave-uniform vote picks the dequantization path for all
+    // NB channel blocks; each block is dequantized right before its 4 MFMAs
+    // so only 16 dequantized registers are live at a time.  Steps past s1
+    // read zeros (weights, activations and scales) and add nothing.
+    auto compute = [&](int d, const float *sc, const float *zp) {
+        bool ok = true;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            ok = ok && (zp[nb] >= -112.0f) && (zp[nb] <= 128.0f) && (fabsf(sc[nb]) < 0x1p100f);
+        if (__all(ok)) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const uint32_t cadd = (uint32_t)(128 - (int)zp[nb]) * 0x01010101u;
+                const float nbias = -128.0f * sc[nb];
+                const uint4 w = wr[d][nb];
+                const v4i b0 = dequant8_fast(w.x, sc[nb], cadd, nbias);
+                const v4i b1 = dequant8_fast(w.y, sc[nb], cadd, nbias);
+                const v4i b2 = dequant8_fast(w.z, sc[nb], cadd, nbias);
+                const v4i b3 = dequant8_fast(w.w, sc[nb], cadd, nbias);
+                acc[nb] = mfma_bf16(xr[d][0], b0, acc[nb]);
+                acc[nb] = mfma_bf16(xr[d][1], b1, acc[nb]);
+                acc[nb] = mfma_bf16(xr[d][2], b2, acc[nb]);
+                acc[nb] = mfma_bf16(xr[d][3], b3, acc[nb]);
+            }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const uint4 w = wr[d][nb];
+                const v4i b0 = dequant8_direct(w.x, sc[nb], zp[nb]);
+                const v4i b1 = dequant8_direct(w.y, sc[nb], zp[nb]);
+                const v4i b2 = dequant8_direct(w.z, sc[nb], zp[nb]);
+                const v4i b3 = dequant8_direct(w.w, sc[nb], zp[nb]);
+                acc[nb] = mfma_bf16(xr[d][0], b0, acc[nb]);
+                acc[nb] = mfma_bf16(xr[d][1], b1, acc[nb]);
+                acc[nb] = mfma_bf16(xr[d][2], b2, acc[nb]);
+                acc[nb] = mfma_bf16(xr[d][3], b3, acc[nb]);
+            }
+        }
+    };
+
+    if constexpr (G128) {
+        // Group = one 128-k step.  The 4 lanes of a channel (kq = 0..3) load
+        // the scales and zero points of 4 consecutive steps with one load
+        // (16 contiguous bytes per channel) and hand them to each other with
+        // ds_bpermute, instead of every lane loading one value per step.
+        float ss_cur[NB], zz_cur[NB], ss_nxt[NB], zz_nxt[NB];
+        auto fetch_sz = [&](float *sd, float *zd, int sb) {
+            const bool ok = sb + kq < s1;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                sd[nb] = bloadf(rs, ok ? goff[nb] + 4 * (sb + kq) : kOOB);
+                zd[nb] = bloadf(rz, ok ? goff[nb] + 4 * (sb + kq) : kOOB);
+            }
+        };
+        fetch_sz(ss_cur, zz_cur, s0);
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            bool ok = true;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                ok = ok && (zr[d][nb] >= -112.0f) && (zr[d][nb] <= 128.0f) &&
-                     (fabsf(sr[d][nb]) < 0x1p100f);
-            if (__all(ok)) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const float sc = sr[d][nb];
-                    const uint32_t cadd = (uint32_t)(128 - (int)zr[d][nb]) * 0x01010101u;
-                    const float nbias = -128.0f * sc;
-                    const uint4 w = wr[d][nb];
-                    const v4i b0 = dequant8_fast(w.x, sc, cadd, nbias);
-                    const v4i b1 = dequant8_fast(w.y, sc, cadd, nbias);
-                    const v4i b2 = dequant8_fast(w.z, sc, cadd, nbias);
-                    const v4i b3 = dequant8_fast(w.w, sc, cadd, nbias);
-                    acc[nb] = mfma_bf16(xr[d][0], b0, acc[nb]);
-                    acc[nb] = mfma_bf16(xr[d][1], b1, acc[nb]);
-                    acc[nb] = mfma_bf16(xr[d][2], b2, acc[nb]);
-                    acc[nb] = mfma_bf16(xr[d][3], b3, acc[nb]);
-                }
-            } else {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const float sc = sr[d][nb], zp = zr[d][nb];
-                    const uint4 w = wr[d][nb];
-                    const v4i b0 = dequant8_direct(w.x, sc, zp);
-                    const v4i b1 = dequant8_direct(w.y, sc, zp);
-                    const v4i b2 = dequant8_direct(w.z, sc, zp);
-                    const v4i b3 = dequant8_direct(w.w, sc, zp);
-                    acc[nb] = mfma_bf16(xr[d][0], b0, acc[nb]);
-                    acc[nb] = mfma_bf16(xr[d][1], b1, acc[nb]);
-                    acc[nb] = mfma_bf16(xr[d][2], b2, acc[nb]);
-                    acc[nb] = mfma_bf16(xr[d][3], b3, acc[nb]);
-                }
-            }
-            fetch(d, s + d + D);
+            fetch(d, s0 + d);
             __builtin_amdgcn_sched_barrier(0);
+        }
+        fetch_sz(ss_nxt, zz_nxt, s0 + 4);
+        for (int s = s0; s < s1; s += 4) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int src = (r16 + 16 * j) * 4;
+                float sc[NB], zp[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    sc[nb] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(ss_cur[nb])));
+                    zp[nb] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(zz_cur[nb])));
+                }
+                compute(j % D, sc, zp);
+                fetch(j % D, s + j + D);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                ss_cur[nb] = ss_nxt[nb];
+                zz_cur[nb] = zz_nxt[nb];
+            }
+            fetch_sz(ss_nxt, zz_nxt, s + 8);
+        }
+    } else {
+        // Any group size (a multiple of 32): each lane loads the scale and
+        // zero point of its own 32 codes every step.
+        float sr[D][NB], zr[D][NB];
+        auto fetch_sz = [&](int d, int ss) {
+            const bool ok = ss < s1;
+            const int g = (ss * 128 + kq * 32) / (int)group;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                sr[d][nb] = bloadf(rs, ok ? goff[nb] + 4 * g : kOOB);
+                zr[d][nb] = bloadf(rz, ok ? goff[nb] + 4 * g : kOOB);
+            }
+        };
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            fetch(d, s0 + d);
+            fetch_sz(d, s0 + d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int s = s0; s < s1; s += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                compute(d, sr[d], zr[d]);
+                fetch(d, s + d + D);
+                fetch_sz(d, s + d + D);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 
@@ -196,13 +251,17 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_mfma(const uint16_t *__restric
 hipError_t launch_w4a16_mfma(const uint16_t *X, int64_t M, int64_t K, int64_t N,
                              const uint8_t *packed, const float *scales, const float *zeros,
                              int64_t group, float *Y, hipStream_t st) {
-    constexpr int NB = 8, D = 1, W = 4;
+    constexpr int NB = 4, D = 1, W = 8;
     const int64_t mblocks = (M + 15) / 16;
     for (int64_t mb0 = 0; mb0 < mblocks; mb0 += 65535) {
         const int64_t cnt = (mblocks - mb0) < 65535 ? (mblocks - mb0) : 65535;
         dim3 grid((unsigned)((N + 16 * NB - 1) / (16 * NB)), (unsigned)cnt);
-        launch_main(k_w4a16_mfma<NB, D, W>, grid, dim3(64 * W), 0, st, X + mb0 * 16 * K, packed, scales,
-                    zeros, Y + mb0 * 16 * N, M - mb0 * 16, K, N, group);
+        if (group == 128)
+            launch_main(k_w4a16_mfma<NB, D, W, true>, grid, dim3(64 * W), 0, st, X + mb0 * 16 * K,
+                        packed, scales, zeros, Y + mb0 * 16 * N, M - mb0 * 16, K, N, group);
+        else
+            launch_main(k_w4a16_mfma<NB, D, W, false>, grid, dim3(64 * W), 0, st, X + mb0 * 16 * K,
+                        packed, scales, zeros, Y + mb0 * 16 * N, M - mb0 * 16, K, N, group);
     }
     return hipGetLastError();
 }
