@@ -219,6 +219,12 @@ int w4a16_linear(const uint16_t *X_bf16, int64_t M, int64_t K, int64_t N, const 
     if (!aligned(X_bf16, 2) || !aligned(scales, 4) || !aligned(zeros, 4) || !aligned(Y, 4))
         return W4_ERR_ALIGN;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (w4::w4a16_lds_ok(K, group_size) && aligned(X_bf16, 16) && aligned(packed, 16) &&
+        aligned(scales, 16) && aligned(zeros, 16)) {
+        g_last_path = "w4a16_lds";
+        return hip_status(
+            w4::launch_w4a16_lds(X_bf16, M, K, N, packed, scales, zeros, Y, st));
+    }
     if (w4::w4a16_fast_ok(M, K, N, group_size) && aligned(X_bf16, 16) && aligned(packed, 16)) {
         g_last_path = "w4a16_mfma";
         return hip_status(

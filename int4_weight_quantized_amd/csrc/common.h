@@ -91,6 +91,48 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
     return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// ------------------------------------------------- direct buffer->LDS loads
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until at most N of this wave's vector-memory operations (here: the
+// direct global->LDS loads) are outstanding and all its LDS operations are
+// done, then join the workgroup barrier.  The "memory" clobber keeps the
+// compiler from moving LDS accesses across it.  (The fences of
+// __syncthreads would instead drain every outstanding direct load.)
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range (6 bits on gfx9)");
+    // lgkmcnt(0) through the builtin, so that the compiler's wait-count
+    // tracking knows every earlier LDS read has completed.
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Raw buffer descriptor (gfx9 layout): 48-bit base, stride 0, byte range,
+// raw-buffer flags.  Reads outside [0, bytes) return zeros.
+__device__ __forceinline__ v4i buffer_desc(const void *base, int64_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const int n = bytes > kMaxRange ? kMaxRange : (int)bytes;
+    return v4i{(int)(uint32_t)p, (int)(uint32_t)((p >> 32) & 0xFFFFu), n, kBufFlags};
+}
+
+// One 16-byte buffer load per lane that writes LDS (lane L of the wave writes
+// LDS[lds_base + 16 L]).  Written as inline asm so that the compiler's
+// wait-count pass, which cannot tell which ring stage such a load fills,
+// does not drain all outstanding loads before every LDS read; all waits for
+// these loads are explicit (wait_and_barrier).  The asm has no register
+// outputs; it sets M0 itself and declares it clobbered.  On gfx9 an LDS
+// direct load needs one wait state after an SALU write of M0, hence the nop.
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds_base, int voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 ::"s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)p));
+}
+
 // ----------------------------------------------------------------- barrier
 // Workgroup barrier that waits only for this wave's LDS operations: vector
 // memory loads issued before it stay in flight (the compiler still waits for

@@ -69,6 +69,11 @@ hipError_t launch_w4a8_generic(const W4A8Args &a, hipStream_t st);
 
 // W4A16.
 bool w4a16_fast_ok(int64_t M, int64_t K, int64_t N, int64_t group);
+// group == 128, K % 512 == 0, 16-byte aligned operands: LDS-staged kernel.
+bool w4a16_lds_ok(int64_t K, int64_t group);
+hipError_t launch_w4a16_lds(const uint16_t *X, int64_t M, int64_t K, int64_t N,
+                            const uint8_t *packed, const float *scales, const float *zeros,
+                            float *Y, hipStream_t st);
 hipError_t launch_w4a16_mfma(const uint16_t *X, int64_t M, int64_t K, int64_t N,
                              const uint8_t *packed, const float *scales, const float *zeros,
                              int64_t group, float *Y, hipStream_t st);

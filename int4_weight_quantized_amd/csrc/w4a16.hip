@@ -248,6 +248,210 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_mfma(const uint16_t *__restric
     }
 }
 
+// ------------------------------------------------ LDS-staged, group 128
+// Block = 2 K halves x WPH waves x 16 output channels for 16 activation rows.
+// In each half, the packed weights, the activations and the scales and zero
+// points of 2 consecutive 128-k steps form one stage; a 3-stage ring per half
+// is filled with direct buffer->LDS loads two stages ahead of the one being
+// multiplied, so many weight bytes are in flight without holding registers.
+// The waves of a half read the same activation stage (fetched once per
+// half-block, not once per wave).  The halves' partial sums meet in LDS in a
+// fixed order.  WPH is chosen so that the blocks cover the output channels in
+// one round over the CUs (the 28672-channel layer: 7 waves per half, 256
+// blocks).
+//
+// LDS layouts (all reads are 16 rows x one 16-byte chunk per quarter-wave of
+// 64-byte rows, chunk kq at slot kq ^ ((row/2) % 4), which is conflict-free):
+//   W plane j (step j of the stage): [16*WPH channels][64 B]
+//   X plane (j, q): [16 rows][64 B]; row r's chunk kq holds the 16 bytes of
+//     activations x[r][128 j + 32 kq + 8 q .. + 8]
+//   S, Z: [16*WPH channels][4 groups] fp32, the 16-byte-aligned group quad
+//     that holds the stage's groups
+constexpr int kLSteps = 2;   // 128-k steps per stage
+constexpr int kLStages = 3;  // ring depth per half
+
+template <int WPH>
+struct W4a16Lds {
+    static constexpr int kCh = 16 * WPH;                       // channels per block
+    static constexpr int kW = kCh * 64 * kLSteps;              // weight bytes per stage
+    static constexpr int kX = 4096 * kLSteps;                  // activation bytes per stage
+    static constexpr int kSZ = ((kCh * 16 + 1023) / 1024) * 1024;  // per table, whole KB
+    static constexpr int kStage = kW + kX + 2 * kSZ;
+    static constexpr int kLoadsW = kW / 1024, kLoadsX = kX / 1024, kLoadsSZ = kSZ / 1024;
+    static constexpr int kLoads = kLoadsW + kLoadsX + 2 * kLoadsSZ;
+    static constexpr int kPerWave = (kLoads + WPH - 1) / WPH;  // every wave issues as many
+    static_assert(2 * kLStages * kStage <= 160 * 1024, "ring fits in LDS");
+};
+
+template <int WPH>
+__global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restrict__ X,
+                                                         const uint8_t *__restrict__ packed,
+                                                         const float *__restrict__ scales,
+                                                         const float *__restrict__ zeros,
+                                                         float *__restrict__ Y, int64_t M,
+                                                         int64_t K64, int64_t N) {
+    using L = W4a16Lds<WPH>;
+    __shared__ __align__(16) uint8_t ring[2 * kLStages * L::kStage];  // [half][stage]
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int half = wave / WPH, wl = wave % WPH;
+    const int lane = threadIdx.x % kWave;
+    const int r16 = lane % 16, kq = lane / 16;
+    const int K = (int)K64, KB = K / 2, G = K / 128;
+    const int64_t n0 = (int64_t)blockIdx.x * L::kCh;
+    const int64_t m0 = (int64_t)blockIdx.y * 16;
+    const int cols = (int)min((int64_t)L::kCh, N - n0);
+    const int rowsm = (int)min((int64_t)16, M - m0);
+
+    // Descriptors cover exactly this block's channels / rows: channels past N
+    // and rows past M read zeros (their outputs are not stored).
+    const v4i rw = buffer_desc(packed + n0 * KB, (int64_t)cols * KB);
+    const v4i rx = buffer_desc(X + m0 * K, (int64_t)rowsm * K * 2);
+    const v4i rs = buffer_desc(scales + n0 * G, (int64_t)cols * G * 4);
+    const v4i rz = buffer_desc(zeros + n0 * G, (int64_t)cols * G * 4);
+
+    const int T = G / (2 * kLSteps);    // stages per half
+    const int s0 = half * T * kLSteps;  // first step of this half
+    uint8_t *const hbase = ring + half * kLStages * L::kStage;
+
+    // Stage t of a half covers steps s0 + 2t, s0 + 2t + 1.  Its 1 KB
+    // wave-loads q: weights (step j = q / WPH, channels 16*(q % WPH) + lane/4),
+    // then activations (step, plane, row lane/4), then the scale and
+    // zero-point tables (lane = channel within a 64-channel group).
+    // Wave wl issues q = wl + WPH*i, i < kPerWave; indices past the end repeat
+    // the last load (same data to the same place), so every wave issues the
+    // same number of loads and waits on the same count.
+    const int sw4 = (lane % 4) ^ ((lane / 8) % 4);  // stored slot -> chunk
+    auto issue = [&](int t) {
+        const uint32_t base = lds_addr(hbase + (t % kLStages) * L::kStage);
+        const int step = s0 + kLSteps * t;
+#pragma unroll
+        for (int i = 0; i < L::kPerWave; ++i) {
+            const int q = min(wl + WPH * i, L::kLoads - 1);
+            if (q < L::kLoadsW) {
+                const int j = q / WPH, c = 16 * (q % WPH) + lane / 4;
+                dma16(rw, base + q * 1024, c * KB + 16 * sw4, (step + j) * 64);
+            } else if (q < L::kLoadsW + L::kLoadsX) {
+                const int qq = q - L::kLoadsW, j = qq / 4, pl = qq % 4, r = lane / 4;
+                dma16(rx, base + L::kW + qq * 1024, r * K * 2 + (4 * sw4 + pl) * 16,
+                      (step + j) * 256);
+            } else {
+                const int qq = q - L::kLoadsW - L::kLoadsX;
+                const int tab = qq / L::kLoadsSZ, part = qq % L::kLoadsSZ;
+                dma16(tab == 0 ? rs : rz, base + L::kW + L::kX + tab * L::kSZ + part * 1024,
+                      (64 * part + lane) * G * 4, (step / 4) * 16);
+            }
+        }
+    };
+
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    const int ch = 16 * wl + r16;                         // this lane's channel
+    const int swz = (kq ^ ((r16 / 2) % 4)) * 16;          // (row/2)%4 = (r16/2)%4
+    const int woff = ch * 64 + swz;
+    const int xoff = L::kW + r16 * 64 + swz;
+
+    auto compute = [&](int t) {
+        const uint8_t *sb = hbase + (t % kLStages) * L::kStage;
+        // scales / zero points of the quad holding this stage's groups
+        const float4 sc4 = *reinterpret_cast<const float4 *>(sb + L::kW + L::kX + ch * 16);
+        const float4 zp4 = *reinterpret_cast<const float4 *>(sb + L::kW + L::kX + L::kSZ + ch * 16);
+        const int g0 = (s0 + kLSteps * t) % 4;   // 0 or 2
+        const float scs[2] = {g0 ? sc4.z : sc4.x, g0 ? sc4.w : sc4.y};
+        const float zps[2] = {g0 ? zp4.z : zp4.x, g0 ? zp4.w : zp4.y};
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < kLSteps; ++j)
+            ok = ok && (zps[j] >= -112.0f) && (zps[j] <= 128.0f) && (fabsf(scs[j]) < 0x1p100f);
+        const bool fast = __all(ok);
+#pragma unroll
+        for (int j = 0; j < kLSteps; ++j) {
+            const uint4 w = *reinterpret_cast<const uint4 *>(sb + j * (L::kCh * 64) + woff);
+            uint4 xr[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                xr[q] = *reinterpret_cast<const uint4 *>(sb + xoff + (4 * j + q) * 1024);
+            v4i b0, b1, b2, b3;
+            if (fast) {
+                const uint32_t cadd = (uint32_t)(128 - (int)zps[j]) * 0x01010101u;
+                const float nbias = -128.0f * scs[j];
+                b0 = dequant8_fast(w.x, scs[j], cadd, nbias);
+                b1 = dequant8_fast(w.y, scs[j], cadd, nbias);
+                b2 = dequant8_fast(w.z, scs[j], cadd, nbias);
+                b3 = dequant8_fast(w.w, scs[j], cadd, nbias);
+            } else {
+                b0 = dequant8_direct(w.x, scs[j], zps[j]);
+                b1 = dequant8_direct(w.y, scs[j], zps[j]);
+                b2 = dequant8_direct(w.z, scs[j], zps[j]);
+                b3 = dequant8_direct(w.w, scs[j], zps[j]);
+            }
+            acc = mfma_bf16(xr[0], b0, acc);
+            acc = mfma_bf16(xr[1], b1, acc);
+            acc = mfma_bf16(xr[2], b2, acc);
+            acc = mfma_bf16(xr[3], b3, acc);
+        }
+    };
+
+    // Ring: stages t+1 and t+2 are in flight while stage t is multiplied.
+    // Before the barrier of step t this wave's loads of stage t are complete
+    // (at most the loads of stage t+1 outstanding); after it, every wave is
+    // done with stage t-1, whose slot receives stage t+2.
+    issue(0);
+    if (T > 1) issue(1);
+    for (int t = 0; t < T; ++t) {
+        if (t + 1 < T)
+            wait_and_barrier<L::kPerWave>();
+        else
+            wait_and_barrier<0>();
+        if (t + 2 < T) issue(t + 2);
+        compute(t);
+    }
+
+    // the second half's partial sums, added to the first half's in LDS
+    wait_and_barrier<0>();
+    v4f *red = reinterpret_cast<v4f *>(ring) + wl * kWave + lane;
+    if (half == 1) *red = acc;
+    wait_and_barrier<0>();
+    if (half == 1) return;
+    acc = acc + *red;
+    const int64_t col = n0 + ch;
+    if (col < N) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t r = m0 + 4 * kq + i;
+            if (r < M) Y[r * N + col] = acc[i];
+        }
+    }
+}
+
+bool w4a16_lds_ok(int64_t K, int64_t group) { return group == 128 && K % (256 * kLSteps) == 0; }
+
+template <int WPH>
+static void go_w4a16_lds(const uint16_t *X, int64_t M, int64_t K, int64_t N, const uint8_t *packed,
+                         const float *scales, const float *zeros, float *Y, hipStream_t st) {
+    const int64_t mblocks = (M + 15) / 16;
+    for (int64_t mb0 = 0; mb0 < mblocks; mb0 += 65535) {
+        const int64_t cnt = (mblocks - mb0) < 65535 ? (mblocks - mb0) : 65535;
+        dim3 grid((unsigned)((N + 16 * WPH - 1) / (16 * WPH)), (unsigned)cnt);
+        launch_main(k_w4a16_lds<WPH>, grid, dim3(128 * WPH), 0, st, X + mb0 * 16 * K, packed,
+                    scales, zeros, Y + mb0 * 16 * N, M - mb0 * 16, K, N);
+    }
+}
+
+// Waves per half: enough channels per block that the channel blocks of one
+// 16-row block fit in one round over the 256 CUs (at most 7 waves per half).
+hipError_t launch_w4a16_lds(const uint16_t *X, int64_t M, int64_t K, int64_t N,
+                            const uint8_t *packed, const float *scales, const float *zeros,
+                            float *Y, hipStream_t st) {
+    const int64_t groups16 = (N + 15) / 16;
+    const int64_t wph = (groups16 + 255) / 256;
+    switch (wph <= 1 ? 1 : wph <= 2 ? 2 : wph <= 4 ? 4 : 7) {
+        case 1: go_w4a16_lds<1>(X, M, K, N, packed, scales, zeros, Y, st); break;
+        case 2: go_w4a16_lds<2>(X, M, K, N, packed, scales, zeros, Y, st); break;
+        case 4: go_w4a16_lds<4>(X, M, K, N, packed, scales, zeros, Y, st); break;
+        default: go_w4a16_lds<7>(X, M, K, N, packed, scales, zeros, Y, st); break;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_w4a16_mfma(const uint16_t *X, int64_t M, int64_t K, int64_t N,
                              const uint8_t *packed, const float *scales, const float *zeros,
                              int64_t group, float *Y, hipStream_t st) {

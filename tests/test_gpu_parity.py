@@ -314,7 +314,9 @@ def _w4a16_check(got, yref, absy, K):
 
 
 W4A16_CASES = [(1, 128, 16, 128), (16, 256, 70, 128), (5, 512, 33, 64), (16, 1024, 130, 32),
-               (20, 384, 48, 128), (3, 96, 10, 32), (2, 40, 6, 4), (64, 256, 64, 128)]
+               (20, 384, 48, 128), (3, 96, 10, 32), (2, 40, 6, 4), (64, 256, 64, 128),
+               # LDS-staged kernel (group 128, K % 512 == 0): ragged N and M
+               (16, 512, 70, 128), (33, 1024, 130, 128), (1, 2048, 64, 128)]
 
 
 @pytest.mark.parametrize("M,K,N,g", W4A16_CASES)
@@ -332,9 +334,10 @@ def test_w4a16_linear(M, K, N, g):
     assert guards_intact(bufy, py)
 
 
-def test_w4a16_zero_point_outside_fast_range():
+@pytest.mark.parametrize("K", [256, 1024])
+def test_w4a16_zero_point_outside_fast_range(K):
     """Groups whose zero point leaves [-112, 128] take the direct dequantization."""
-    K, N, M, g = 256, 32, 4, 128
+    N, M, g = 32, 4, 128
     rng = np.random.default_rng(77)
     W = (rng.standard_normal((K, N)) * 0.01).astype(np.float32)
     W[:, :8] += 3.0       # far-positive groups: zero point about -4000
@@ -355,7 +358,7 @@ def test_w4a16_full_workload():
     W, xb, g = d["W"], d["x_bf16"], d["group"]
     packed, s, z = W4.w4_quantize_weight(dev(W), "asym", g)
     y = W4.w4a16_linear(dev(xb.view(np.int16)), packed, s, z, g)
-    assert W4.w4_last_path() == "w4a16_mfma"
+    assert W4.w4_last_path() == "w4a16_lds"
     got = host(y)
     cols = _sample(W.shape[1], 384, 3)
     pref, sref, zref = oracle.quantize_weight_asym(np.ascontiguousarray(W[:, cols]), g)
