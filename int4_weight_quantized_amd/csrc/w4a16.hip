@@ -263,8 +263,9 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_mfma(const uint16_t *__restric
 // LDS layouts (all reads are 16 rows x one 16-byte chunk per quarter-wave of
 // 64-byte rows, chunk kq at slot kq ^ ((row/2) % 4), which is conflict-free):
 //   W plane j (step j of the stage): [16*WPH channels][64 B]
-//   X plane (j, q): [16 rows][64 B]; row r's chunk kq holds the 16 bytes of
-//     activations x[r][128 j + 32 kq + 8 q .. + 8]
+//   X plane (j, kq): [16 rows][64 B] = the 32 activations x[r][128 j + 32 kq ..
+//     + 32] of each row, 16-byte chunk q at slot q ^ kq ^ ((r/2) % 4) (the
+//     quarter-waves kq then read distinct slot columns: conflict-free)
 //   S, Z: [16*WPH channels][4 groups] fp32, the 16-byte-aligned group quad
 //     that holds the stage's groups
 constexpr int kLSteps = 2;   // 128-k steps per stage
@@ -315,7 +316,8 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
 
     // Stage t of a half covers steps s0 + 2t, s0 + 2t + 1.  Its 1 KB
     // wave-loads q: weights (step j = q / WPH, channels 16*(q % WPH) + lane/4),
-    // then activations (step, plane, row lane/4), then the scale and
+    // then activations (step, plane kq, row lane/4: 64 contiguous bytes per
+    // row), then the scale and
     // zero-point tables (lane = channel within a 64-channel group).
     // Wave wl issues q = wl + WPH*i, i < kPerWave; indices past the end repeat
     // the last load (same data to the same place), so every wave issues the
@@ -331,8 +333,8 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
                 const int j = q / WPH, c = 16 * (q % WPH) + lane / 4;
                 dma16(rw, base + q * 1024, c * KB + 16 * sw4, (step + j) * 64);
             } else if (q < L::kLoadsW + L::kLoadsX) {
-                const int qq = q - L::kLoadsW, j = qq / 4, pl = qq % 4, r = lane / 4;
-                dma16(rx, base + L::kW + qq * 1024, r * K * 2 + (4 * sw4 + pl) * 16,
+                const int qq = q - L::kLoadsW, j = qq / 4, pk = qq % 4, r = lane / 4;
+                dma16(rx, base + L::kW + qq * 1024, r * K * 2 + 64 * pk + 16 * (sw4 ^ pk),
                       (step + j) * 256);
             } else {
                 const int qq = q - L::kLoadsW - L::kLoadsX;
@@ -347,7 +349,7 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
     const int ch = 16 * wl + r16;                         // this lane's channel
     const int swz = (kq ^ ((r16 / 2) % 4)) * 16;          // (row/2)%4 = (r16/2)%4
     const int woff = ch * 64 + swz;
-    const int xoff = L::kW + r16 * 64 + swz;
+    const int xoff = L::kW + kq * 1024 + r16 * 64;
 
     auto compute = [&](int t) {
         const uint8_t *sb = hbase + (t % kLStages) * L::kStage;
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
             uint4 xr[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                xr[q] = *reinterpret_cast<const uint4 *>(sb + xoff + (4 * j + q) * 1024);
+                xr[q] = *reinterpret_cast<const uint4 *>(sb + xoff + 4096 * j + (swz ^ (16 * q)));
             v4i b0, b1, b2, b3;
             if (fast) {
                 const uint32_t cadd = (uint32_t)(128 - (int)zps[j]) * 0x01010101u;
