@@ -13,6 +13,10 @@ arrays.  The formulas and their sources are documented there:
 * per-row dynamic int8 activations (scale = absmax / 127) -- same, step 3;
 * exact int8 x int4 products summed in int32 -- steps 4-5;
 * dequantization by input_scale * per_channel_kernel_scale -- step 6;
+* symmetric per-output-channel int8 weights (scale = absmax / 127, codes in
+  [-128, 127], one per byte) and the W8A8 forward -- the INT8 path that the
+  Keras guide's "How it works" says the INT4 path follows apart from the
+  unpacking; "INT4" concept entry, section 4.1 with b = 8;
 * asymmetric group-wise int4 (scale = range / 15, zero point, codes 0..15)
   and the weight-only W4A16 product -- "4-bit Integer Quantization for LLMs",
   quantization principle; "INT4" concept entry, sections 4.1, 4.2 and 4.5.
@@ -54,6 +58,9 @@ def _load():
             "orc_dequant": [_P, _P, _P, _P, _I, _I, _P],
             "orc_w4a8_linear": [_P, _I, _I, _I, _P, _P, _P, _P],
             "orc_quantize_weight_asym": [_P, _I, _I, _I, _P, _P, _P],
+            "orc_quantize_weight_w8": [_P, _I, _I, _P, _P],
+            "orc_matmul_w8_i32": [_P, _P, _I, _I, _I, _P],
+            "orc_w8a8_linear": [_P, _I, _I, _I, _P, _P, _P, _P],
             "orc_w4a16_dequant": [_P, _P, _P, _I, _I, _I, _P],
             "orc_w4a16_linear": [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P],
         }
@@ -158,6 +165,44 @@ def w4a8_linear(X: np.ndarray, packed: np.ndarray, sw: np.ndarray, bias=None) ->
     Y = np.zeros((M, N), np.float32)
     _check(_load().orc_w4a8_linear(_ptr(X), M, K, N, _ptr(packed), _ptr(sw), _ptr(b), _ptr(Y)),
            "w4a8_linear")
+    return Y
+
+
+def quantize_weight_w8(W: np.ndarray):
+    """W [K, N] fp32 -> (Wq int8 [N, K], sw fp32 [N])."""
+    W = _f32(W)
+    K, N = W.shape
+    Wq = np.zeros((N, K), np.int8)
+    sw = np.zeros(N, np.float32)
+    _check(_load().orc_quantize_weight_w8(_ptr(W), K, N, _ptr(Wq), _ptr(sw)),
+           "quantize_weight_w8")
+    return Wq, sw
+
+
+def matmul_w8_i32(Xq: np.ndarray, Wq: np.ndarray) -> np.ndarray:
+    """acc [M, N] int32 = Xq [M, K] times Wq [N, K] transposed (exact)."""
+    Xq = np.ascontiguousarray(Xq, np.int8)
+    Wq = np.ascontiguousarray(Wq, np.int8)
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    assert Wq.shape[1] == K
+    acc = np.zeros((M, N), np.int32)
+    _check(_load().orc_matmul_w8_i32(_ptr(Xq), _ptr(Wq), M, K, N, _ptr(acc)), "matmul_w8_i32")
+    return acc
+
+
+def w8a8_linear(X: np.ndarray, Wq: np.ndarray, sw: np.ndarray, bias=None) -> np.ndarray:
+    """Y [M, N] fp32 of the whole W8A8 forward."""
+    X = _f32(X)
+    M, K = X.shape
+    Wq = np.ascontiguousarray(Wq, np.int8)
+    N = Wq.shape[0]
+    assert Wq.shape[1] == K
+    sw = _f32(sw)
+    b = None if bias is None else _f32(bias)
+    Y = np.zeros((M, N), np.float32)
+    _check(_load().orc_w8a8_linear(_ptr(X), M, K, N, _ptr(Wq), _ptr(sw), _ptr(b), _ptr(Y)),
+           "w8a8_linear")
     return Y
 
 

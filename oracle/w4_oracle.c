@@ -171,6 +171,74 @@ int orc_w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N,
     return rc;
 }
 
+/* W8A8, the INT8 path that [KERAS] "How it works" says the INT4 path follows
+ * apart from the unpacking: steps 1-6 with 8-bit weight codes.  [ENCY] 4.1
+ * with b = 8: symmetric scale = max|x| / (2^(b-1) - 1) = / 127 per output
+ * channel; codes are round(W/scale) limited to the int8 range [-128, 127]
+ * (INT4-vs-INT8 comparison article, 2.1).  The codes are stored one per byte
+ * as int8, channel-major: Wq[n*K + k]. */
+int orc_quantize_weight_w8(const float *W, int64_t K, int64_t N, int8_t *Wq, float *sw) {
+    if (K < 1 || N < 1) return ORC_ERR_SHAPE;
+    if (!round_mode_ok()) return ORC_ERR_ROUNDMODE;
+    for (int64_t n = 0; n < N; ++n) {
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float w = W[k * N + n];
+            if (!isfinite(w)) return ORC_ERR_NONFINITE;
+            float aw = fabsf(w);
+            if (aw > a) a = aw;
+        }
+        float s = (a == 0.0f) ? 0.0f : a / 127.0f;
+        sw[n] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            int q = 0;
+            if (s != 0.0f) {
+                float t = W[k * N + n] / s;
+                float r = clampf(rne(t), -128.0f, 127.0f);
+                q = (int)r;
+            }
+            Wq[n * K + k] = (int8_t)q;
+        }
+    }
+    return ORC_OK;
+}
+
+/* [KERAS] step 5 for 8-bit weights: acc[m][n] = sum_k Xq[m][k] * Wq[n][k],
+ * summed in int64 and checked to fit int32. */
+int orc_matmul_w8_i32(const int8_t *Xq, const int8_t *Wq, int64_t M, int64_t K, int64_t N,
+                      int32_t *acc) {
+    if (M < 1 || K < 1 || N < 1) return ORC_ERR_SHAPE;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t s = 0;
+            for (int64_t k = 0; k < K; ++k)
+                s += (int64_t)Xq[m * K + k] * (int64_t)Wq[n * K + k];
+            if (s > INT32_MAX || s < INT32_MIN) return ORC_ERR_RANGE;
+            acc[m * N + n] = (int32_t)s;
+        }
+    }
+    return ORC_OK;
+}
+
+/* The whole W8A8 forward: steps 3, 5 and 6 as in orc_w4a8_linear. */
+int orc_w8a8_linear(const float *X, int64_t M, int64_t K, int64_t N, const int8_t *Wq,
+                    const float *sw, const float *bias, float *Y) {
+    if (M < 1 || K < 1 || N < 1) return ORC_ERR_SHAPE;
+    int8_t *Xq = (int8_t *)malloc((size_t)(M * K));
+    float *sx = (float *)malloc((size_t)M * sizeof(float));
+    int32_t *acc = (int32_t *)malloc((size_t)(M * N) * sizeof(int32_t));
+    int rc = ORC_ERR_SHAPE;
+    if (Xq && sx && acc) {
+        rc = orc_quantize_act(X, M, K, Xq, sx);
+        if (rc == ORC_OK) rc = orc_matmul_w8_i32(Xq, Wq, M, K, N, acc);
+        if (rc == ORC_OK) rc = orc_dequant(acc, sx, sw, bias, M, N, Y);
+    }
+    free(Xq);
+    free(sx);
+    free(acc);
+    return rc;
+}
+
 /* [W4A16] "量化原理": W_int = round(W/scale + zero_point), dequantized as
  * (W_int - zero_point) * scale, codes 0..15.  [ENCY] 4.1: asymmetric scale =
  * (x_max - x_min) / (2^b - 1) = / 15, x_q = round(x/scale) + zero_point.

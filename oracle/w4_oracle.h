@@ -61,6 +61,18 @@ int orc_w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N,
                     const uint8_t *packed, const float *sw, const float *bias,
                     float *Y);
 
+/* Symmetric per-output-channel int8 weight quantization (scale = absmax/127,
+ * codes in [-128, 127]).  Outputs Wq [N][K] int8 (channel-major), sw [N]. */
+int orc_quantize_weight_w8(const float *W, int64_t K, int64_t N, int8_t *Wq, float *sw);
+
+/* acc[m][n] = sum_k Xq[m][k] * Wq[n][k]  (exact integer dot product). */
+int orc_matmul_w8_i32(const int8_t *Xq, const int8_t *Wq, int64_t M, int64_t K, int64_t N,
+                      int32_t *acc);
+
+/* The whole W8A8 forward: quantize X per row, integer GEMM, dequant (+bias). */
+int orc_w8a8_linear(const float *X, int64_t M, int64_t K, int64_t N, const int8_t *Wq,
+                    const float *sw, const float *bias, float *Y);
+
 /* Asymmetric group-wise int4 quantization along K (codes 0..15).
  * Outputs packed [N][(K+1)/2], scales [N][K/g], zeros [N][K/g] (integer-valued). */
 int orc_quantize_weight_asym(const float *W, int64_t K, int64_t N, int64_t group,
