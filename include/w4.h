@@ -60,7 +60,8 @@ typedef enum {
 } w4_scheme;
 
 /* Largest K accepted by the integer paths: |acc| <= 128*8*K must fit int32
- * with the 16x headroom the unpacking uses (16*1024*K < 2^31). */
+ * with the 16x headroom the unpacking uses (16*1024*K < 2^31); the W8A8
+ * bound 128*128*K < 2^31 is the same. */
 #define W4_MAX_K 131071
 
 /* Quantize a weight matrix and pack it (Keras guide steps 1-2 for
@@ -127,6 +128,37 @@ int w4a8_linear_q(const int8_t *Xq, const float *sx, const uint8_t *packed,
 int w4a8_matmul_i32(const int8_t *Xq, const uint8_t *packed, int64_t M,
                     int64_t K, int64_t N, int32_t *acc, void *workspace,
                     size_t workspace_bytes, void *stream);
+
+/* ---- W8A8: the INT8 path that the Keras guide's "How it works" says the
+ * INT4 path follows apart from the unpacking (steps 1-6 with 8-bit weight
+ * codes; "INT4" concept entry, section 4.1 with b = 8 for the scale). */
+
+/* Symmetric per-output-channel int8 weight quantization.
+ *   W   [K][N] fp32, finite.
+ *   sw  [N]: sw[n] = fl(max_k |W[k][n]| / 127) (0 for an all-zero channel).
+ *   Wq  [N][K] int8, channel-major (one code per byte, no packing):
+ *       clamp(rne(fl(W / sw)), -128, 127) (0 where sw is 0).
+ * Returns W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN or W4_ERR_HIP. */
+int w8_quantize_weight(const float *W, int64_t K, int64_t N, int8_t *Wq, float *sw,
+                       void *stream);
+
+/* Bytes of device workspace that w8a8_linear and w8a8_matmul_i32 need (0 when
+ * none is needed, and for invalid sizes). */
+size_t w8a8_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/* The W8A8 forward: as w4a8_linear with int8 weight codes Wq [N][K] (any byte
+ * values) and scales sw [N] from w8_quantize_weight:
+ *   Y = fl(fl(float(acc) * fl(sx[m] * sw[n])) [+ bias[n]]),
+ *   acc = sum_k Xq[m][k] * Wq[n][k] exactly.
+ * Workspace, alignment and return codes as w4a8_linear. */
+int w8a8_linear(const float *X, int64_t M, int64_t K, int64_t N, const int8_t *Wq,
+                const float *sw, const float *bias, float *Y, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+/* The exact W8A8 integer product alone, for checking:
+ *   acc [M][N] int32 = sum_k Xq[m][k] * Wq[n][k]. */
+int w8a8_matmul_i32(const int8_t *Xq, const int8_t *Wq, int64_t M, int64_t K, int64_t N,
+                    int32_t *acc, void *workspace, size_t workspace_bytes, void *stream);
 
 /* The weight-only W4A16 forward (weight-only page: activations stay 16-bit,
  * weights are dequantized at compute time; concept entry 4.5, schemes A/C).

@@ -11,6 +11,9 @@ functions carry the C names:
 * ``w4a8_linear``         -- the W4A8 forward from fp32 activations;
 * ``w4a8_linear_q``       -- the W4A8 forward from int8 activations;
 * ``w4a8_matmul_i32``     -- the exact int32 accumulators alone;
+* ``w8_quantize_weight``  -- symmetric per-channel int8 weights (W8A8);
+* ``w8a8_linear``         -- the W8A8 forward from fp32 activations;
+* ``w8a8_matmul_i32``     -- its exact int32 accumulators alone;
 * ``w4a16_linear``        -- the weight-only forward with bf16 activations.
 
 There is no CPU fallback: without the built library (``build.py``) or
@@ -60,6 +63,10 @@ def lib():
             "w4a8_linear_q": ([_P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _Z, _P], ctypes.c_int),
             "w4a8_matmul_i32": ([_P, _P, _I, _I, _I, _P, _P, _Z, _P], ctypes.c_int),
             "w4a16_linear": ([_P, _I, _I, _I, _P, _P, _P, _I, _P, _P], ctypes.c_int),
+            "w8_quantize_weight": ([_P, _I, _I, _P, _P, _P], ctypes.c_int),
+            "w8a8_workspace_bytes": ([_I, _I, _I], _Z),
+            "w8a8_linear": ([_P, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P], ctypes.c_int),
+            "w8a8_matmul_i32": ([_P, _P, _I, _I, _I, _P, _P, _Z, _P], ctypes.c_int),
             "w4_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "w4_last_path": ([], ctypes.c_char_p),
             "w4_time_next_kernel": ([_P, _P], ctypes.c_int),
@@ -213,6 +220,51 @@ def w4a8_matmul_i32(Xq: torch.Tensor, packed: torch.Tensor, acc=None, workspace=
                                _dev(workspace, "workspace", torch.uint8), workspace.numel(),
                                _stream(stream))
     _check("w4a8_matmul_i32", rc)
+    return acc
+
+
+def w8_quantize_weight(W: torch.Tensor, Wq=None, sw=None, stream=None):
+    """W [K, N] fp32 -> (Wq int8 [N, K], sw fp32 [N])."""
+    K, N = W.shape
+    if Wq is None:
+        Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    if sw is None:
+        sw = torch.empty((N,), dtype=torch.float32, device=W.device)
+    rc = lib().w8_quantize_weight(_dev(W, "W", torch.float32), K, N, _dev(Wq, "Wq", torch.int8),
+                                  _dev(sw, "sw", torch.float32), _stream(stream))
+    _check("w8_quantize_weight", rc)
+    return Wq, sw
+
+
+def w8a8_linear(X: torch.Tensor, Wq: torch.Tensor, sw: torch.Tensor, bias=None, Y=None,
+                workspace=None, stream=None) -> torch.Tensor:
+    """Y [M, N] fp32 = dequant(quant(X) . Wq^T) (+ bias)."""
+    M, K = X.shape
+    N = Wq.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    workspace, need = _workspace(M, K, N, X.device, workspace)
+    rc = lib().w8a8_linear(_dev(X, "X", torch.float32), M, K, N, _dev(Wq, "Wq", torch.int8),
+                           _dev(sw, "sw", torch.float32), _opt(bias, "bias", torch.float32),
+                           _dev(Y, "Y", torch.float32),
+                           _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                           _stream(stream))
+    _check("w8a8_linear", rc)
+    return Y
+
+
+def w8a8_matmul_i32(Xq: torch.Tensor, Wq: torch.Tensor, acc=None, workspace=None,
+                    stream=None) -> torch.Tensor:
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    if acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
+    workspace, need = _workspace(M, K, N, Xq.device, workspace)
+    rc = lib().w8a8_matmul_i32(_dev(Xq, "Xq", torch.int8), _dev(Wq, "Wq", torch.int8), M, K, N,
+                               _dev(acc, "acc", torch.int32),
+                               _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                               _stream(stream))
+    _check("w8a8_matmul_i32", rc)
     return acc
 
 

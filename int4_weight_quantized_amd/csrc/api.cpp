@@ -34,13 +34,15 @@ bool shape_ok(int64_t M, int64_t K, int64_t N) {
 
 enum class Src { FP32, Q };
 
-// Shared dispatch of the three W4A8 entry points.
-int w4a8_dispatch(Src src, const float *X, const int8_t *Xq, const float *sx,
+// Shared dispatch of the W4A8 and W8A8 entry points (w8: `packed` holds int8
+// codes [N][K]; the MFMA paths then take natural-layout activations).
+int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const float *sx,
                   const uint8_t *packed, const float *sw, const float *bias, int64_t M,
                   int64_t K, int64_t N, float *Y, int32_t *acc, void *workspace,
                   size_t workspace_bytes, hipStream_t st) {
     using namespace w4;
     W4A8Args a{};
+    a.w8 = w8;
     a.X = nullptr;
     a.Xq = Xq;
     a.sx = sx;
@@ -62,27 +64,29 @@ int w4a8_dispatch(Src src, const float *X, const int8_t *Xq, const float *sx,
     hipError_t e;
 
     // Few rows: one VALU GEMV launch (activation quantization fused).
-    if (aligned16 && gemv_dot4_ok(M, K)) {
+    if (aligned16 && gemv_dot4_ok(M, K, w8)) {
         if (src == Src::FP32) a.X = X;
-        g_last_path = "gemv_dot4";
+        g_last_path = w8 ? "w8_gemv_dot4" : "gemv_dot4";
         return hip_status(launch_gemv_dot4(a, st));
     }
-    // Activations for the MFMA paths: P8 layout in the workspace.
+    // Activations for the MFMA paths: P8 layout in the workspace (natural
+    // layout for 8-bit weights, which then use pre-quantized input as is).
     if (fast) {
         if (src == Src::FP32) {
-            e = launch_quant_act(X, M, K, ws_q, ws_s, true, st);
+            e = launch_quant_act(X, M, K, ws_q, ws_s, !w8, st);
             if (e != hipSuccess) return W4_ERR_HIP;
             a.sx = ws_s;
-        } else {
+            a.Xq = ws_q;
+        } else if (!w8) {
             e = launch_to_p8(Xq, M, K, ws_q, st);
             if (e != hipSuccess) return W4_ERR_HIP;
+            a.Xq = ws_q;
         }
-        a.Xq = ws_q;
         if (M <= 64) {
-            g_last_path = "gemv_mfma";
+            g_last_path = w8 ? "w8_gemv_mfma" : "gemv_mfma";
             return hip_status(launch_gemv_mfma(a, st));
         }
-        g_last_path = "gemm_mfma";
+        g_last_path = w8 ? "w8_gemm_mfma" : "gemm_mfma";
         return hip_status(launch_gemm_mfma(a, st));
     }
     // Anything else: natural layout, one thread per output.
@@ -92,7 +96,7 @@ int w4a8_dispatch(Src src, const float *X, const int8_t *Xq, const float *sx,
         a.Xq = ws_q;
         a.sx = ws_s;
     }
-    g_last_path = "w4a8_generic";
+    g_last_path = w8 ? "w8a8_generic" : "w4a8_generic";
     return hip_status(launch_w4a8_generic(a, st));
 }
 
@@ -181,8 +185,9 @@ int w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N, const uint8_t *
         return W4_ERR_ALIGN;
     int rc = check_workspace(M, K, workspace, workspace_bytes);
     if (rc != W4_OK) return rc;
-    return w4a8_dispatch(Src::FP32, X, nullptr, nullptr, packed, sw, bias, M, K, N, Y, nullptr,
-                         workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+    return w4a8_dispatch(Src::FP32, false, X, nullptr, nullptr, packed, sw, bias, M, K, N, Y,
+                         nullptr, workspace, workspace_bytes,
+                         reinterpret_cast<hipStream_t>(stream));
 }
 
 int w4a8_linear_q(const int8_t *Xq, const float *sx, const uint8_t *packed, const float *sw,
@@ -194,7 +199,7 @@ int w4a8_linear_q(const int8_t *Xq, const float *sx, const uint8_t *packed, cons
         return W4_ERR_ALIGN;
     int rc = check_workspace(M, K, workspace, workspace_bytes);
     if (rc != W4_OK) return rc;
-    return w4a8_dispatch(Src::Q, nullptr, Xq, sx, packed, sw, bias, M, K, N, Y, nullptr,
+    return w4a8_dispatch(Src::Q, false, nullptr, Xq, sx, packed, sw, bias, M, K, N, Y, nullptr,
                          workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -205,8 +210,49 @@ int w4a8_matmul_i32(const int8_t *Xq, const uint8_t *packed, int64_t M, int64_t 
     if (!aligned(acc, 4)) return W4_ERR_ALIGN;
     int rc = check_workspace(M, K, workspace, workspace_bytes);
     if (rc != W4_OK) return rc;
-    return w4a8_dispatch(Src::Q, nullptr, Xq, nullptr, packed, nullptr, nullptr, M, K, N,
+    return w4a8_dispatch(Src::Q, false, nullptr, Xq, nullptr, packed, nullptr, nullptr, M, K, N,
                          nullptr, acc, workspace, workspace_bytes,
+                         reinterpret_cast<hipStream_t>(stream));
+}
+
+int w8_quantize_weight(const float *W, int64_t K, int64_t N, int8_t *Wq, float *sw,
+                       void *stream) {
+    if (!W || !Wq || !sw) return W4_ERR_NULL;
+    if (!shape_ok(1, K, N)) return W4_ERR_SHAPE;
+    if (!aligned(W, 4) || !aligned(sw, 4)) return W4_ERR_ALIGN;
+    g_last_path = "quant_weight_w8";
+    return hip_status(
+        w4::launch_quant_weight_w8(W, K, N, Wq, sw, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t w8a8_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (!shape_ok(M, K, N)) return 0;
+    return ws_bytes(M, K);
+}
+
+int w8a8_linear(const float *X, int64_t M, int64_t K, int64_t N, const int8_t *Wq,
+                const float *sw, const float *bias, float *Y, void *workspace,
+                size_t workspace_bytes, void *stream) {
+    if (!X || !Wq || !sw || !Y) return W4_ERR_NULL;
+    if (!shape_ok(M, K, N)) return W4_ERR_SHAPE;
+    if (!aligned(X, 4) || !aligned(sw, 4) || !aligned(Y, 4) || (bias && !aligned(bias, 4)))
+        return W4_ERR_ALIGN;
+    int rc = check_workspace(M, K, workspace, workspace_bytes);
+    if (rc != W4_OK) return rc;
+    return w4a8_dispatch(Src::FP32, true, X, nullptr, nullptr,
+                         reinterpret_cast<const uint8_t *>(Wq), sw, bias, M, K, N, Y, nullptr,
+                         workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+int w8a8_matmul_i32(const int8_t *Xq, const int8_t *Wq, int64_t M, int64_t K, int64_t N,
+                    int32_t *acc, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!Xq || !Wq || !acc) return W4_ERR_NULL;
+    if (!shape_ok(M, K, N)) return W4_ERR_SHAPE;
+    if (!aligned(acc, 4)) return W4_ERR_ALIGN;
+    int rc = check_workspace(M, K, workspace, workspace_bytes);
+    if (rc != W4_OK) return rc;
+    return w4a8_dispatch(Src::Q, true, nullptr, Xq, nullptr, reinterpret_cast<const uint8_t *>(Wq),
+                         nullptr, nullptr, M, K, N, nullptr, acc, workspace, workspace_bytes,
                          reinterpret_cast<hipStream_t>(stream));
 }
 

@@ -18,6 +18,13 @@
 // (16 * code as int8) and the int32 sums are divided by 16 in the epilogue,
 // which also applies the dequantization.
 //
+// The W8A8 product (the guide's INT8 path: int8 weight codes, natural-order
+// activations, no unpacking) runs the same kernel with W8 = true: its weight
+// tile (256 channels x 128 int8 codes = 32 KB) has the activation tile's
+// shape and uses the same super-row layout and load pattern; a stage is then
+// 64 KB, so the ring has 2 stages (the next tile loads while the current one
+// is multiplied).
+//
 // Measured on gfx950: one wave per SIMD issues independent int8 MFMAs at
 // about 60% of the unit's rate and two or more at ~94%; VALU instructions
 // between MFMAs are not hidden.  Layouts with 16 waves (64x64 per wave) or 4
@@ -28,21 +35,26 @@
 
 namespace w4 {
 
-constexpr int kBM = 256, kBN = 256, kBK = 128, kStages = 3;
-constexpr int kABytes = kBM * kBK;       // 32 KB
-constexpr int kBBytes = kBN * kBK / 2;   // 16 KB
-constexpr int kStageBytes = kABytes + kBBytes;
+constexpr int kBM = 256, kBN = 256, kBK = 128;
+constexpr int kABytes = kBM * kBK;  // 32 KB
 
-template <Out OUT>
+template <bool W8>
+struct GemmStage {
+    static constexpr int kBBytes = W8 ? kBN * kBK : kBN * kBK / 2;  // 32 or 16 KB
+    static constexpr int kBytes = kABytes + kBBytes;
+};
+
+template <Out OUT, bool W8>
 __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
+    constexpr int kStageBytes = GemmStage<W8>::kBytes;
     // One array per ring stage: each unrolled iteration below names its
     // stages statically, so the compiler can tell the stage being read from
-    // the stages being filled.
+    // the stages being filled.  (8-bit weights use two stages.)
     __shared__ __align__(16) uint8_t stage0[kStageBytes];
     __shared__ __align__(16) uint8_t stage1[kStageBytes];
-    __shared__ __align__(16) uint8_t stage2[kStageBytes];
+    __shared__ __align__(16) uint8_t stage2[W8 ? 16 : kStageBytes];
 
-    const int64_t M = a.M, N = a.N, K = a.K, KB = a.K / 2;
+    const int64_t M = a.M, N = a.N, K = a.K, KB = W8 ? a.K : a.K / 2;
     const int tiles_n = (int)((N + kBN - 1) / kBN);
     const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
     const int64_t m0 = (int64_t)(tile / tiles_n) * kBM;
@@ -74,6 +86,8 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
     // B: 16 wave-loads of 16 channels x 64 B; this wave issues q = 2*wave + i,
     // i.e. channels 32*wave + 16*i + lane/4.  Stored position lane%4 holds the
     // channel's global chunk (lane%4) ^ ((lane/8)%4).
+    // With 8-bit weights the B tile repeats the A pattern (rows = channels,
+    // row stride K bytes), so the same per-lane offsets serve both.
     const v4i rbs = buffer_desc(a.packed + n0 * KB, min((int64_t)kBN, N - n0) * KB);
     const int b_voff = (32 * wave + lane / 4) * (int)KB + (((lane % 4) ^ ((lane / 8) % 4)) * 16);
     auto issue = [&](uint8_t *st, int kt) {
@@ -81,10 +95,17 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             dma16(ra, base + (4 * wave + i) * 1024, a_voff[i % 2], 8 * i * (int)K + kt * kBK);
+        if (W8) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            dma16(rbs, base + kABytes + (2 * wave + i) * 1024, b_voff,
-                  16 * i * (int)KB + kt * (kBK / 2));
+            for (int i = 0; i < 4; ++i)
+                dma16(rbs, base + kABytes + (4 * wave + i) * 1024, a_voff[i % 2],
+                      8 * i * (int)K + kt * kBK);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                dma16(rbs, base + kABytes + (2 * wave + i) * 1024, b_voff,
+                      16 * i * (int)KB + kt * (kBK / 2));
+        }
     };
 
     // ---- fragment read offsets inside a stage (row block rb adds rb*2048,
@@ -95,6 +116,13 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
     for (int h = 0; h < 2; ++h)
         aoff[h] = (wm * 64 + r16 / 2) * 256 + (((8 * (r16 % 2) + 2 * kq + h) ^ ((r16 / 2) % 8)) * 16);
     const int boff = kABytes + (wn * 64 + r16) * 64 + ((kq ^ ((r16 / 2) % 4)) * 16);
+    // 8-bit weights: channel c = wn*64 + nb*16 + r16 in super-row c/2 (the A
+    // formula with wn*32 super-rows per wave column; block nb adds nb*2048)
+    int b8off[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        b8off[h] = kABytes + (wn * 32 + r16 / 2) * 256 +
+                   (((8 * (r16 % 2) + 2 * kq + h) ^ ((r16 / 2) % 8)) * 16);
 
     v4i acc[8][4];
 #pragma unroll
@@ -104,18 +132,26 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
 
     auto compute = [&](const uint8_t *st) {
         uint4 wraw[4];
+        if (!W8) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-            wraw[nb] = *reinterpret_cast<const uint4 *>(st + boff + nb * 1024);
+            for (int nb = 0; nb < 4; ++nb)
+                wraw[nb] = *reinterpret_cast<const uint4 *>(st + boff + nb * 1024);
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            // this half's 16 codes of each channel block, unpacked (16 * code)
+            // this half's 16 codes of each channel block, unpacked (16 * code),
+            // or the 16 int8 codes themselves
             v4i bh[4];
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
-                const uint32_t p0 = h ? wraw[nb].z : wraw[nb].x;
-                const uint32_t p1 = h ? wraw[nb].w : wraw[nb].y;
-                bh[nb] = v4i{(int)lo16(p0), (int)hi16(p0), (int)lo16(p1), (int)hi16(p1)};
+                if (W8) {
+                    const uint4 w = *reinterpret_cast<const uint4 *>(st + b8off[h] + nb * 2048);
+                    bh[nb] = v4i{(int)w.x, (int)w.y, (int)w.z, (int)w.w};
+                } else {
+                    const uint32_t p0 = h ? wraw[nb].z : wraw[nb].x;
+                    const uint32_t p1 = h ? wraw[nb].w : wraw[nb].y;
+                    bh[nb] = v4i{(int)lo16(p0), (int)hi16(p0), (int)lo16(p1), (int)hi16(p1)};
+                }
             }
 #pragma unroll
             for (int rb = 0; rb < 8; ++rb) {
@@ -142,17 +178,35 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
         compute(cur);
     };
 
+    // 8-bit weights, 2-stage ring: tile kt sits in `cur` and is complete
+    // (no load outstanding) at the barrier, after which every wave is done
+    // with the other stage, which receives tile kt+1.
+    auto step2 = [&](int kt, int KT, const uint8_t *cur, uint8_t *nxt) {
+        wait_and_barrier<0>();
+        if (kt + 1 < KT) issue(nxt, kt + 1);
+        compute(cur);
+    };
+
     const int KT = (int)(K / kBK);
-    issue(stage0, 0);
-    if (KT > 1) issue(stage1, 1);
     int kt = 0;
-    for (; kt + 3 <= KT; kt += 3) {
-        step(kt, KT, stage0, stage2);
-        step(kt + 1, KT, stage1, stage0);
-        step(kt + 2, KT, stage2, stage1);
+    if (W8) {
+        issue(stage0, 0);
+        for (; kt + 2 <= KT; kt += 2) {
+            step2(kt, KT, stage0, stage1);
+            step2(kt + 1, KT, stage1, stage0);
+        }
+        if (kt < KT) step2(kt, KT, stage0, stage1);
+    } else {
+        issue(stage0, 0);
+        if (KT > 1) issue(stage1, 1);
+        for (; kt + 3 <= KT; kt += 3) {
+            step(kt, KT, stage0, stage2);
+            step(kt + 1, KT, stage1, stage0);
+            step(kt + 2, KT, stage2, stage1);
+        }
+        if (kt < KT) step(kt, KT, stage0, stage2);
+        if (kt + 1 < KT) step(kt + 1, KT, stage1, stage0);
     }
-    if (kt < KT) step(kt, KT, stage0, stage2);
-    if (kt + 1 < KT) step(kt + 1, KT, stage1, stage0);
 
     // ---- epilogue.  Dequantize in registers (lane holds rows 4*(lane/16)+i
     // of each 16x16 block, column lane%16), stage one 16-row block of each
@@ -180,7 +234,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
             const float sxr = (OUT == Out::Y) ? a.sx[min(row, M - 1)] : 0.0f;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
-                const int v = acc[rb][nb][i] >> 4;
+                const int v = W8 ? acc[rb][nb][i] : (acc[rb][nb][i] >> 4);
                 uint32_t bits;
                 if (OUT == Out::I32) {
                     bits = (uint32_t)v;
@@ -221,12 +275,20 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
     }
 }
 
-hipError_t launch_gemm_mfma(const W4A8Args &a, hipStream_t st) {
+template <bool W8>
+static void go_gemm(const W4A8Args &a, hipStream_t st) {
     const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
     if (a.out == Out::I32)
-        launch_main(k_gemm_mfma<Out::I32>, dim3((unsigned)tiles), dim3(512), 0, st, a);
+        launch_main(k_gemm_mfma<Out::I32, W8>, dim3((unsigned)tiles), dim3(512), 0, st, a);
     else
-        launch_main(k_gemm_mfma<Out::Y>, dim3((unsigned)tiles), dim3(512), 0, st, a);
+        launch_main(k_gemm_mfma<Out::Y, W8>, dim3((unsigned)tiles), dim3(512), 0, st, a);
+}
+
+hipError_t launch_gemm_mfma(const W4A8Args &a, hipStream_t st) {
+    if (a.w8)
+        go_gemm<true>(a, st);
+    else
+        go_gemm<false>(a, st);
     return hipGetLastError();
 }
 

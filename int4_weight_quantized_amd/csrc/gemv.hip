@@ -1,6 +1,8 @@
 // Decode-shaped W4A8 products (few activation rows, many output channels):
 // the packed int4 weights are streamed from HBM once with 128-bit loads and
-// unpacked in registers (Keras INT4 guide, "How it works", steps 4-5).
+// unpacked in registers (Keras INT4 guide, "How it works", steps 4-5).  The
+// same kernels run the W8A8 product (the guide's INT8 path: int8 weight codes,
+// no unpacking) when instantiated with W8 = true.
 //
 //  * k_gemv_dot4  (M <= 4): VALU dot products (v_dot4_i32_i8).  The
 //    activation quantization (step 3) is fused into the prologue, so one
@@ -26,21 +28,25 @@ namespace w4 {
 // flight (the barriers wait for LDS only, so the weight loads stay in
 // flight), (4) dot products, chunk by chunk as the loads land, (5) 16-lane
 // DPP sum and epilogue.
-constexpr int kDot4MaxK = 8192;
+// With W8 a 16-byte chunk holds 16 int8 codes (instead of 32 int4 codes) and
+// the activations stay in natural order.
+constexpr int kDot4MaxK = 8192, kDot4MaxKW8 = 4096;
 
-bool gemv_dot4_ok(int64_t M, int64_t K) {
-    return M >= 1 && M <= 4 && K % 32 == 0 && K <= kDot4MaxK;
+bool gemv_dot4_ok(int64_t M, int64_t K, bool w8) {
+    return M >= 1 && M <= 4 && K % 32 == 0 && K <= (w8 ? kDot4MaxKW8 : kDot4MaxK);
 }
 
-template <int M, int ROWS, int UB, bool FUSED, Out OUT>
+template <int M, int ROWS, int UB, bool FUSED, Out OUT, bool W8>
 __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
-    constexpr int T = 16 * ROWS;                   // threads
-    constexpr int NG = (4 * UB + ROWS - 1) / ROWS;  // 8-groups of k per thread (K <= 512*UB)
+    constexpr int T = 16 * ROWS;  // threads
+    constexpr int KPC = W8 ? 16 : 32;  // codes per 16-byte chunk
+    // 8-groups of k per thread (K <= 16 * KPC * UB)
+    constexpr int NG = (2 * KPC * UB / 16 + ROWS - 1) / ROWS;
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ float red[T / kWave][M];
     int8_t *xs = reinterpret_cast<int8_t *>(smem);
     const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
-    const int K = (int)a.K, KB = K / 2, C = K / 32, G8 = K / 8;
+    const int K = (int)a.K, KB = W8 ? K : K / 2, C = K / KPC, G8 = K / 8;
     const int j = t & 15, r = t >> 4;
     const int64_t n0 = (int64_t)blockIdx.x * ROWS;
     const int rows = (int)min((int64_t)ROWS, a.N - n0);
@@ -114,6 +120,7 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
             const float s = (am == 0.0f) ? 0.0f : am / 127.0f;
             sxm[m] = s;
             // codes of the thread's 8-groups, stored P8: [x0 x2 x4 x6 | x1 x3 x5 x7]
+            // (natural order for 8-bit weights)
             auto quantize = [&](auto code) {
 #pragma unroll
                 for (int i = 0; i < NG; ++i) {
@@ -121,8 +128,13 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
                     if (g < G8) {
                         const float4 v0 = xa[m][i], v1 = xb[m][i];
                         uint2 p;
-                        p.x = pack4_i8(code(v0.x), code(v0.z), code(v1.x), code(v1.z));
-                        p.y = pack4_i8(code(v0.y), code(v0.w), code(v1.y), code(v1.w));
+                        if (W8) {
+                            p.x = pack4_i8(code(v0.x), code(v0.y), code(v0.z), code(v0.w));
+                            p.y = pack4_i8(code(v1.x), code(v1.y), code(v1.z), code(v1.w));
+                        } else {
+                            p.x = pack4_i8(code(v0.x), code(v0.z), code(v1.x), code(v1.z));
+                            p.y = pack4_i8(code(v0.y), code(v0.w), code(v1.y), code(v1.w));
+                        }
                         *reinterpret_cast<uint2 *>(xs + m * K + 8 * g) = p;
                     }
                 }
@@ -142,8 +154,8 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
             for (int i = 0; i < NG; ++i) {
                 const int g = t + T * i;
                 if (g < G8) {
-                    uint2 p;
-                    natural_to_p8(xn[m][i].x, xn[m][i].y, p.x, p.y);
+                    uint2 p = xn[m][i];
+                    if (!W8) natural_to_p8(xn[m][i].x, xn[m][i].y, p.x, p.y);
                     *reinterpret_cast<uint2 *>(xs + m * K + 8 * g) = p;
                 }
             }
@@ -151,7 +163,8 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
     }
     lds_barrier();
 
-    // (4) int8 dot products of 16*code with the P8 activations.
+    // (4) int8 dot products of 16*code with the P8 activations (of the int8
+    // codes with the natural-order activations for 8-bit weights).
     int acc[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[m] = 0;
@@ -160,6 +173,19 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
         // Past the end of the row the weights are zero; clamp the LDS read.
         const int cx = min(j + 16 * u, C - 1);
         const uint4 w = wb[u];
+        if (W8) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const uint4 x0 = *reinterpret_cast<const uint4 *>(xs + m * K + cx * 16);
+                int s = acc[m];
+                s = __builtin_amdgcn_sdot4((int)w.x, (int)x0.x, s, false);
+                s = __builtin_amdgcn_sdot4((int)w.y, (int)x0.y, s, false);
+                s = __builtin_amdgcn_sdot4((int)w.z, (int)x0.z, s, false);
+                s = __builtin_amdgcn_sdot4((int)w.w, (int)x0.w, s, false);
+                acc[m] = s;
+            }
+            continue;
+        }
         const uint32_t l0 = lo16(w.x), h0 = hi16(w.x), l1 = lo16(w.y), h1 = hi16(w.y);
         const uint32_t l2 = lo16(w.z), h2 = hi16(w.z), l3 = lo16(w.w), h3 = hi16(w.w);
 #pragma unroll
@@ -179,9 +205,9 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
         }
     }
 
-    // (5) sum the 16 lanes of each channel; divide out the 16 of the codes.
+    // (5) sum the 16 lanes of each channel; divide out the 16 of the int4 codes.
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] = sum16(acc[m]) >> 4;
+    for (int m = 0; m < M; ++m) acc[m] = W8 ? sum16(acc[m]) : (sum16(acc[m]) >> 4);
     if (j == 0 && r < rows) {
 #pragma unroll
         for (int m = 0; m < M; ++m) {
@@ -197,41 +223,51 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
     }
 }
 
-template <int M, int ROWS, int UB>
+template <int M, int ROWS, int UB, bool W8>
 static void go_dot4(const W4A8Args &a, hipStream_t st) {
     dim3 grid((unsigned)((a.N + ROWS - 1) / ROWS));
     const uint32_t shm = (uint32_t)(M * a.K);
     if (a.out == Out::I32)
-        launch_main(k_gemv_dot4<M, ROWS, UB, false, Out::I32>, grid, dim3(16 * ROWS), shm, st, a);
+        launch_main(k_gemv_dot4<M, ROWS, UB, false, Out::I32, W8>, grid, dim3(16 * ROWS), shm, st,
+                    a);
     else if (a.X)
-        launch_main(k_gemv_dot4<M, ROWS, UB, true, Out::Y>, grid, dim3(16 * ROWS), shm, st, a);
+        launch_main(k_gemv_dot4<M, ROWS, UB, true, Out::Y, W8>, grid, dim3(16 * ROWS), shm, st, a);
     else
-        launch_main(k_gemv_dot4<M, ROWS, UB, false, Out::Y>, grid, dim3(16 * ROWS), shm, st, a);
+        launch_main(k_gemv_dot4<M, ROWS, UB, false, Out::Y, W8>, grid, dim3(16 * ROWS), shm, st,
+                    a);
 }
 
-// UB = chunks per lane, the smallest instantiated value >= ceil(K/32 / 16).
-template <int M>
+// UB = chunks per lane, the smallest instantiated value >= ceil(chunks / 16).
+template <int M, bool W8>
 static void go_dot4_m(const W4A8Args &a, hipStream_t st) {
-    const int64_t ub = (a.K / 32 + 15) / 16;
+    const int64_t ub = (a.K / (W8 ? 16 : 32) + 15) / 16;
     if (ub <= 2)
-        go_dot4<M, 16, 2>(a, st);
+        go_dot4<M, 16, 2, W8>(a, st);
     else if (ub <= 3)
-        go_dot4<M, 16, 3>(a, st);
+        go_dot4<M, 16, 3, W8>(a, st);
     else if (ub <= 4)
-        go_dot4<M, 16, 4>(a, st);
+        go_dot4<M, 16, 4, W8>(a, st);
     else if (ub <= 8)
-        go_dot4<M, 16, 8>(a, st);
+        go_dot4<M, 16, 8, W8>(a, st);
     else
-        go_dot4<M, 16, 16>(a, st);
+        go_dot4<M, 16, 16, W8>(a, st);
+}
+
+template <bool W8>
+static void go_dot4_w(const W4A8Args &a, hipStream_t st) {
+    switch (a.M) {
+        case 1: go_dot4_m<1, W8>(a, st); break;
+        case 2: go_dot4_m<2, W8>(a, st); break;
+        case 3: go_dot4_m<3, W8>(a, st); break;
+        default: go_dot4_m<4, W8>(a, st); break;
+    }
 }
 
 hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st) {
-    switch (a.M) {
-        case 1: go_dot4_m<1>(a, st); break;
-        case 2: go_dot4_m<2>(a, st); break;
-        case 3: go_dot4_m<3>(a, st); break;
-        default: go_dot4_m<4>(a, st); break;
-    }
+    if (a.w8)
+        go_dot4_w<true>(a, st);
+    else
+        go_dot4_w<false>(a, st);
     return hipGetLastError();
 }
 
@@ -247,12 +283,15 @@ hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st) {
 // feed two v_mfma_i32_16x16x64_i8 (the first 16 and the last 16 codes of each
 // lane).  The weight and activation operands use identical k slots per lane,
 // so the order in which the MFMA consumes the slots does not matter.
+// With W8 the lane loads the 32 int8 codes of the same k slots (two 16-byte
+// loads) and the activations come in natural order.
 // Accumulator layout (16x16 i32): lane l holds rows 4*(l/16)+i, column l%16.
 // Weights and activations of the next D steps are in flight in a register
 // ring while the current step multiplies.  Rows past M and channels past N
 // read zeros (their outputs are not stored).
-template <int MB, int NB, int D, int W, Out OUT>
+template <int MB, int NB, int D, int W, Out OUT, bool W8>
 __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args a) {
+    constexpr int WL = W8 ? 2 : 1;  // 16-byte weight loads per lane and step
     constexpr int kPairs = MB * NB;                 // 16x16 output blocks
     constexpr int kPerWave = (kPairs + W - 1) / W;  // epilogue blocks per wave
     __shared__ int red[kPairs * 4 * kWave];         // [pair][i][lane]
@@ -260,7 +299,7 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
     const int r16 = lane % 16, kq = lane / 16;
-    const int K = (int)a.K, KB = K / 2;
+    const int K = (int)a.K, KB = W8 ? K : K / 2;
     const int64_t N = a.N, M = a.M;
     const int S = K / 128;
     const int s0 = S * wave / W, s1 = S * (wave + 1) / W;
@@ -274,7 +313,7 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args a) {
     const auto ra = make_rsrc(a.Xq, M * K);
     int boff[NB], aoff[MB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) boff[nb] = (16 * nb + r16) * KB + kq * 16;
+    for (int nb = 0; nb < NB; ++nb) boff[nb] = (16 * nb + r16) * KB + kq * 16 * WL;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) aoff[mb] = (16 * mb + r16) * K + kq * 32;
 
@@ -284,11 +323,14 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args a) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = v4i{0, 0, 0, 0};
 
-    uint4 wr[D][NB], xr0[D][MB], xr1[D][MB];
+    uint4 wr[D][NB][WL], xr0[D][MB], xr1[D][MB];
     auto fetch = [&](int d, int ss) {
         const bool ok = ss < s1;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) wr[d][nb] = bload16(rb, ok ? boff[nb] + 64 * ss : kOOB);
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int h = 0; h < WL; ++h)
+                wr[d][nb][h] = bload16(rb, ok ? boff[nb] + 64 * WL * ss + 16 * h : kOOB);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int o = ok ? aoff[mb] + 128 * ss : kOOB;
@@ -329,9 +371,15 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args a) {
                 v4i b0[NB], b1[NB];
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    const uint4 w = wr[d][nb];
-                    b0[nb] = v4i{(int)lo16(w.x), (int)hi16(w.x), (int)lo16(w.y), (int)hi16(w.y)};
-                    b1[nb] = v4i{(int)lo16(w.z), (int)hi16(w.z), (int)lo16(w.w), (int)hi16(w.w)};
+                    if (W8) {
+                        const uint4 w0 = wr[d][nb][0], w1 = wr[d][nb][WL - 1];
+                        b0[nb] = v4i{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w};
+                        b1[nb] = v4i{(int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+                    } else {
+                        const uint4 w = wr[d][nb][0];
+                        b0[nb] = v4i{(int)lo16(w.x), (int)hi16(w.x), (int)lo16(w.y), (int)hi16(w.y)};
+                        b1[nb] = v4i{(int)lo16(w.z), (int)hi16(w.z), (int)lo16(w.w), (int)hi16(w.w)};
+                    }
                 }
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
@@ -370,7 +418,7 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args a) {
         for (int i = 0; i < 4; ++i) {
             const int64_t row = 16 * mb + 4 * kq + i;
             if (row >= M) continue;
-            const int v = red[(p * 4 + i) * kWave + lane] >> 4;
+            const int v = W8 ? red[(p * 4 + i) * kWave + lane] : (red[(p * 4 + i) * kWave + lane] >> 4);
             if (OUT == Out::I32) {
                 a.acc[row * N + col] = v;
             } else {
@@ -383,23 +431,31 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args a) {
     }
 }
 
-template <int MB, int NB, int D, int W>
+template <int MB, int NB, int D, int W, bool W8>
 static void go_mfma(const W4A8Args &a, hipStream_t st) {
     dim3 grid((unsigned)((a.N + 16 * NB - 1) / (16 * NB)));
     if (a.out == Out::I32)
-        launch_main(k_gemv_mfma<MB, NB, D, W, Out::I32>, grid, dim3(64 * W), 0, st, a);
+        launch_main(k_gemv_mfma<MB, NB, D, W, Out::I32, W8>, grid, dim3(64 * W), 0, st, a);
     else
-        launch_main(k_gemv_mfma<MB, NB, D, W, Out::Y>, grid, dim3(64 * W), 0, st, a);
+        launch_main(k_gemv_mfma<MB, NB, D, W, Out::Y, W8>, grid, dim3(64 * W), 0, st, a);
+}
+
+template <bool W8>
+static void go_mfma_w(const W4A8Args &a, hipStream_t st) {
+    const int mb = (int)((a.M + 15) / 16);
+    switch (mb) {
+        case 1: go_mfma<1, 4, 2, 8, W8>(a, st); break;
+        case 2: go_mfma<2, 4, 2, 8, W8>(a, st); break;
+        case 3: go_mfma<3, 4, 1, 8, W8>(a, st); break;
+        default: go_mfma<4, 4, 1, 8, W8>(a, st); break;
+    }
 }
 
 hipError_t launch_gemv_mfma(const W4A8Args &a, hipStream_t st) {
-    const int mb = (int)((a.M + 15) / 16);
-    switch (mb) {
-        case 1: go_mfma<1, 4, 2, 8>(a, st); break;
-        case 2: go_mfma<2, 4, 2, 8>(a, st); break;
-        case 3: go_mfma<3, 4, 1, 8>(a, st); break;
-        default: go_mfma<4, 4, 1, 8>(a, st); break;
-    }
+    if (a.w8)
+        go_mfma_w<true>(a, st);
+    else
+        go_mfma_w<false>(a, st);
     return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 // Shape-agnostic kernels: any M, K, N and alignment (for example the Keras
 // guide's toy model, K = 10 and K = 32).  One thread per output element.
+// W4A8 and W8A8 products: exact int32 sums, then the step-6 dequantization.
 #include "common.h"
 #include "kernels.h"
 
@@ -35,10 +36,38 @@ __global__ __launch_bounds__(256) void k_w4a8_generic(const int8_t *__restrict__
     }
 }
 
+// W8A8: the same with int8 codes, one per byte (row n holds K bytes).
+__global__ __launch_bounds__(256) void k_w8a8_generic(const int8_t *__restrict__ Xq,
+                                                      const float *__restrict__ sx,
+                                                      const int8_t *__restrict__ Wq,
+                                                      const float *__restrict__ sw,
+                                                      const float *__restrict__ bias,
+                                                      float *__restrict__ Y,
+                                                      int32_t *__restrict__ accout, int64_t M,
+                                                      int64_t K, int64_t N) {
+    const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= N) return;
+    const int8_t *row = Wq + n * K;
+    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+        const int8_t *x = Xq + m * K;
+        int acc = 0;
+        for (int64_t k = 0; k < K; ++k) acc += (int)x[k] * (int)row[k];
+        if (accout)
+            accout[m * N + n] = acc;
+        else
+            Y[m * N + n] = dequant(acc, sx[m], sw[n], bias, (int)n);
+    }
+}
+
 hipError_t launch_w4a8_generic(const W4A8Args &a, hipStream_t st) {
     dim3 g((unsigned)((a.N + 255) / 256), (unsigned)(a.M < 65535 ? a.M : 65535));
-    launch_main(k_w4a8_generic, g, dim3(256), 0, st, a.Xq, a.sx, a.packed, a.sw, a.bias, a.Y,
-                a.out == Out::I32 ? a.acc : nullptr, a.M, a.K, a.N);
+    if (a.w8)
+        launch_main(k_w8a8_generic, g, dim3(256), 0, st, a.Xq, a.sx,
+                    reinterpret_cast<const int8_t *>(a.packed), a.sw, a.bias, a.Y,
+                    a.out == Out::I32 ? a.acc : nullptr, a.M, a.K, a.N);
+    else
+        launch_main(k_w4a8_generic, g, dim3(256), 0, st, a.Xq, a.sx, a.packed, a.sw, a.bias, a.Y,
+                    a.out == Out::I32 ? a.acc : nullptr, a.M, a.K, a.N);
     return hipGetLastError();
 }
 

@@ -36,35 +36,40 @@ struct W4A8Args {
     const float *X;       // fp32 activations [M][K] (fused quantization) or NULL
     const int8_t *Xq;     // int8 activations, natural or P8 layout, or NULL
     const float *sx;      // [M] activation scales (with Xq)
-    const uint8_t *packed;
+    const uint8_t *packed;  // int4 codes [N][K/2], or int8 codes [N][K] when w8
     const float *sw;
     const float *bias;
     float *Y;
     int32_t *acc;
     int64_t M, K, N;
     Out out;
+    bool w8;  // 8-bit weight codes (W8A8): natural-layout activations, no unpacking
 };
 
 hipError_t launch_quant_weight_sym(const float *W, int64_t K, int64_t N, uint8_t *packed,
                                    float *sw, hipStream_t st);
+hipError_t launch_quant_weight_w8(const float *W, int64_t K, int64_t N, int8_t *Wq, float *sw,
+                                  hipStream_t st);
 hipError_t launch_quant_weight_asym(const float *W, int64_t K, int64_t N, int64_t group,
                                     uint8_t *packed, float *scales, float *zeros, hipStream_t st);
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx, bool p8,
                             hipStream_t st);
 hipError_t launch_to_p8(const int8_t *Xq, int64_t M, int64_t K, int8_t *out, hipStream_t st);
 
-// M <= 4, K % 32 == 0, K <= 8192, 16-byte aligned: VALU dot4 GEMV.  Uses a.X (fused
-// quantization prologue) when non-NULL, else a.Xq (natural layout) + a.sx.
-bool gemv_dot4_ok(int64_t M, int64_t K);
+// M <= 4, K % 32 == 0, K <= 8192 (4096 for 8-bit weights), 16-byte aligned: VALU
+// dot4 GEMV.  Uses a.X (fused quantization prologue) when non-NULL, else a.Xq
+// (natural layout) + a.sx.
+bool gemv_dot4_ok(int64_t M, int64_t K, bool w8);
 hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st);
 
-// M <= 64, K % 128 == 0: MFMA GEMV; a.Xq in P8 layout.
+// M <= 64, K % 128 == 0: MFMA GEMV; a.Xq in P8 layout (natural for 8-bit weights).
 hipError_t launch_gemv_mfma(const W4A8Args &a, hipStream_t st);
 
-// Any M, K % 128 == 0: LDS-tiled MFMA GEMM; a.Xq in P8 layout.
+// Any M, K % 128 == 0: LDS-tiled MFMA GEMM; a.Xq in P8 layout (natural for
+// 8-bit weights).
 hipError_t launch_gemm_mfma(const W4A8Args &a, hipStream_t st);
 
-// Any shape: one thread per output, natural-layout a.Xq.
+// Any shape: one thread per output, natural-layout a.Xq (int4 or int8 codes).
 hipError_t launch_w4a8_generic(const W4A8Args &a, hipStream_t st);
 
 // W4A16.

@@ -7,6 +7,10 @@
 // principle; "INT4" concept entry 4.1-4.2):
 //   scale = fl(fl(max - min) / 15), zero = 0 - rne(fl(min / scale)),
 //   code = clamp(rne(fl(W / scale)) + zero, 0, 15).
+// Symmetric int8 weights (the INT8 path that the Keras guide's "How it works"
+// says the INT4 path follows; "INT4" concept entry 4.1 with b = 8):
+//   scale[n] = fl(max_k |W[k][n]| / 127), code = clamp(rne(fl(W / scale)), -128, 127),
+//   stored one per byte, channel-major [N][K].
 // Activations (Keras guide step 3): sx[m] = fl(max_k |X[m][k]| / 127),
 //   Xq = clamp(rne(fl(X / sx)), -128, 127).
 #include "common.h"
@@ -45,8 +49,41 @@ __global__ __launch_bounds__(256) void k_absmax_cols(const float *__restrict__ W
 }
 
 // Pass 2: codes of a [128 x 64] tile.  Thread (c, part) owns column c and the
-// 16 bytes (32 k) part*16 .. part*16+15 of the tile; loads are coalesced over
-// the 64 columns of a wave.  `amax` still holds absmax bits here.
+// 32 k values part*32 .. part*32+31 of the tile (16 packed bytes, or 32 int8
+// codes); loads are coalesced over the 64 columns of a wave.  `amax` still
+// holds absmax bits here.
+__global__ __launch_bounds__(256) void k_quant_w8_tile(const float *__restrict__ W, int64_t K,
+                                                       int64_t N,
+                                                       const uint32_t *__restrict__ amax,
+                                                       int8_t *__restrict__ Wq) {
+    const int c = threadIdx.x % 64, part = threadIdx.x / 64;
+    const int64_t col = (int64_t)blockIdx.x * 64 + c;
+    if (col >= N) return;
+    const float a = __uint_as_float(amax[col]);
+    const float s = (a == 0.0f) ? 0.0f : a / 127.0f;
+    const int64_t kbeg = (int64_t)blockIdx.y * 128 + part * 32;
+    uint32_t words[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int64_t k = kbeg + 4 * j + b;
+            const int q = (k < K) ? quant_code(W[k * N + col], s, -128.0f, 127.0f) : 0;
+            v |= (uint32_t)(q & 0xFF) << (8 * b);
+        }
+        words[j] = v;
+    }
+    int8_t *dst = Wq + col * K + kbeg;
+    if ((K % 16) == 0 && kbeg + 32 <= K && (reinterpret_cast<uintptr_t>(Wq) & 15) == 0) {
+        reinterpret_cast<uint4 *>(dst)[0] = uint4{words[0], words[1], words[2], words[3]};
+        reinterpret_cast<uint4 *>(dst)[1] = uint4{words[4], words[5], words[6], words[7]};
+    } else {
+        for (int j = 0; j < 32; ++j)
+            if (kbeg + j < K) dst[j] = (int8_t)(words[j / 4] >> (8 * (j % 4)));
+    }
+}
+
 __global__ __launch_bounds__(256) void k_quant_sym_tile(const float *__restrict__ W, int64_t K,
                                                         int64_t N,
                                                         const uint32_t *__restrict__ amax,
@@ -82,27 +119,45 @@ __global__ __launch_bounds__(256) void k_quant_sym_tile(const float *__restrict_
     }
 }
 
-// Pass 3: absmax bits -> scale, in place.
-__global__ void k_finalize_sym_scales(uint32_t *__restrict__ amax_to_scale, int64_t N) {
+// Pass 3: absmax bits -> scale (absmax / qmax, qmax = 7 or 127), in place.
+__global__ void k_finalize_sym_scales(uint32_t *__restrict__ amax_to_scale, int64_t N,
+                                      float qmax) {
     int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (n >= N) return;
     float a = __uint_as_float(amax_to_scale[n]);
-    float s = (a == 0.0f) ? 0.0f : a / 7.0f;
+    float s = (a == 0.0f) ? 0.0f : a / qmax;
     reinterpret_cast<float *>(amax_to_scale)[n] = s;
 }
 
-hipError_t launch_quant_weight_sym(const float *W, int64_t K, int64_t N, uint8_t *packed,
-                                   float *sw, hipStream_t st) {
-    uint32_t *amax = reinterpret_cast<uint32_t *>(sw);
+// Passes 0-1 (shared by the int4 and int8 forms): clear and fill the absmax
+// bits in the scale array.
+static void absmax_pass(const float *W, int64_t K, int64_t N, uint32_t *amax, hipStream_t st) {
     hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, amax, N,
                        0u);
     const int64_t krows = 256;
     dim3 g1((unsigned)((N + 63) / 64), (unsigned)((K + krows - 1) / krows));
     hipLaunchKernelGGL(k_absmax_cols, g1, dim3(256), 0, st, W, K, N, krows, amax);
+}
+
+hipError_t launch_quant_weight_sym(const float *W, int64_t K, int64_t N, uint8_t *packed,
+                                   float *sw, hipStream_t st) {
+    uint32_t *amax = reinterpret_cast<uint32_t *>(sw);
+    absmax_pass(W, K, N, amax, st);
     dim3 g2((unsigned)((N + 63) / 64), (unsigned)((K + 127) / 128));
     hipLaunchKernelGGL(k_quant_sym_tile, g2, dim3(256), 0, st, W, K, N, amax, packed);
     hipLaunchKernelGGL(k_finalize_sym_scales, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st,
-                       amax, N);
+                       amax, N, 7.0f);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_weight_w8(const float *W, int64_t K, int64_t N, int8_t *Wq, float *sw,
+                                  hipStream_t st) {
+    uint32_t *amax = reinterpret_cast<uint32_t *>(sw);
+    absmax_pass(W, K, N, amax, st);
+    dim3 g2((unsigned)((N + 63) / 64), (unsigned)((K + 127) / 128));
+    hipLaunchKernelGGL(k_quant_w8_tile, g2, dim3(256), 0, st, W, K, N, amax, Wq);
+    hipLaunchKernelGGL(k_finalize_sym_scales, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st,
+                       amax, N, 127.0f);
     return hipGetLastError();
 }
 

@@ -40,7 +40,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["w4_quantize_weight", "a8_quantize_act", "w4a8_linear", "w4a16_linear",
                  "w4a8_linear_q", "w4a8_matmul_i32", "w4a8_workspace_bytes",
-                 "w4_status_string", "w4_last_path"]:
+                 "w8_quantize_weight", "w8a8_workspace_bytes", "w8a8_linear",
+                 "w8a8_matmul_i32", "w4_status_string", "w4_last_path"]:
         assert want in names, names
 
 
@@ -104,6 +105,29 @@ def test_linear_checks(w4):
     assert g(FAKE, FAKE, FAKE, FAKE, None, 2, 64, -8, FAKE, FAKE, ws, None) == W4_ERR_SHAPE
     h = w4.lib().w4a8_matmul_i32
     assert h(FAKE, FAKE, 2, 64, 8, None, FAKE, ws, None) == W4_ERR_NULL
+    assert h(FAKE, FAKE, 2, 64, 8, FAKE + 2, FAKE, ws, None) == W4_ERR_ALIGN
+    assert h(FAKE, FAKE, 2, 64, 8, FAKE, FAKE, 3, None) == W4_ERR_WORKSPACE
+
+
+def test_w8a8_checks(w4):
+    q = w4.lib().w8_quantize_weight
+    assert q(None, 4, 4, FAKE, FAKE, None) == W4_ERR_NULL
+    assert q(FAKE, 4, 4, None, FAKE, None) == W4_ERR_NULL
+    assert q(FAKE, 0, 4, FAKE, FAKE, None) == W4_ERR_SHAPE
+    assert q(FAKE, w4.W4_MAX_K + 1, 4, FAKE, FAKE, None) == W4_ERR_SHAPE
+    assert q(FAKE, 4, 4, FAKE, FAKE + 2, None) == W4_ERR_ALIGN
+    ws = w4.lib().w8a8_workspace_bytes(2, 64, 8)
+    assert ws == w4.w4a8_workspace_bytes(2, 64, 8)
+    assert w4.lib().w8a8_workspace_bytes(1, 0, 8) == 0
+    f = w4.lib().w8a8_linear
+    assert f(None, 2, 64, 8, FAKE, FAKE, None, FAKE, FAKE, ws, None) == W4_ERR_NULL
+    assert f(FAKE, 2, 64, 8, None, FAKE, None, FAKE, FAKE, ws, None) == W4_ERR_NULL
+    assert f(FAKE, 2, 64, 0, FAKE, FAKE, None, FAKE, FAKE, ws, None) == W4_ERR_SHAPE
+    assert f(FAKE, 2, 64, 8, FAKE, FAKE, None, FAKE + 2, FAKE, ws, None) == W4_ERR_ALIGN
+    assert f(FAKE, 2, 64, 8, FAKE, FAKE, None, FAKE, None, 0, None) == W4_ERR_WORKSPACE
+    assert f(FAKE, 2, 64, 8, FAKE, FAKE, None, FAKE, FAKE + 16, ws, None) == W4_ERR_ALIGN
+    h = w4.lib().w8a8_matmul_i32
+    assert h(FAKE, None, 2, 64, 8, FAKE, FAKE, ws, None) == W4_ERR_NULL
     assert h(FAKE, FAKE, 2, 64, 8, FAKE + 2, FAKE, ws, None) == W4_ERR_ALIGN
     assert h(FAKE, FAKE, 2, 64, 8, FAKE, FAKE, 3, None) == W4_ERR_WORKSPACE
 
