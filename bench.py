@@ -17,8 +17,9 @@ Also reported in the same line:
                 launch / average kernel duration from HIP events attached to
                 the kernel's dispatch) against the 8 TB/s HBM peak;
   parts         the other workloads (Gemma M=8, 7B-class M=1/16/64, the
-                4096^3 prefill in int8 TOPS, the 70B-class W4A16 layer) and
-                the weight quantizers, each with per-kernel durations;
+                4096^3 prefill in int8 TOPS, the same layers with int8
+                weights (W8A8), the 70B-class W4A16 layer) and the weight
+                quantizers, each with per-kernel durations;
   cpu_baseline  the CPU oracle on a bounded sample of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-parts]
@@ -88,22 +89,33 @@ def w4a8_bytes(M, K, N):
     return N * ((K + 1) // 2) + 4 * N + 4 * M * K + 4 * M * N
 
 
+def w8a8_bytes(M, K, N):
+    """Algorithmic bytes of one W8A8 forward: int8 weights, fp32 channel
+    scales, fp32 activations in, fp32 outputs out."""
+    return N * K + 4 * N + 4 * M * K + 4 * M * N
+
+
 def w4a16_bytes(M, K, N, g):
     """Packed int4 weights, fp32 scale + zero point per group, bf16 x, fp32 y."""
     return N * ((K + 1) // 2) + 8 * N * (K // g) + 2 * M * K + 4 * M * N
 
 
 class W4A8Case:
-    def __init__(self, w4, torch, name, shape_name, M, rotate=True, copies=None):
+    """One W4A8 layer (or, with w8=True, the same layer as W8A8)."""
+
+    def __init__(self, w4, torch, name, shape_name, M, rotate=True, copies=None, w8=False):
         import workloads
         d = workloads.generate(shape_name, M=M)
         self.name, self.M, self.K, self.N = name, M if M else d["M"], d["K"], d["N"]
-        self.torch, self.w4 = torch, w4
+        self.torch, self.w4, self.w8 = torch, w4, w8
         dev = torch.device("cuda")
         self.x = torch.from_numpy(d["x"]).to(dev)
         W = torch.from_numpy(d["W"]).to(dev)
         t0 = time.perf_counter()
-        p, s, _ = w4.w4_quantize_weight(W, "sym")
+        if w8:
+            p, s = w4.w8_quantize_weight(W)
+        else:
+            p, s, _ = w4.w4_quantize_weight(W, "sym")
         torch.cuda.synchronize()
         self.quant_s = time.perf_counter() - t0
         del W
@@ -116,13 +128,14 @@ class W4A8Case:
         self.y = torch.empty((self.M, self.N), dtype=torch.float32, device=dev)
         self.ws = torch.empty(max(1, w4.w4a8_workspace_bytes(self.M, self.K, self.N)),
                               dtype=torch.uint8, device=dev)
-        self.bytes = w4a8_bytes(self.M, self.K, self.N)
+        self.bytes = (w8a8_bytes if w8 else w4a8_bytes)(self.M, self.K, self.N)
         self.ops = 2 * self.M * self.N * self.K
         self.host_x, self.host_W = d["x"], d["W"]
 
     def step(self, i):
         c = i % self.copies
-        self.w4.w4a8_linear(self.x, self.P[c], self.S[c], Y=self.y, workspace=self.ws)
+        f = self.w4.w8a8_linear if self.w8 else self.w4.w4a8_linear
+        f(self.x, self.P[c], self.S[c], Y=self.y, workspace=self.ws)
 
 
 class W4A16Case:
@@ -246,8 +259,9 @@ def main():
     ap.add_argument("--no-parts", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None,
                     help="run one workload's product kernel (for profilers): gemma_m1, gemma_m8, "
-                         "mlp7b_m1, mlp7b_m16, mlp7b_m64, prefill, w4a16; or copy (a 64 MiB "
-                         "device copy, for counter calibration)")
+                         "mlp7b_m1, mlp7b_m16, mlp7b_m64, prefill, w4a16, w8a8_gemma_m1, "
+                         "w8a8_mlp7b_m1, w8a8_prefill; or copy (a 64 MiB device copy, for "
+                         "counter calibration)")
     ap.add_argument("--launches", type=int, default=200)
     ap.add_argument("--copies", type=int, default=0,
                     help="with --only: number of rotating weight copies (0 = enough to exceed "
@@ -278,8 +292,10 @@ def main():
         specs = {"gemma_m1": ("gemma", 1), "gemma_m8": ("gemma", 8), "mlp7b_m1": ("mlp7b", 1),
                  "mlp7b_m16": ("mlp7b", 16), "mlp7b_m64": ("mlp7b", 64),
                  "prefill": ("prefill", None)}
+        w8 = args.only.startswith("w8a8_")
+        key = args.only[5:] if w8 else args.only
         case = (W4A16Case(w4, torch, copies=args.copies) if args.only == "w4a16"
-                else W4A8Case(w4, torch, args.only, *specs[args.only], copies=args.copies))
+                else W4A8Case(w4, torch, args.only, *specs[key], copies=args.copies, w8=w8))
         for i in range(args.warmup + args.steps):
             case.step(i)
         torch.cuda.synchronize()
@@ -315,9 +331,9 @@ def main():
 
     parts = []
     if not args.no_parts:
-        def w4a8_part(name, shape, M, bound, rotate=True):
+        def w4a8_part(name, shape, M, bound, rotate=True, w8=False):
             log(f"part: {name}")
-            c = W4A8Case(w4, torch, name, shape, M, rotate=rotate)
+            c = W4A8Case(w4, torch, name, shape, M, rotate=rotate, w8=w8)
             st = graph_step_time(torch, c, min(args.steps, 200), 10)
             p = w4.w4_last_path()
             ka, km = kernel_time(torch, hip, w4, c, min(args.launches, 100))
@@ -344,6 +360,10 @@ def main():
         w4a8_part("mlp7b_m16", "mlp7b", 16, "hbm")
         w4a8_part("mlp7b_m64", "mlp7b", 64, "hbm")
         w4a8_part("prefill_4096", "prefill", None, "mfma", rotate=False)
+        w4a8_part("w8a8_gemma_m1", "gemma", 1, "hbm", w8=True)
+        w4a8_part("w8a8_mlp7b_m1", "mlp7b", 1, "hbm", w8=True)
+        w4a8_part("w8a8_mlp7b_m16", "mlp7b", 16, "hbm", w8=True)
+        w4a8_part("w8a8_prefill_4096", "prefill", None, "mfma", rotate=False, w8=True)
         log("part: w4a16_70b_m16")
         c = W4A16Case(w4, torch)
         st = graph_step_time(torch, c, 50, 5)
