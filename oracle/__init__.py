@@ -11,6 +11,7 @@ arrays.  The formulas and their sources are documented there:
 * symmetric per-output-channel int4 weights (scale = absmax / 7, codes in
   [-8, 7], two per byte) -- Keras INT4 guide, "How it works", steps 1-2;
 * per-row dynamic int8 activations (scale = absmax / 127) -- same, step 3;
+* the toy model's ReLU on a Dense output (after the bias);
 * exact int8 x int4 products summed in int32 -- steps 4-5;
 * dequantization by input_scale * per_channel_kernel_scale -- step 6;
 * symmetric per-output-channel int8 weights (scale = absmax / 127, codes in
@@ -61,6 +62,7 @@ def _load():
             "orc_quantize_weight_w8": [_P, _I, _I, _P, _P],
             "orc_matmul_w8_i32": [_P, _P, _I, _I, _I, _P],
             "orc_w8a8_linear": [_P, _I, _I, _I, _P, _P, _P, _P],
+            "orc_relu": [_P, _I],
             "orc_w4a16_dequant": [_P, _P, _P, _I, _I, _I, _P],
             "orc_w4a16_linear": [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P],
         }
@@ -166,6 +168,13 @@ def w4a8_linear(X: np.ndarray, packed: np.ndarray, sw: np.ndarray, bias=None) ->
     _check(_load().orc_w4a8_linear(_ptr(X), M, K, N, _ptr(packed), _ptr(sw), _ptr(b), _ptr(Y)),
            "w4a8_linear")
     return Y
+
+
+def relu(Y: np.ndarray) -> np.ndarray:
+    """The Dense layer's ReLU on an fp32 output (a copy): y > 0 ? y : +0."""
+    out = np.array(Y, dtype=np.float32, copy=True, order="C")
+    _check(_load().orc_relu(_ptr(out), out.size), "relu")
+    return out
 
 
 def quantize_weight_w8(W: np.ndarray):

@@ -171,6 +171,19 @@ int orc_w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N,
     return rc;
 }
 
+/* [KERAS] toy model (section "Quantize a minimal functional model"): the first
+ * Dense layer carries activation="relu", applied to the layer output after the
+ * bias: y = y if y > 0 else +0 (so -0 becomes +0). */
+int orc_relu(float *Y, int64_t n) {
+    if (n < 0) return ORC_ERR_SHAPE;
+    for (int64_t i = 0; i < n; ++i) {
+        float y = Y[i];
+        if (!isfinite(y)) return ORC_ERR_NONFINITE;
+        Y[i] = (y > 0.0f) ? y : 0.0f;
+    }
+    return ORC_OK;
+}
+
 /* W8A8, the INT8 path that [KERAS] "How it works" says the INT4 path follows
  * apart from the unpacking: steps 1-6 with 8-bit weight codes.  [ENCY] 4.1
  * with b = 8: symmetric scale = max|x| / (2^(b-1) - 1) = / 127 per output

@@ -61,6 +61,9 @@ int orc_w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N,
                     const uint8_t *packed, const float *sw, const float *bias,
                     float *Y);
 
+/* ReLU on a layer output, in place: y > 0 ? y : +0. */
+int orc_relu(float *Y, int64_t n);
+
 /* Symmetric per-output-channel int8 weight quantization (scale = absmax/127,
  * codes in [-128, 127]).  Outputs Wq [N][K] int8 (channel-major), sw [N]. */
 int orc_quantize_weight_w8(const float *W, int64_t K, int64_t N, int8_t *Wq, float *sw);

@@ -427,3 +427,29 @@ def test_storage_formulas():
     per_weight_bits = (N * K // 2 + 2 * 4 * N * K // g) * 8 / (N * K)
     assert per_weight_bits == 4.5
     assert N * K // 2 + 2 * 4 * N * K // g + 2 * M * K + 4 * M * N == 2**27
+
+
+# ------------------------------------------------------------------- ReLU
+def test_relu_special_values(orc):
+    """IEEE facts: positive values pass unchanged (bit for bit), negative values,
+    -0.0 and +0.0 give +0.0; non-finite outputs are rejected."""
+    y = np.array([[1.5, -2.0, -0.0, 0.0, 3.4e38, -1e-45, 1e-45]], np.float32)
+    r = orc.relu(y)
+    assert r.view(np.uint32).tolist() == np.array(
+        [[1.5, 0.0, 0.0, 0.0, 3.4e38, 0.0, 1e-45]], np.float32).view(np.uint32).tolist()
+    assert y[0, 1] == -2.0  # the input is not modified
+    with pytest.raises(orc.OracleError):
+        orc.relu(np.array([np.nan], np.float32))
+
+
+def test_relu_on_layer_outputs(orc):
+    """Invariants on a real layer output: r >= +0 everywhere (no -0), r == y
+    where y > 0, and the positive part plus the negative part gives y back."""
+    d = workloads.random_case(77, 9, 301, 40, outliers=3, bias=True)
+    packed, sw = orc.quantize_weight_sym(d["W"])
+    y = orc.w4a8_linear(d["x"], packed, sw, d["bias"])
+    r = orc.relu(y)
+    assert np.all(r.view(np.uint32) >> 31 == 0)
+    assert np.array_equal(r[y > 0], y[y > 0]) and np.all(r[y <= 0] == 0)
+    assert np.array_equal(r + np.minimum(y, 0), y)
+    assert 0 < (y > 0).mean() < 1
