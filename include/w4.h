@@ -51,8 +51,16 @@ typedef enum {
     W4_ERR_ALIGN = -3,     /* a pointer is not aligned to its element size        */
     W4_ERR_SCHEME = -4,    /* unknown quantization scheme                         */
     W4_ERR_WORKSPACE = -5, /* workspace missing or smaller than required          */
-    W4_ERR_HIP = -6        /* the HIP runtime reported an error                   */
+    W4_ERR_HIP = -6,       /* the HIP runtime reported an error                   */
+    W4_ERR_ARG = -7        /* an enumerated argument has an unknown value         */
 } w4_status;
+
+/* Activation applied to a layer's output after dequantization and bias (the
+ * Keras guide's toy model: Dense(32, activation="relu")). */
+typedef enum {
+    W4_ACT_NONE = 0,
+    W4_ACT_RELU = 1 /* y > 0 ? y : +0 */
+} w4_activation;
 
 typedef enum {
     W4_SYM_PER_CHANNEL = 0, /* signed codes [-8,7], scale = absmax/7 per channel  */
@@ -116,6 +124,18 @@ int w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N,
                 const uint8_t *packed, const float *sw, const float *bias,
                 float *Y, void *workspace, size_t workspace_bytes, void *stream);
 
+/* w4a8_linear followed by an activation, fused into the product kernel's
+ * epilogue: Y = act(fl(fl(float(acc) * fl(sx[m] * sw[n])) [+ bias[n]])).
+ * For M <= 4 (K % 32 == 0, K <= 8192, 16-byte aligned X and packed) the whole
+ * decode step -- activation quantization, unpacking, product,
+ * dequantization, bias and activation -- is one kernel launch.
+ *   activation  W4_ACT_NONE or W4_ACT_RELU; any other value: W4_ERR_ARG.
+ * Other arguments and return codes as w4a8_linear. */
+int w4a8_linear_act(const float *X, int64_t M, int64_t K, int64_t N,
+                    const uint8_t *packed, const float *sw, const float *bias,
+                    int activation, float *Y, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
 /* The W4A8 forward from already-quantized activations (Keras guide steps 4-6):
  *   Xq [M][K] int8 and sx [M] fp32 (any values); the rest as w4a8_linear. */
 int w4a8_linear_q(const int8_t *Xq, const float *sx, const uint8_t *packed,
@@ -154,6 +174,12 @@ size_t w8a8_workspace_bytes(int64_t M, int64_t K, int64_t N);
 int w8a8_linear(const float *X, int64_t M, int64_t K, int64_t N, const int8_t *Wq,
                 const float *sw, const float *bias, float *Y, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/* w8a8_linear followed by an activation fused into the epilogue (as
+ * w4a8_linear_act; the single-launch decode path covers K <= 4096). */
+int w8a8_linear_act(const float *X, int64_t M, int64_t K, int64_t N, const int8_t *Wq,
+                    const float *sw, const float *bias, int activation, float *Y,
+                    void *workspace, size_t workspace_bytes, void *stream);
 
 /* The exact W8A8 integer product alone, for checking:
  *   acc [M][N] int32 = sum_k Xq[m][k] * Wq[n][k]. */

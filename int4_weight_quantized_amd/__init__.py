@@ -9,10 +9,12 @@ functions carry the C names:
   asymmetric group-wise int4 (``scheme="asym"``) weights, packed two per byte;
 * ``a8_quantize_act``     -- per-row dynamic int8 activations;
 * ``w4a8_linear``         -- the W4A8 forward from fp32 activations;
+* ``w4a8_linear_act``     -- the same with a fused activation (ReLU);
 * ``w4a8_linear_q``       -- the W4A8 forward from int8 activations;
 * ``w4a8_matmul_i32``     -- the exact int32 accumulators alone;
 * ``w8_quantize_weight``  -- symmetric per-channel int8 weights (W8A8);
 * ``w8a8_linear``         -- the W8A8 forward from fp32 activations;
+* ``w8a8_linear_act``     -- the same with a fused activation (ReLU);
 * ``w8a8_matmul_i32``     -- its exact int32 accumulators alone;
 * ``w4a16_linear``        -- the weight-only forward with bf16 activations.
 
@@ -33,6 +35,9 @@ W4_OK = 0
 W4_SYM_PER_CHANNEL = 0
 W4_ASYM_GROUP = 1
 W4_MAX_K = 131071
+W4_ACT_NONE = 0
+W4_ACT_RELU = 1
+_ACTS = {None: W4_ACT_NONE, "none": W4_ACT_NONE, "relu": W4_ACT_RELU}
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int64
@@ -60,6 +65,10 @@ def lib():
             "a8_quantize_act": ([_P, _I, _I, _P, _P, _P], ctypes.c_int),
             "w4a8_workspace_bytes": ([_I, _I, _I], _Z),
             "w4a8_linear": ([_P, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P], ctypes.c_int),
+            "w4a8_linear_act": ([_P, _I, _I, _I, _P, _P, _P, ctypes.c_int, _P, _P, _Z, _P],
+                                ctypes.c_int),
+            "w8a8_linear_act": ([_P, _I, _I, _I, _P, _P, _P, ctypes.c_int, _P, _P, _Z, _P],
+                                ctypes.c_int),
             "w4a8_linear_q": ([_P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _Z, _P], ctypes.c_int),
             "w4a8_matmul_i32": ([_P, _P, _I, _I, _I, _P, _P, _Z, _P], ctypes.c_int),
             "w4a16_linear": ([_P, _I, _I, _I, _P, _P, _P, _I, _P, _P], ctypes.c_int),
@@ -191,6 +200,30 @@ def w4a8_linear(X: torch.Tensor, packed: torch.Tensor, sw: torch.Tensor, bias=No
     return Y
 
 
+def _act(activation) -> int:
+    if activation not in _ACTS:
+        raise ValueError(f"unknown activation {activation!r} (None or 'relu')")
+    return _ACTS[activation]
+
+
+def w4a8_linear_act(X: torch.Tensor, packed: torch.Tensor, sw: torch.Tensor, bias=None,
+                    activation="relu", Y=None, workspace=None, stream=None) -> torch.Tensor:
+    """Y [M, N] fp32 = act(dequant(quant(X) . unpack(packed)) (+ bias)), one fused epilogue."""
+    M, K = X.shape
+    N = packed.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    workspace, need = _workspace(M, K, N, X.device, workspace)
+    rc = lib().w4a8_linear_act(_dev(X, "X", torch.float32), M, K, N,
+                               _dev(packed, "packed", torch.uint8), _dev(sw, "sw", torch.float32),
+                               _opt(bias, "bias", torch.float32), _act(activation),
+                               _dev(Y, "Y", torch.float32),
+                               _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                               _stream(stream))
+    _check("w4a8_linear_act", rc)
+    return Y
+
+
 def w4a8_linear_q(Xq: torch.Tensor, sx: torch.Tensor, packed: torch.Tensor, sw: torch.Tensor,
                   bias=None, Y=None, workspace=None, stream=None) -> torch.Tensor:
     M, K = Xq.shape
@@ -250,6 +283,23 @@ def w8a8_linear(X: torch.Tensor, Wq: torch.Tensor, sw: torch.Tensor, bias=None, 
                            _dev(workspace, "workspace", torch.uint8), workspace.numel(),
                            _stream(stream))
     _check("w8a8_linear", rc)
+    return Y
+
+
+def w8a8_linear_act(X: torch.Tensor, Wq: torch.Tensor, sw: torch.Tensor, bias=None,
+                    activation="relu", Y=None, workspace=None, stream=None) -> torch.Tensor:
+    """Y [M, N] fp32 = act(dequant(quant(X) . Wq^T) (+ bias)), one fused epilogue."""
+    M, K = X.shape
+    N = Wq.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    workspace, need = _workspace(M, K, N, X.device, workspace)
+    rc = lib().w8a8_linear_act(_dev(X, "X", torch.float32), M, K, N, _dev(Wq, "Wq", torch.int8),
+                               _dev(sw, "sw", torch.float32), _opt(bias, "bias", torch.float32),
+                               _act(activation), _dev(Y, "Y", torch.float32),
+                               _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                               _stream(stream))
+    _check("w8a8_linear_act", rc)
     return Y
 
 

@@ -39,10 +39,11 @@ enum class Src { FP32, Q };
 int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const float *sx,
                   const uint8_t *packed, const float *sw, const float *bias, int64_t M,
                   int64_t K, int64_t N, float *Y, int32_t *acc, void *workspace,
-                  size_t workspace_bytes, hipStream_t st) {
+                  size_t workspace_bytes, hipStream_t st, bool relu = false) {
     using namespace w4;
     W4A8Args a{};
     a.w8 = w8;
+    a.relu = relu;
     a.X = nullptr;
     a.Xq = Xq;
     a.sx = sx;
@@ -133,6 +134,7 @@ const char *w4_status_string(int status) {
         case W4_ERR_SCHEME: return "unknown quantization scheme";
         case W4_ERR_WORKSPACE: return "workspace missing or too small";
         case W4_ERR_HIP: return "HIP runtime error";
+        case W4_ERR_ARG: return "unknown value of an enumerated argument";
         default: return "unknown status";
     }
 }
@@ -176,18 +178,26 @@ size_t w4a8_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     return ws_bytes(M, K);
 }
 
-int w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N, const uint8_t *packed,
-                const float *sw, const float *bias, float *Y, void *workspace,
-                size_t workspace_bytes, void *stream) {
+int w4a8_linear_act(const float *X, int64_t M, int64_t K, int64_t N, const uint8_t *packed,
+                    const float *sw, const float *bias, int activation, float *Y,
+                    void *workspace, size_t workspace_bytes, void *stream) {
     if (!X || !packed || !sw || !Y) return W4_ERR_NULL;
     if (!shape_ok(M, K, N)) return W4_ERR_SHAPE;
+    if (activation != W4_ACT_NONE && activation != W4_ACT_RELU) return W4_ERR_ARG;
     if (!aligned(X, 4) || !aligned(sw, 4) || !aligned(Y, 4) || (bias && !aligned(bias, 4)))
         return W4_ERR_ALIGN;
     int rc = check_workspace(M, K, workspace, workspace_bytes);
     if (rc != W4_OK) return rc;
     return w4a8_dispatch(Src::FP32, false, X, nullptr, nullptr, packed, sw, bias, M, K, N, Y,
                          nullptr, workspace, workspace_bytes,
-                         reinterpret_cast<hipStream_t>(stream));
+                         reinterpret_cast<hipStream_t>(stream), activation == W4_ACT_RELU);
+}
+
+int w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N, const uint8_t *packed,
+                const float *sw, const float *bias, float *Y, void *workspace,
+                size_t workspace_bytes, void *stream) {
+    return w4a8_linear_act(X, M, K, N, packed, sw, bias, W4_ACT_NONE, Y, workspace,
+                           workspace_bytes, stream);
 }
 
 int w4a8_linear_q(const int8_t *Xq, const float *sx, const uint8_t *packed, const float *sw,
@@ -230,18 +240,27 @@ size_t w8a8_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     return ws_bytes(M, K);
 }
 
-int w8a8_linear(const float *X, int64_t M, int64_t K, int64_t N, const int8_t *Wq,
-                const float *sw, const float *bias, float *Y, void *workspace,
-                size_t workspace_bytes, void *stream) {
+int w8a8_linear_act(const float *X, int64_t M, int64_t K, int64_t N, const int8_t *Wq,
+                    const float *sw, const float *bias, int activation, float *Y,
+                    void *workspace, size_t workspace_bytes, void *stream) {
     if (!X || !Wq || !sw || !Y) return W4_ERR_NULL;
     if (!shape_ok(M, K, N)) return W4_ERR_SHAPE;
+    if (activation != W4_ACT_NONE && activation != W4_ACT_RELU) return W4_ERR_ARG;
     if (!aligned(X, 4) || !aligned(sw, 4) || !aligned(Y, 4) || (bias && !aligned(bias, 4)))
         return W4_ERR_ALIGN;
     int rc = check_workspace(M, K, workspace, workspace_bytes);
     if (rc != W4_OK) return rc;
     return w4a8_dispatch(Src::FP32, true, X, nullptr, nullptr,
                          reinterpret_cast<const uint8_t *>(Wq), sw, bias, M, K, N, Y, nullptr,
-                         workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+                         workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream),
+                         activation == W4_ACT_RELU);
+}
+
+int w8a8_linear(const float *X, int64_t M, int64_t K, int64_t N, const int8_t *Wq,
+                const float *sw, const float *bias, float *Y, void *workspace,
+                size_t workspace_bytes, void *stream) {
+    return w8a8_linear_act(X, M, K, N, Wq, sw, bias, W4_ACT_NONE, Y, workspace, workspace_bytes,
+                           stream);
 }
 
 int w8a8_matmul_i32(const int8_t *Xq, const int8_t *Wq, int64_t M, int64_t K, int64_t N,

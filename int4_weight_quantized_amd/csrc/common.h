@@ -235,6 +235,12 @@ __device__ __forceinline__ float dequant(int acc, float sx, float sw, const floa
     return y;
 }
 
+// The Dense layer's ReLU after the bias (Keras guide, toy model): y > 0 ? y : +0
+// (a select, not a max, so -0 becomes +0).
+__device__ __forceinline__ float relu_if(float y, bool relu) {
+    return (relu && !(y > 0.0f)) ? 0.0f : y;
+}
+
 // Map a linear block index to a tile index so that the blocks the hardware
 // places on one XCD (consecutive ids go round-robin over the 8 XCDs) get a
 // contiguous range of tiles and share that XCD's L2.

@@ -242,6 +242,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
                     const float sc = sxr * swc[nb];
                     float y = (float)v * sc;
                     if (a.bias) y = y + bc[nb];
+                    y = relu_if(y, a.relu);
                     bits = __float_as_uint(y);
                 }
                 stg[lr * kPitch + nb * 16 + r16] = bits;

@@ -217,6 +217,7 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
                 const float s = sxm[m] * swn;
                 float y = (float)acc[m] * s;
                 if (a.bias) y = y + bn;
+                y = relu_if(y, a.relu);
                 a.Y[(int64_t)m * a.N + n] = y;
             }
         }
@@ -425,6 +426,7 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args a) {
                 const float sc = sxr[j][i] * swc[j];
                 float y = (float)v * sc;
                 if (a.bias) y = y + bc[j];
+                y = relu_if(y, a.relu);
                 a.Y[row * N + col] = y;
             }
         }

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void k_w4a8_generic(const int8_t *__restrict__
                                                       const float *__restrict__ bias,
                                                       float *__restrict__ Y,
                                                       int32_t *__restrict__ accout, int64_t M,
-                                                      int64_t K, int64_t N) {
+                                                      int64_t K, int64_t N, bool relu) {
     const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (n >= N) return;
     const uint8_t *row = packed + n * ((K + 1) / 2);
@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void k_w4a8_generic(const int8_t *__restrict__
         if (accout)
             accout[m * N + n] = acc;
         else
-            Y[m * N + n] = dequant(acc, sx[m], sw[n], bias, (int)n);
+            Y[m * N + n] = relu_if(dequant(acc, sx[m], sw[n], bias, (int)n), relu);
     }
 }
 
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void k_w8a8_generic(const int8_t *__restrict__
                                                       const float *__restrict__ bias,
                                                       float *__restrict__ Y,
                                                       int32_t *__restrict__ accout, int64_t M,
-                                                      int64_t K, int64_t N) {
+                                                      int64_t K, int64_t N, bool relu) {
     const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (n >= N) return;
     const int8_t *row = Wq + n * K;
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void k_w8a8_generic(const int8_t *__restrict__
         if (accout)
             accout[m * N + n] = acc;
         else
-            Y[m * N + n] = dequant(acc, sx[m], sw[n], bias, (int)n);
+            Y[m * N + n] = relu_if(dequant(acc, sx[m], sw[n], bias, (int)n), relu);
     }
 }
 
@@ -64,10 +64,10 @@ hipError_t launch_w4a8_generic(const W4A8Args &a, hipStream_t st) {
     if (a.w8)
         launch_main(k_w8a8_generic, g, dim3(256), 0, st, a.Xq, a.sx,
                     reinterpret_cast<const int8_t *>(a.packed), a.sw, a.bias, a.Y,
-                    a.out == Out::I32 ? a.acc : nullptr, a.M, a.K, a.N);
+                    a.out == Out::I32 ? a.acc : nullptr, a.M, a.K, a.N, a.relu);
     else
         launch_main(k_w4a8_generic, g, dim3(256), 0, st, a.Xq, a.sx, a.packed, a.sw, a.bias, a.Y,
-                    a.out == Out::I32 ? a.acc : nullptr, a.M, a.K, a.N);
+                    a.out == Out::I32 ? a.acc : nullptr, a.M, a.K, a.N, a.relu);
     return hipGetLastError();
 }
 

@@ -43,7 +43,8 @@ struct W4A8Args {
     int32_t *acc;
     int64_t M, K, N;
     Out out;
-    bool w8;  // 8-bit weight codes (W8A8): natural-layout activations, no unpacking
+    bool w8;    // 8-bit weight codes (W8A8): natural-layout activations, no unpacking
+    bool relu;  // ReLU after dequantization and bias (Out::Y only)
 };
 
 hipError_t launch_quant_weight_sym(const float *W, int64_t K, int64_t N, uint8_t *packed,

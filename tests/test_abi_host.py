@@ -17,6 +17,7 @@ HEADER = os.path.join(ROOT, "include", "w4.h")
 
 W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_SCHEME, W4_ERR_WORKSPACE, W4_ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6)
+W4_ERR_ARG = -7
 FAKE = 1 << 20  # a non-NULL, 256-aligned address; never dereferenced by these calls
 
 
@@ -41,7 +42,8 @@ def test_header_declares_the_boundary():
     for want in ["w4_quantize_weight", "a8_quantize_act", "w4a8_linear", "w4a16_linear",
                  "w4a8_linear_q", "w4a8_matmul_i32", "w4a8_workspace_bytes",
                  "w8_quantize_weight", "w8a8_workspace_bytes", "w8a8_linear",
-                 "w8a8_matmul_i32", "w4_status_string", "w4_last_path"]:
+                 "w8a8_matmul_i32", "w4a8_linear_act", "w8a8_linear_act",
+                 "w4_status_string", "w4_last_path"]:
         assert want in names, names
 
 
@@ -52,7 +54,7 @@ def test_library_exports_every_declared_symbol(w4):
 
 
 def test_status_strings(w4):
-    for st in range(-6, 1):
+    for st in range(-7, 1):
         assert w4.w4_status_string(st) and w4.w4_status_string(st) != "unknown status"
     assert w4.w4_status_string(-99) == "unknown status"
 
@@ -130,6 +132,19 @@ def test_w8a8_checks(w4):
     assert h(FAKE, None, 2, 64, 8, FAKE, FAKE, ws, None) == W4_ERR_NULL
     assert h(FAKE, FAKE, 2, 64, 8, FAKE + 2, FAKE, ws, None) == W4_ERR_ALIGN
     assert h(FAKE, FAKE, 2, 64, 8, FAKE, FAKE, 3, None) == W4_ERR_WORKSPACE
+
+
+def test_linear_act_checks(w4):
+    ws = w4.w4a8_workspace_bytes(2, 64, 8)
+    for f in (w4.lib().w4a8_linear_act, w4.lib().w8a8_linear_act):
+        assert f(None, 2, 64, 8, FAKE, FAKE, None, 1, FAKE, FAKE, ws, None) == W4_ERR_NULL
+        assert f(FAKE, 2, 64, 8, FAKE, FAKE, None, 2, FAKE, FAKE, ws, None) == W4_ERR_ARG
+        assert f(FAKE, 2, 64, 8, FAKE, FAKE, None, -1, FAKE, FAKE, ws, None) == W4_ERR_ARG
+        assert f(FAKE, 0, 64, 8, FAKE, FAKE, None, 1, FAKE, FAKE, ws, None) == W4_ERR_SHAPE
+        assert f(FAKE, 2, 64, 8, FAKE, FAKE, None, 1, FAKE + 2, FAKE, ws, None) == W4_ERR_ALIGN
+        assert f(FAKE, 2, 64, 8, FAKE, FAKE, None, 1, FAKE, FAKE, ws - 1, None) == W4_ERR_WORKSPACE
+    with pytest.raises(ValueError):
+        w4._act("gelu")
 
 
 def test_w4a16_checks(w4):
