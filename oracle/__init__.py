@@ -12,6 +12,8 @@ arrays.  The formulas and their sources are documented there:
   [-8, 7], two per byte) -- Keras INT4 guide, "How it works", steps 1-2;
 * per-row dynamic int8 activations (scale = absmax / 127) -- same, step 3;
 * the toy model's ReLU on a Dense output (after the bias);
+* weight dequantization and the lossy LoRA merge (dequantize, add the delta,
+  requantize) -- Keras guide, "Limitations";
 * exact int8 x int4 products summed in int32 -- steps 4-5;
 * dequantization by input_scale * per_channel_kernel_scale -- step 6;
 * symmetric per-output-channel int8 weights (scale = absmax / 127, codes in
@@ -63,6 +65,8 @@ def _load():
             "orc_matmul_w8_i32": [_P, _P, _I, _I, _I, _P],
             "orc_w8a8_linear": [_P, _I, _I, _I, _P, _P, _P, _P],
             "orc_relu": [_P, _I],
+            "orc_dequant_weight": [_P, _P, _P, _I, _I, _I, _P],
+            "orc_merge_delta": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
             "orc_w4a16_dequant": [_P, _P, _P, _I, _I, _I, _P],
             "orc_w4a16_linear": [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P],
         }
@@ -226,6 +230,32 @@ def quantize_weight_asym(W: np.ndarray, group: int):
     _check(_load().orc_quantize_weight_asym(_ptr(W), K, N, group, _ptr(packed),
                                             _ptr(scales), _ptr(zeros)), "quantize_weight_asym")
     return packed, scales, zeros
+
+
+def dequant_weight(packed, scales, zeros, K: int, group: int = 0) -> np.ndarray:
+    """W [K, N] fp32 from packed codes: symmetric when zeros is None."""
+    packed = np.ascontiguousarray(packed, np.uint8)
+    N = packed.shape[0]
+    W = np.zeros((K, N), np.float32)
+    z = None if zeros is None else _f32(zeros)
+    _check(_load().orc_dequant_weight(_ptr(packed), _ptr(_f32(scales)), _ptr(z), K, N, group,
+                                      _ptr(W)), "dequant_weight")
+    return W
+
+
+def merge_delta(packed, scales, zeros, K: int, delta: np.ndarray, group: int = 0):
+    """Requantize dequant(packed) + delta [K, N]; returns (packed, scales, zeros)."""
+    packed = np.ascontiguousarray(packed, np.uint8)
+    N = packed.shape[0]
+    delta = _f32(delta)
+    assert delta.shape == (K, N)
+    po = np.zeros_like(packed)
+    so = np.zeros_like(_f32(scales))
+    zo = None if zeros is None else np.zeros_like(_f32(zeros))
+    _check(_load().orc_merge_delta(_ptr(packed), _ptr(_f32(scales)),
+                                   _ptr(None if zeros is None else _f32(zeros)), K, N, group,
+                                   _ptr(delta), _ptr(po), _ptr(so), _ptr(zo)), "merge_delta")
+    return po, so, zo
 
 
 def bf16_rne(x: np.ndarray) -> np.ndarray:

@@ -303,6 +303,53 @@ int orc_quantize_weight_asym(const float *W, int64_t K, int64_t N, int64_t group
     return ORC_OK;
 }
 
+/* [KERAS] "Limitations": the LoRA export path dequantizes the weights, adds
+ * the delta and requantizes.  Weight dequantization follows the dequant
+ * formulas of the pages: symmetric codes ([KERAS] step 6 applied to the
+ * kernel, [BLOG] 6.2): w = fl(q * s); asymmetric groups ([W4A16] "量化原理"):
+ * w = fl(fl(q - zp) * s).  Output W [K][N] fp32. */
+int orc_dequant_weight(const uint8_t *packed, const float *scales, const float *zeros,
+                       int64_t K, int64_t N, int64_t group, float *W) {
+    if (K < 1 || N < 1) return ORC_ERR_SHAPE;
+    if (zeros && (group < 1 || K % group != 0)) return ORC_ERR_SHAPE;
+    for (int64_t k = 0; k < K; ++k) {
+        for (int64_t n = 0; n < N; ++n) {
+            float w;
+            if (zeros) {
+                const int64_t G = K / group;
+                int q = unpack_unsigned(packed, K, n, k);
+                float d = (float)q - zeros[n * G + k / group];
+                w = d * scales[n * G + k / group];
+            } else {
+                int q = orc_unpack_signed(packed, K, n, k);
+                w = (float)q * scales[n];
+            }
+            W[k * N + n] = w;
+        }
+    }
+    return ORC_OK;
+}
+
+/* The merge itself: W' = fl(dequant(packed) + delta), then the scheme's
+ * quantization of W' (new codes, scales and zero points). */
+int orc_merge_delta(const uint8_t *packed, const float *scales, const float *zeros,
+                    int64_t K, int64_t N, int64_t group, const float *delta,
+                    uint8_t *packed_out, float *scales_out, float *zeros_out) {
+    if (K < 1 || N < 1) return ORC_ERR_SHAPE;
+    float *W = (float *)malloc((size_t)(K * N) * sizeof(float));
+    if (!W) return ORC_ERR_SHAPE;
+    int rc = orc_dequant_weight(packed, scales, zeros, K, N, group, W);
+    if (rc == ORC_OK) {
+        for (int64_t i = 0; i < K * N; ++i) W[i] = W[i] + delta[i];
+        if (zeros)
+            rc = orc_quantize_weight_asym(W, K, N, group, packed_out, scales_out, zeros_out);
+        else
+            rc = orc_quantize_weight_sym(W, K, N, packed_out, scales_out);
+    }
+    free(W);
+    return rc;
+}
+
 /* Round-to-nearest-even of an fp32 value to the bf16 format (the upper 16 bits
  * of the fp32 encoding).  NaN is kept quiet. */
 uint16_t orc_bf16_rne(float f) {

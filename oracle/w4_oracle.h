@@ -81,6 +81,17 @@ int orc_w8a8_linear(const float *X, int64_t M, int64_t K, int64_t N, const int8_
 int orc_quantize_weight_asym(const float *W, int64_t K, int64_t N, int64_t group,
                              uint8_t *packed, float *scales, float *zeros);
 
+/* Weight dequantization to fp32 W [K][N]: zeros == NULL -> symmetric codes,
+ * w = fl(q * s[n]); else asymmetric groups, w = fl(fl(q - zp) * s). */
+int orc_dequant_weight(const uint8_t *packed, const float *scales, const float *zeros,
+                       int64_t K, int64_t N, int64_t group, float *W);
+
+/* LoRA-style merge: requantize fl(dequant(packed) + delta) with the same scheme
+ * (zeros == NULL: symmetric per channel; else asymmetric groups). */
+int orc_merge_delta(const uint8_t *packed, const float *scales, const float *zeros,
+                    int64_t K, int64_t N, int64_t group, const float *delta,
+                    uint8_t *packed_out, float *scales_out, float *zeros_out);
+
 /* fp32 -> bf16 round-half-to-even (bit pattern). */
 uint16_t orc_bf16_rne(float f);
 
