@@ -93,6 +93,32 @@ int w4_quantize_weight(const float *W, int64_t K, int64_t N, int scheme,
                        int64_t group_size, uint8_t *packed, float *scales,
                        float *zeros, void *stream);
 
+/* Dequantize packed int4 weights back to fp32 (the dequantization step of
+ * the LoRA export path, Keras guide "Limitations"; formulas of step 6 and of
+ * the weight-only page's quantization principle).
+ *   packed, scales, zeros, scheme, group_size as produced by w4_quantize_weight.
+ *   W  [K][N] fp32: fl(code * scale[n]) for W4_SYM_PER_CHANNEL,
+ *      fl(fl(code - zero) * scale) for W4_ASYM_GROUP.
+ * Returns W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_SCHEME or W4_ERR_HIP. */
+int w4_dequantize_weight(const uint8_t *packed, const float *scales, const float *zeros,
+                         int64_t K, int64_t N, int scheme, int64_t group_size, float *W,
+                         void *stream);
+
+/* The lossy LoRA merge (Keras guide, "Limitations": dequantize -> add the
+ * delta -> requantize):
+ *   work = fl(dequant(packed) + delta)   (delta [K][N] fp32, e.g. B @ A),
+ *   (packed_out, scales_out, zeros_out) = w4_quantize_weight(work, same scheme).
+ *   work  caller-owned device scratch of K*N fp32 (overwritten; must not
+ *         overlap any other argument).
+ * packed_out / scales_out / zeros_out may be the input arrays (in place): the
+ * steps run in order on `stream`.  zeros and zeros_out are NULL for
+ * W4_SYM_PER_CHANNEL.
+ * Returns W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_SCHEME or W4_ERR_HIP. */
+int w4_merge_delta(const uint8_t *packed, const float *scales, const float *zeros,
+                   int64_t K, int64_t N, int scheme, int64_t group_size,
+                   const float *delta, uint8_t *packed_out, float *scales_out,
+                   float *zeros_out, float *work, void *stream);
+
 /* Per-row dynamic int8 activation quantization (Keras guide step 3).
  *   X   [M][K] fp32, finite.
  *   sx  [M]: sx[m] = fl(max_k |X[m][k]| / 127) (0 for an all-zero row).

@@ -7,6 +7,8 @@ functions carry the C names:
 
 * ``w4_quantize_weight``  -- symmetric per-channel int4 (``scheme="sym"``) or
   asymmetric group-wise int4 (``scheme="asym"``) weights, packed two per byte;
+* ``w4_dequantize_weight`` -- packed codes back to fp32 weights;
+* ``w4_merge_delta``      -- the lossy LoRA merge (dequantize, add, requantize);
 * ``a8_quantize_act``     -- per-row dynamic int8 activations;
 * ``w4a8_linear``         -- the W4A8 forward from fp32 activations;
 * ``w4a8_linear_act``     -- the same with a fused activation (ReLU);
@@ -73,6 +75,9 @@ def lib():
             "w4a8_matmul_i32": ([_P, _P, _I, _I, _I, _P, _P, _Z, _P], ctypes.c_int),
             "w4a16_linear": ([_P, _I, _I, _I, _P, _P, _P, _I, _P, _P], ctypes.c_int),
             "w8_quantize_weight": ([_P, _I, _I, _P, _P, _P], ctypes.c_int),
+            "w4_dequantize_weight": ([_P, _P, _P, _I, _I, ctypes.c_int, _I, _P, _P], ctypes.c_int),
+            "w4_merge_delta": ([_P, _P, _P, _I, _I, ctypes.c_int, _I, _P, _P, _P, _P, _P, _P],
+                               ctypes.c_int),
             "w8a8_workspace_bytes": ([_I, _I, _I], _Z),
             "w8a8_linear": ([_P, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P], ctypes.c_int),
             "w8a8_matmul_i32": ([_P, _P, _I, _I, _I, _P, _P, _Z, _P], ctypes.c_int),
@@ -168,6 +173,49 @@ def w4_quantize_weight(W: torch.Tensor, scheme: str = "sym", group_size: int = 0
                                   _opt(zeros, "zeros", torch.float32), _stream(stream))
     _check("w4_quantize_weight", rc)
     return packed, scales, zeros
+
+
+def _scheme(scheme: str) -> int:
+    return {"sym": W4_SYM_PER_CHANNEL, "asym": W4_ASYM_GROUP}.get(scheme, -1)
+
+
+def w4_dequantize_weight(packed: torch.Tensor, scales: torch.Tensor, zeros, K: int,
+                         scheme: str = "sym", group_size: int = 0, W=None, stream=None):
+    """packed [N, ceil(K/2)] (+ scales, zeros) -> W [K, N] fp32."""
+    N = packed.shape[0]
+    if W is None:
+        W = torch.empty((K, N), dtype=torch.float32, device=packed.device)
+    rc = lib().w4_dequantize_weight(_dev(packed, "packed", torch.uint8),
+                                    _dev(scales, "scales", torch.float32),
+                                    _opt(zeros, "zeros", torch.float32), K, N, _scheme(scheme),
+                                    group_size, _dev(W, "W", torch.float32), _stream(stream))
+    _check("w4_dequantize_weight", rc)
+    return W
+
+
+def w4_merge_delta(packed: torch.Tensor, scales: torch.Tensor, zeros, delta: torch.Tensor,
+                   scheme: str = "sym", group_size: int = 0, in_place: bool = False,
+                   work=None, stream=None):
+    """Requantize dequant(packed) + delta [K, N]; returns (packed, scales, zeros),
+    new tensors unless in_place (then the inputs are overwritten)."""
+    K, N = delta.shape
+    if in_place:
+        po, so, zo = packed, scales, zeros
+    else:
+        po, so = torch.empty_like(packed), torch.empty_like(scales)
+        zo = None if zeros is None else torch.empty_like(zeros)
+    if work is None:
+        work = torch.empty((K, N), dtype=torch.float32, device=packed.device)
+    rc = lib().w4_merge_delta(_dev(packed, "packed", torch.uint8),
+                              _dev(scales, "scales", torch.float32),
+                              _opt(zeros, "zeros", torch.float32), K, N, _scheme(scheme),
+                              group_size, _dev(delta, "delta", torch.float32),
+                              _dev(po, "packed_out", torch.uint8),
+                              _dev(so, "scales_out", torch.float32),
+                              _opt(zo, "zeros_out", torch.float32),
+                              _dev(work, "work", torch.float32), _stream(stream))
+    _check("w4_merge_delta", rc)
+    return po, so, zo
 
 
 def a8_quantize_act(X: torch.Tensor, Xq=None, sx=None, stream=None):

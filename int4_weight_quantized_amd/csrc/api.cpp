@@ -164,6 +164,65 @@ int w4_quantize_weight(const float *W, int64_t K, int64_t N, int scheme, int64_t
     return W4_ERR_SCHEME;
 }
 
+// Shared checks of the dequantize and merge entry points: scheme, group and
+// pointer alignment of the code / scale / zero-point arrays.
+static int dequant_args_ok(const uint8_t *packed, const float *scales, const float *zeros,
+                           int64_t K, int64_t N, int scheme, int64_t group_size) {
+    if (!packed || !scales) return W4_ERR_NULL;
+    if (!shape_ok(1, K, N)) return W4_ERR_SHAPE;
+    if (!aligned(scales, 4)) return W4_ERR_ALIGN;
+    if (scheme == W4_SYM_PER_CHANNEL) {
+        if (group_size != 0 || zeros) return W4_ERR_SHAPE;
+        return W4_OK;
+    }
+    if (scheme == W4_ASYM_GROUP) {
+        if (!zeros) return W4_ERR_NULL;
+        if (!aligned(zeros, 4)) return W4_ERR_ALIGN;
+        if (group_size < 2 || group_size % 2 != 0 || K % group_size != 0) return W4_ERR_SHAPE;
+        if (K / group_size > 65535) return W4_ERR_SHAPE;
+        return W4_OK;
+    }
+    return W4_ERR_SCHEME;
+}
+
+int w4_dequantize_weight(const uint8_t *packed, const float *scales, const float *zeros,
+                         int64_t K, int64_t N, int scheme, int64_t group_size, float *W,
+                         void *stream) {
+    int rc = dequant_args_ok(packed, scales, zeros, K, N, scheme, group_size);
+    if (rc != W4_OK) return rc;
+    if (!W) return W4_ERR_NULL;
+    if (!aligned(W, 4)) return W4_ERR_ALIGN;
+    g_last_path = "dequant_weight";
+    return hip_status(w4::launch_dequant_weight(packed, scales,
+                                                scheme == W4_ASYM_GROUP ? zeros : nullptr, K, N,
+                                                group_size, nullptr, W,
+                                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+int w4_merge_delta(const uint8_t *packed, const float *scales, const float *zeros, int64_t K,
+                   int64_t N, int scheme, int64_t group_size, const float *delta,
+                   uint8_t *packed_out, float *scales_out, float *zeros_out, float *work,
+                   void *stream) {
+    int rc = dequant_args_ok(packed, scales, zeros, K, N, scheme, group_size);
+    if (rc != W4_OK) return rc;
+    if (!delta || !packed_out || !scales_out || !work) return W4_ERR_NULL;
+    if (scheme == W4_ASYM_GROUP && !zeros_out) return W4_ERR_NULL;
+    if (scheme == W4_SYM_PER_CHANNEL && zeros_out) return W4_ERR_SHAPE;
+    if (!aligned(delta, 4) || !aligned(scales_out, 4) || !aligned(work, 4) ||
+        (zeros_out && !aligned(zeros_out, 4)))
+        return W4_ERR_ALIGN;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const bool asym = scheme == W4_ASYM_GROUP;
+    hipError_t e = w4::launch_dequant_weight(packed, scales, asym ? zeros : nullptr, K, N,
+                                             group_size, delta, work, st);
+    if (e != hipSuccess) return W4_ERR_HIP;
+    g_last_path = "merge_delta";
+    if (asym)
+        return hip_status(w4::launch_quant_weight_asym(work, K, N, group_size, packed_out,
+                                                       scales_out, zeros_out, st));
+    return hip_status(w4::launch_quant_weight_sym(work, K, N, packed_out, scales_out, st));
+}
+
 int a8_quantize_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx, void *stream) {
     if (!X || !Xq || !sx) return W4_ERR_NULL;
     if (M < 1 || K < 1 || M > 0x7FFFFFFF || K > ((int64_t)1 << 40) / M) return W4_ERR_SHAPE;

@@ -53,6 +53,11 @@ hipError_t launch_quant_weight_w8(const float *W, int64_t K, int64_t N, int8_t *
                                   hipStream_t st);
 hipError_t launch_quant_weight_asym(const float *W, int64_t K, int64_t N, int64_t group,
                                     uint8_t *packed, float *scales, float *zeros, hipStream_t st);
+// W [K][N] = dequantized codes (+ delta [K][N] when non-NULL); zeros == NULL
+// selects the symmetric form.
+hipError_t launch_dequant_weight(const uint8_t *packed, const float *scales, const float *zeros,
+                                 int64_t K, int64_t N, int64_t group, const float *delta,
+                                 float *W, hipStream_t st);
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx, bool p8,
                             hipStream_t st);
 hipError_t launch_to_p8(const int8_t *Xq, int64_t M, int64_t K, int8_t *out, hipStream_t st);

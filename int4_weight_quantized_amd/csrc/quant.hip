@@ -161,6 +161,67 @@ hipError_t launch_quant_weight_w8(const float *W, int64_t K, int64_t N, int8_t *
     return hipGetLastError();
 }
 
+// ------------------------------------------------ weight dequantization
+// W[k][n] = fl(q * s[n]) (symmetric) or fl(fl(q - zp) * s) (asymmetric groups),
+// then + delta[k][n] when a delta is given (the LoRA merge's dequantize-and-add
+// step; Keras guide, "Limitations").  Thread (c, part) of a block owns column
+// c of 64 and 32 consecutive k of a 128-k slab: it reads the column's 16
+// packed bytes and writes W (and reads delta) coalesced over the 64 columns.
+template <bool ASYM>
+__global__ __launch_bounds__(256) void k_dequant_weight(const uint8_t *__restrict__ packed,
+                                                        const float *__restrict__ scales,
+                                                        const float *__restrict__ zeros,
+                                                        const float *__restrict__ delta,
+                                                        int64_t K, int64_t N, int64_t group,
+                                                        float *__restrict__ W) {
+    const int c = threadIdx.x % 64, part = threadIdx.x / 64;
+    const int64_t n = (int64_t)blockIdx.x * 64 + c;
+    if (n >= N) return;
+    const int64_t KB = (K + 1) / 2;
+    const int64_t kbeg = (int64_t)blockIdx.y * 128 + part * 32;
+    if (kbeg >= K) return;
+    const uint8_t *row = packed + n * KB + kbeg / 2;
+    uint8_t bytes[16];
+    if ((KB % 16) == 0 && kbeg / 2 + 16 <= KB && (reinterpret_cast<uintptr_t>(packed) & 15) == 0) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(row);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) bytes[j] = (uint8_t)(w[j / 4] >> (8 * (j % 4)));
+    } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) bytes[j] = (kbeg / 2 + j < KB) ? row[j] : 0;
+    }
+    const int64_t G = ASYM ? K / group : 1;
+    for (int j = 0; j < 32; ++j) {
+        const int64_t k = kbeg + j;
+        if (k >= K) break;
+        const int nib = (j & 1) ? (bytes[j / 2] >> 4) : (bytes[j / 2] & 0xF);
+        float w;
+        if (ASYM) {
+            const int64_t gi = n * G + k / group;
+            const float d = (float)nib - zeros[gi];
+            w = d * scales[gi];
+        } else {
+            w = (float)(nib >= 8 ? nib - 16 : nib) * scales[n];
+        }
+        if (delta) w = w + delta[k * N + n];
+        W[k * N + n] = w;
+    }
+}
+
+hipError_t launch_dequant_weight(const uint8_t *packed, const float *scales, const float *zeros,
+                                 int64_t K, int64_t N, int64_t group, const float *delta,
+                                 float *W, hipStream_t st) {
+    dim3 g((unsigned)((N + 63) / 64), (unsigned)((K + 127) / 128));
+    if (zeros)
+        hipLaunchKernelGGL(k_dequant_weight<true>, g, dim3(256), 0, st, packed, scales, zeros,
+                           delta, K, N, group, W);
+    else
+        hipLaunchKernelGGL(k_dequant_weight<false>, g, dim3(256), 0, st, packed, scales, zeros,
+                           delta, K, N, group, W);
+    return hipGetLastError();
+}
+
 // --------------------------------------------------- asymmetric group int4
 // One block per (64 columns, one group).  Thread (c, part): column c, a
 // contiguous quarter of the group's byte pairs.  The group size is even.

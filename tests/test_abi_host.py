@@ -43,6 +43,7 @@ def test_header_declares_the_boundary():
                  "w4a8_linear_q", "w4a8_matmul_i32", "w4a8_workspace_bytes",
                  "w8_quantize_weight", "w8a8_workspace_bytes", "w8a8_linear",
                  "w8a8_matmul_i32", "w4a8_linear_act", "w8a8_linear_act",
+                 "w4_dequantize_weight", "w4_merge_delta",
                  "w4_status_string", "w4_last_path"]:
         assert want in names, names
 
@@ -145,6 +146,25 @@ def test_linear_act_checks(w4):
         assert f(FAKE, 2, 64, 8, FAKE, FAKE, None, 1, FAKE, FAKE, ws - 1, None) == W4_ERR_WORKSPACE
     with pytest.raises(ValueError):
         w4._act("gelu")
+
+
+def test_dequant_merge_checks(w4):
+    d = w4.lib().w4_dequantize_weight
+    assert d(None, FAKE, None, 4, 4, 0, 0, FAKE, None) == W4_ERR_NULL
+    assert d(FAKE, FAKE, None, 4, 4, 0, 0, None, None) == W4_ERR_NULL
+    assert d(FAKE, FAKE, None, 0, 4, 0, 0, FAKE, None) == W4_ERR_SHAPE
+    assert d(FAKE, FAKE, None, 4, 4, 5, 0, FAKE, None) == W4_ERR_SCHEME
+    assert d(FAKE, FAKE, FAKE, 4, 4, 0, 0, FAKE, None) == W4_ERR_SHAPE     # sym takes no zeros
+    assert d(FAKE, FAKE, None, 256, 4, 1, 128, FAKE, None) == W4_ERR_NULL  # asym needs zeros
+    assert d(FAKE, FAKE, FAKE, 200, 4, 1, 128, FAKE, None) == W4_ERR_SHAPE
+    assert d(FAKE, FAKE, None, 4, 4, 0, 0, FAKE + 2, None) == W4_ERR_ALIGN
+    m = w4.lib().w4_merge_delta
+    assert m(FAKE, FAKE, None, 4, 4, 0, 0, None, FAKE, FAKE, None, FAKE, None) == W4_ERR_NULL
+    assert m(FAKE, FAKE, None, 4, 4, 0, 0, FAKE, FAKE, FAKE, None, None, None) == W4_ERR_NULL
+    assert m(FAKE, FAKE, None, 4, 4, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == W4_ERR_SHAPE
+    assert m(FAKE, FAKE, FAKE, 256, 4, 1, 128, FAKE, FAKE, FAKE, None, FAKE, None) == W4_ERR_NULL
+    assert m(FAKE, FAKE, None, 4, 4, 0, 0, FAKE, FAKE, FAKE, None, FAKE + 1, None) == W4_ERR_ALIGN
+    assert m(FAKE, FAKE, None, 4, 4, 9, 0, FAKE, FAKE, FAKE, None, FAKE, None) == W4_ERR_SCHEME
 
 
 def test_w4a16_checks(w4):
