@@ -14,6 +14,9 @@ arrays.  The formulas and their sources are documented there:
 * the toy model's ReLU on a Dense output (after the bias);
 * weight dequantization and the lossy LoRA merge (dequantize, add the delta,
   requantize) -- Keras guide, "Limitations";
+* AWQ-style activation-aware channel scaling (calibration magnitudes ->
+  power-of-two channel scales, W diag(s), x / s) -- "INT4" concept entry,
+  section 4.4;
 * exact int8 x int4 products summed in int32 -- steps 4-5;
 * dequantization by input_scale * per_channel_kernel_scale -- step 6;
 * symmetric per-output-channel int8 weights (scale = absmax / 127, codes in
@@ -65,6 +68,11 @@ def _load():
             "orc_matmul_w8_i32": [_P, _P, _I, _I, _I, _P],
             "orc_w8a8_linear": [_P, _I, _I, _I, _P, _P, _P, _P],
             "orc_relu": [_P, _I],
+            "orc_awq_channel_scales": [_P, _I, _I, ctypes.c_int, ctypes.c_int, _P],
+            "orc_awq_scale_bf16": [_P, _I, _I, _P, _P],
+            "orc_awq_fold_weight": [_P, _I, _I, _P, _P],
+            "orc_awq_quantize_act": [_P, _I, _I, _P, _P, _P],
+            "orc_w4a8_linear_awq": [_P, _I, _I, _I, _P, _P, _P, _P, _P],
             "orc_dequant_weight": [_P, _P, _P, _I, _I, _I, _P],
             "orc_merge_delta": [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P],
             "orc_w4a16_dequant": [_P, _P, _P, _I, _I, _I, _P],
@@ -179,6 +187,55 @@ def relu(Y: np.ndarray) -> np.ndarray:
     out = np.array(Y, dtype=np.float32, copy=True, order="C")
     _check(_load().orc_relu(_ptr(out), out.size), "relu")
     return out
+
+
+def awq_channel_scales(Xcal: np.ndarray, alpha=(1, 2)) -> np.ndarray:
+    """Calibration activations [M, K] -> power-of-two channel scales s [K]."""
+    Xcal = _f32(Xcal)
+    M, K = Xcal.shape
+    s = np.zeros(K, np.float32)
+    _check(_load().orc_awq_channel_scales(_ptr(Xcal), M, K, int(alpha[0]), int(alpha[1]),
+                                          _ptr(s)), "awq_channel_scales")
+    return s
+
+
+def awq_scale_bf16(Xbf16: np.ndarray, s: np.ndarray) -> np.ndarray:
+    X = np.ascontiguousarray(Xbf16, np.uint16)
+    M, K = X.shape
+    out = np.zeros_like(X)
+    _check(_load().orc_awq_scale_bf16(_ptr(X), M, K, _ptr(_f32(s)), _ptr(out)), "awq_scale_bf16")
+    return out
+
+
+def awq_fold_weight(W: np.ndarray, s: np.ndarray) -> np.ndarray:
+    W = _f32(W)
+    K, N = W.shape
+    out = np.zeros_like(W)
+    _check(_load().orc_awq_fold_weight(_ptr(W), K, N, _ptr(_f32(s)), _ptr(out)), "awq_fold")
+    return out
+
+
+def awq_quantize_act(X: np.ndarray, s: np.ndarray):
+    X = _f32(X)
+    M, K = X.shape
+    Xq = np.zeros((M, K), np.int8)
+    sx = np.zeros(M, np.float32)
+    _check(_load().orc_awq_quantize_act(_ptr(X), M, K, _ptr(_f32(s)), _ptr(Xq), _ptr(sx)),
+           "awq_quantize_act")
+    return Xq, sx
+
+
+def w4a8_linear_awq(X: np.ndarray, packed: np.ndarray, sw: np.ndarray, s: np.ndarray,
+                    bias=None) -> np.ndarray:
+    X = _f32(X)
+    M, K = X.shape
+    packed = np.ascontiguousarray(packed, np.uint8)
+    N = packed.shape[0]
+    b = None if bias is None else _f32(bias)
+    Y = np.zeros((M, N), np.float32)
+    _check(_load().orc_w4a8_linear_awq(_ptr(X), M, K, N, _ptr(packed), _ptr(_f32(sw)),
+                                       _ptr(_f32(s)), _ptr(b), _ptr(Y)), "w4a8_linear_awq")
+    return Y
 
 
 def quantize_weight_w8(W: np.ndarray):

@@ -184,6 +184,122 @@ int orc_relu(float *Y, int64_t n) {
     return ORC_OK;
 }
 
+/* [ENCY] 4.4 (AWQ's core idea): on calibration data, measure the activation
+ * magnitude of every input channel; scale up the weights of the important
+ * channels, W' = W diag(s), quantize W', and at inference divide the
+ * activations by s before quantizing them.  The page fixes neither the
+ * magnitude statistic nor the rule from magnitude to s; this oracle takes:
+ *   a_k = max_m |Xcal[m][k]|                      (magnitude of channel k),
+ *   E_k = floor(log2 a_k)  (E_k = -150 for a_k = 0, below every finite value),
+ *   E_med = the lower median of E_k over the K channels,
+ *   s_k = 2^e_k, e_k = min(24, max(0, floor(alpha * (E_k - E_med)))),
+ * alpha = alpha_num / alpha_den (1/2 by default in the library): a fraction of
+ * the log-magnitude excess over the median, as a power of two, so that W * s
+ * and x / s are exact in fp32 and bf16. */
+static int cmp_int(const void *a, const void *b) {
+    const int x = *(const int *)a, y = *(const int *)b;
+    return (x > y) - (x < y);
+}
+
+int orc_awq_channel_scales(const float *Xcal, int64_t M, int64_t K, int alpha_num,
+                           int alpha_den, float *s) {
+    if (M < 1 || K < 1 || alpha_num < 0 || alpha_den < 1) return ORC_ERR_SHAPE;
+    int *E = (int *)malloc((size_t)K * sizeof(int));
+    int *sorted = (int *)malloc((size_t)K * sizeof(int));
+    if (!E || !sorted) {
+        free(E);
+        free(sorted);
+        return ORC_ERR_SHAPE;
+    }
+    int rc = ORC_OK;
+    for (int64_t k = 0; k < K && rc == ORC_OK; ++k) {
+        float a = 0.0f;
+        for (int64_t m = 0; m < M; ++m) {
+            float x = Xcal[m * K + k];
+            if (!isfinite(x)) {
+                rc = ORC_ERR_NONFINITE;
+                break;
+            }
+            if (fabsf(x) > a) a = fabsf(x);
+        }
+        int ex = 0;
+        if (a == 0.0f) {
+            E[k] = -150;
+        } else {
+            frexpf(a, &ex); /* a = f * 2^ex with f in [0.5, 1) */
+            E[k] = ex - 1;
+        }
+        sorted[k] = E[k];
+    }
+    if (rc == ORC_OK) {
+        qsort(sorted, (size_t)K, sizeof(int), cmp_int);
+        const int med = sorted[(K - 1) / 2];
+        for (int64_t k = 0; k < K; ++k) {
+            int d = E[k] - med;
+            int e = d > 0 ? (d * alpha_num) / alpha_den : 0;
+            if (e > 24) e = 24;
+            s[k] = ldexpf(1.0f, e);
+        }
+    }
+    free(E);
+    free(sorted);
+    return rc;
+}
+
+/* W' = W diag(s): row k of W [K][N] times s_k, one rounding each. */
+int orc_awq_fold_weight(const float *W, int64_t K, int64_t N, const float *s, float *Wout) {
+    if (K < 1 || N < 1) return ORC_ERR_SHAPE;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) Wout[k * N + n] = W[k * N + n] * s[k];
+    return ORC_OK;
+}
+
+/* Activation side: x' = fl(x / s_k), then [KERAS] step 3 on x'. */
+int orc_awq_quantize_act(const float *X, int64_t M, int64_t K, const float *s, int8_t *Xq,
+                         float *sx) {
+    if (M < 1 || K < 1) return ORC_ERR_SHAPE;
+    float *Xs = (float *)malloc((size_t)(M * K) * sizeof(float));
+    if (!Xs) return ORC_ERR_SHAPE;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) Xs[m * K + k] = X[m * K + k] / s[k];
+    int rc = orc_quantize_act(Xs, M, K, Xq, sx);
+    free(Xs);
+    return rc;
+}
+
+/* bf16 activations for the weight-only path: x' = bf16(fl(x / s_k)) (exact
+ * when s_k is a power of two). */
+int orc_awq_scale_bf16(const uint16_t *X, int64_t M, int64_t K, const float *s, uint16_t *Xout) {
+    if (M < 1 || K < 1) return ORC_ERR_SHAPE;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            uint32_t u = (uint32_t)X[m * K + k] << 16;
+            float x;
+            memcpy(&x, &u, 4);
+            Xout[m * K + k] = orc_bf16_rne(x / s[k]);
+        }
+    return ORC_OK;
+}
+
+/* The W4A8 forward with AWQ scaling: packed / sw quantize W diag(s). */
+int orc_w4a8_linear_awq(const float *X, int64_t M, int64_t K, int64_t N, const uint8_t *packed,
+                        const float *sw, const float *s, const float *bias, float *Y) {
+    if (M < 1 || K < 1 || N < 1) return ORC_ERR_SHAPE;
+    int8_t *Xq = (int8_t *)malloc((size_t)(M * K));
+    float *sx = (float *)malloc((size_t)M * sizeof(float));
+    int32_t *acc = (int32_t *)malloc((size_t)(M * N) * sizeof(int32_t));
+    int rc = ORC_ERR_SHAPE;
+    if (Xq && sx && acc) {
+        rc = orc_awq_quantize_act(X, M, K, s, Xq, sx);
+        if (rc == ORC_OK) rc = orc_matmul_i32(Xq, packed, M, K, N, acc);
+        if (rc == ORC_OK) rc = orc_dequant(acc, sx, sw, bias, M, N, Y);
+    }
+    free(Xq);
+    free(sx);
+    free(acc);
+    return rc;
+}
+
 /* W8A8, the INT8 path that [KERAS] "How it works" says the INT4 path follows
  * apart from the unpacking: steps 1-6 with 8-bit weight codes.  [ENCY] 4.1
  * with b = 8: symmetric scale = max|x| / (2^(b-1) - 1) = / 127 per output

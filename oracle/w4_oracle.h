@@ -64,6 +64,26 @@ int orc_w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N,
 /* ReLU on a layer output, in place: y > 0 ? y : +0. */
 int orc_relu(float *Y, int64_t n);
 
+/* AWQ-style channel scales from calibration activations Xcal [M][K]:
+ * s_k = 2^min(24, max(0, floor(alpha (E_k - E_med)))), E_k = floor(log2 max_m |x|),
+ * alpha = alpha_num / alpha_den. */
+int orc_awq_channel_scales(const float *Xcal, int64_t M, int64_t K, int alpha_num,
+                           int alpha_den, float *s);
+
+/* bf16 activations divided by s: Xout = bf16(fl(X / s_k)) (bit patterns). */
+int orc_awq_scale_bf16(const uint16_t *X, int64_t M, int64_t K, const float *s, uint16_t *Xout);
+
+/* Wout[k][n] = fl(W[k][n] * s[k]). */
+int orc_awq_fold_weight(const float *W, int64_t K, int64_t N, const float *s, float *Wout);
+
+/* Xq, sx = per-row int8 quantization of x' = fl(X / s) (s per column k). */
+int orc_awq_quantize_act(const float *X, int64_t M, int64_t K, const float *s, int8_t *Xq,
+                         float *sx);
+
+/* The W4A8 forward on x' = X / s with weights quantized from W diag(s). */
+int orc_w4a8_linear_awq(const float *X, int64_t M, int64_t K, int64_t N, const uint8_t *packed,
+                        const float *sw, const float *s, const float *bias, float *Y);
+
 /* Symmetric per-output-channel int8 weight quantization (scale = absmax/127,
  * codes in [-128, 127]).  Outputs Wq [N][K] int8 (channel-major), sw [N]. */
 int orc_quantize_weight_w8(const float *W, int64_t K, int64_t N, int8_t *Wq, float *sw);
