@@ -53,6 +53,15 @@ def test_scales_closed_form(orc):
         assert np.array_equal(s, want), (num, den, s)
 
 
+def test_zero_channels_as_median(orc):
+    """All-zero channels sit below every finite magnitude (E = -150): with two
+    of three channels zero the median is -150, so a channel of magnitude
+    2^-140 (E = -140) is 10 octaves above it: s = 2^10 at alpha = 1."""
+    X = np.array([[0.0, 0.0, 2.0**-140], [0.0, 0.0, -(2.0**-141)]], np.float32)
+    assert orc.awq_channel_scales(X, (1, 1)).tolist() == [1.0, 1.0, 1024.0]
+    assert orc.awq_channel_scales(X, (1, 2)).tolist() == [1.0, 1.0, 32.0]
+
+
 def test_scales_huge_channel_capped(orc):
     X = calib(16, big={2: 2.0**100})
     s = orc.awq_channel_scales(X, (1, 1))
