@@ -175,6 +175,50 @@ int w4a8_matmul_i32(const int8_t *Xq, const uint8_t *packed, int64_t M,
                     int64_t K, int64_t N, int32_t *acc, void *workspace,
                     size_t workspace_bytes, void *stream);
 
+/* ---- AWQ-style activation-aware channel scaling ("INT4" concept entry,
+ * section 4.4: measure each input channel's activation magnitude on
+ * calibration data, scale the weights of the important channels up,
+ * W' = W diag(s), quantize W', and divide the activations by s at inference;
+ * x/s times W diag(s) is x W).  The page fixes neither the magnitude
+ * statistic nor the rule from magnitude to s; these calls take:
+ *   a_k   = max over the calibration rows of |x[m][k]|,
+ *   E_k   = floor(log2 a_k) (-150 for an all-zero channel),
+ *   E_med = the lower median of E over the K channels,
+ *   s_k   = 2^e_k, e_k = min(24, max(0, floor(alpha_num * (E_k - E_med) / alpha_den))).
+ * Powers of two make the fold and the activation division exact in fp32 and
+ * bf16; only the quantization error changes. */
+
+/* Channel scales s [K] fp32 from calibration activations Xcal [M][K] fp32
+ * (finite).  0 <= alpha_num <= 1024, 1 <= alpha_den <= 1024, else W4_ERR_ARG.
+ * Returns W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ARG, W4_ERR_ALIGN or W4_ERR_HIP. */
+int awq_channel_scales(const float *Xcal, int64_t M, int64_t K, int alpha_num,
+                       int alpha_den, float *s, void *stream);
+
+/* W_out [K][N] = fl(W[k][n] * s[k]) (W_out may be W).  The result is then
+ * quantized with w4_quantize_weight (either scheme) or w8_quantize_weight. */
+int awq_fold_weight(const float *W, int64_t K, int64_t N, const float *s, float *W_out,
+                    void *stream);
+
+/* a8_quantize_act of x' = fl(X[m][k] / s[k]) (s any positive finite values). */
+int awq_quantize_act(const float *X, int64_t M, int64_t K, const float *s, int8_t *Xq,
+                     float *sx, void *stream);
+
+/* Weight-only path: X_out = bf16_rne(fl(float(X_bf16[m][k]) / s[k])) (bit
+ * patterns; exact for power-of-two s), to feed w4a16_linear with weights
+ * quantized from W diag(s). */
+int awq_scale_act_bf16(const uint16_t *X_bf16, int64_t M, int64_t K, const float *s,
+                       uint16_t *X_out, void *stream);
+
+/* The W4A8 forward with AWQ scaling: Y = act(dequant(quant(X / s) . codes)
+ * [+ bias]), with packed / sw from w4_quantize_weight(awq_fold_weight(W, s)).
+ * The division by s is fused into the activation quantization (into the
+ * single-launch decode kernel for M <= 4).  s [K] is 16-byte aligned.
+ * Other arguments and return codes as w4a8_linear_act. */
+int w4a8_linear_awq(const float *X, int64_t M, int64_t K, int64_t N,
+                    const uint8_t *packed, const float *sw, const float *s,
+                    const float *bias, int activation, float *Y, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
 /* ---- W8A8: the INT8 path that the Keras guide's "How it works" says the
  * INT4 path follows apart from the unpacking (steps 1-6 with 8-bit weight
  * codes; "INT4" concept entry, section 4.1 with b = 8 for the scale). */

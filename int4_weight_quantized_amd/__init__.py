@@ -18,7 +18,10 @@ functions carry the C names:
 * ``w8a8_linear``         -- the W8A8 forward from fp32 activations;
 * ``w8a8_linear_act``     -- the same with a fused activation (ReLU);
 * ``w8a8_matmul_i32``     -- its exact int32 accumulators alone;
-* ``w4a16_linear``        -- the weight-only forward with bf16 activations.
+* ``w4a16_linear``        -- the weight-only forward with bf16 activations;
+* ``awq_channel_scales``, ``awq_fold_weight``, ``awq_quantize_act``,
+  ``awq_scale_act_bf16``, ``w4a8_linear_awq`` -- AWQ-style activation-aware
+  channel scaling (power-of-two scales from calibration activations).
 
 There is no CPU fallback: without the built library (``build.py``) or
 without a GPU every call raises.
@@ -75,6 +78,12 @@ def lib():
             "w4a8_matmul_i32": ([_P, _P, _I, _I, _I, _P, _P, _Z, _P], ctypes.c_int),
             "w4a16_linear": ([_P, _I, _I, _I, _P, _P, _P, _I, _P, _P], ctypes.c_int),
             "w8_quantize_weight": ([_P, _I, _I, _P, _P, _P], ctypes.c_int),
+            "awq_channel_scales": ([_P, _I, _I, ctypes.c_int, ctypes.c_int, _P, _P], ctypes.c_int),
+            "awq_fold_weight": ([_P, _I, _I, _P, _P, _P], ctypes.c_int),
+            "awq_quantize_act": ([_P, _I, _I, _P, _P, _P, _P], ctypes.c_int),
+            "awq_scale_act_bf16": ([_P, _I, _I, _P, _P, _P], ctypes.c_int),
+            "w4a8_linear_awq": ([_P, _I, _I, _I, _P, _P, _P, _P, ctypes.c_int, _P, _P, _Z, _P],
+                                ctypes.c_int),
             "w4_dequantize_weight": ([_P, _P, _P, _I, _I, ctypes.c_int, _I, _P, _P], ctypes.c_int),
             "w4_merge_delta": ([_P, _P, _P, _I, _I, ctypes.c_int, _I, _P, _P, _P, _P, _P, _P],
                                ctypes.c_int),
@@ -364,6 +373,73 @@ def w8a8_matmul_i32(Xq: torch.Tensor, Wq: torch.Tensor, acc=None, workspace=None
                                _stream(stream))
     _check("w8a8_matmul_i32", rc)
     return acc
+
+
+def awq_channel_scales(Xcal: torch.Tensor, alpha=(1, 2), s=None, stream=None) -> torch.Tensor:
+    """Calibration activations [M, K] fp32 -> power-of-two channel scales s [K]."""
+    M, K = Xcal.shape
+    if s is None:
+        s = torch.empty((K,), dtype=torch.float32, device=Xcal.device)
+    rc = lib().awq_channel_scales(_dev(Xcal, "Xcal", torch.float32), M, K, int(alpha[0]),
+                                  int(alpha[1]), _dev(s, "s", torch.float32), _stream(stream))
+    _check("awq_channel_scales", rc)
+    return s
+
+
+def awq_fold_weight(W: torch.Tensor, s: torch.Tensor, W_out=None, stream=None) -> torch.Tensor:
+    """W [K, N] -> W diag(s) (W_out may be W)."""
+    K, N = W.shape
+    if W_out is None:
+        W_out = torch.empty_like(W)
+    rc = lib().awq_fold_weight(_dev(W, "W", torch.float32), K, N, _dev(s, "s", torch.float32),
+                               _dev(W_out, "W_out", torch.float32), _stream(stream))
+    _check("awq_fold_weight", rc)
+    return W_out
+
+
+def awq_quantize_act(X: torch.Tensor, s: torch.Tensor, Xq=None, sx=None, stream=None):
+    """(Xq, sx) of X / s (per column)."""
+    M, K = X.shape
+    if Xq is None:
+        Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if sx is None:
+        sx = torch.empty((M,), dtype=torch.float32, device=X.device)
+    rc = lib().awq_quantize_act(_dev(X, "X", torch.float32), M, K, _dev(s, "s", torch.float32),
+                                _dev(Xq, "Xq", torch.int8), _dev(sx, "sx", torch.float32),
+                                _stream(stream))
+    _check("awq_quantize_act", rc)
+    return Xq, sx
+
+
+def awq_scale_act_bf16(X_bf16: torch.Tensor, s: torch.Tensor, X_out=None, stream=None):
+    """bf16 (or int16 bit-pattern) activations divided by s per column."""
+    M, K = X_bf16.shape
+    if X_out is None:
+        X_out = torch.empty_like(X_bf16)
+    dt = X_bf16.dtype
+    rc = lib().awq_scale_act_bf16(_dev(X_bf16, "X_bf16", dt), M, K, _dev(s, "s", torch.float32),
+                                  _dev(X_out, "X_out", dt), _stream(stream))
+    _check("awq_scale_act_bf16", rc)
+    return X_out
+
+
+def w4a8_linear_awq(X: torch.Tensor, packed: torch.Tensor, sw: torch.Tensor, s: torch.Tensor,
+                    bias=None, activation=None, Y=None, workspace=None,
+                    stream=None) -> torch.Tensor:
+    """Y = act(dequant(quant(X / s) . unpack(packed)) (+ bias)); packed, sw from W diag(s)."""
+    M, K = X.shape
+    N = packed.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    workspace, need = _workspace(M, K, N, X.device, workspace)
+    rc = lib().w4a8_linear_awq(_dev(X, "X", torch.float32), M, K, N,
+                               _dev(packed, "packed", torch.uint8), _dev(sw, "sw", torch.float32),
+                               _dev(s, "s", torch.float32), _opt(bias, "bias", torch.float32),
+                               _act(activation), _dev(Y, "Y", torch.float32),
+                               _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                               _stream(stream))
+    _check("w4a8_linear_awq", rc)
+    return Y
 
 
 def w4a16_linear(X_bf16: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,

@@ -39,11 +39,13 @@ enum class Src { FP32, Q };
 int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const float *sx,
                   const uint8_t *packed, const float *sw, const float *bias, int64_t M,
                   int64_t K, int64_t N, float *Y, int32_t *acc, void *workspace,
-                  size_t workspace_bytes, hipStream_t st, bool relu = false) {
+                  size_t workspace_bytes, hipStream_t st, bool relu = false,
+                  const float *act_div = nullptr) {
     using namespace w4;
     W4A8Args a{};
     a.w8 = w8;
     a.relu = relu;
+    a.act_div = act_div;
     a.X = nullptr;
     a.Xq = Xq;
     a.sx = sx;
@@ -74,7 +76,7 @@ int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const floa
     // layout for 8-bit weights, which then use pre-quantized input as is).
     if (fast) {
         if (src == Src::FP32) {
-            e = launch_quant_act(X, M, K, ws_q, ws_s, !w8, st);
+            e = launch_quant_act(X, M, K, ws_q, ws_s, !w8, st, act_div);
             if (e != hipSuccess) return W4_ERR_HIP;
             a.sx = ws_s;
             a.Xq = ws_q;
@@ -92,7 +94,7 @@ int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const floa
     }
     // Anything else: natural layout, one thread per output.
     if (src == Src::FP32) {
-        e = launch_quant_act(X, M, K, ws_q, ws_s, false, st);
+        e = launch_quant_act(X, M, K, ws_q, ws_s, false, st, act_div);
         if (e != hipSuccess) return W4_ERR_HIP;
         a.Xq = ws_q;
         a.sx = ws_s;
@@ -250,6 +252,63 @@ int w4a8_linear_act(const float *X, int64_t M, int64_t K, int64_t N, const uint8
     return w4a8_dispatch(Src::FP32, false, X, nullptr, nullptr, packed, sw, bias, M, K, N, Y,
                          nullptr, workspace, workspace_bytes,
                          reinterpret_cast<hipStream_t>(stream), activation == W4_ACT_RELU);
+}
+
+int w4a8_linear_awq(const float *X, int64_t M, int64_t K, int64_t N, const uint8_t *packed,
+                    const float *sw, const float *s, const float *bias, int activation, float *Y,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    if (!X || !packed || !sw || !s || !Y) return W4_ERR_NULL;
+    if (!shape_ok(M, K, N)) return W4_ERR_SHAPE;
+    if (activation != W4_ACT_NONE && activation != W4_ACT_RELU) return W4_ERR_ARG;
+    if (!aligned(X, 4) || !aligned(sw, 4) || !aligned(Y, 4) || (bias && !aligned(bias, 4)))
+        return W4_ERR_ALIGN;
+    if (!aligned(s, 16)) return W4_ERR_ALIGN;
+    int rc = check_workspace(M, K, workspace, workspace_bytes);
+    if (rc != W4_OK) return rc;
+    return w4a8_dispatch(Src::FP32, false, X, nullptr, nullptr, packed, sw, bias, M, K, N, Y,
+                         nullptr, workspace, workspace_bytes,
+                         reinterpret_cast<hipStream_t>(stream), activation == W4_ACT_RELU, s);
+}
+
+int awq_channel_scales(const float *Xcal, int64_t M, int64_t K, int alpha_num, int alpha_den,
+                       float *s, void *stream) {
+    if (!Xcal || !s) return W4_ERR_NULL;
+    if (M < 1 || K < 1 || K > W4_MAX_K || M > ((int64_t)1 << 40) / K) return W4_ERR_SHAPE;
+    if (alpha_num < 0 || alpha_num > 1024 || alpha_den < 1 || alpha_den > 1024) return W4_ERR_ARG;
+    if (!aligned(Xcal, 4) || !aligned(s, 4)) return W4_ERR_ALIGN;
+    g_last_path = "awq_scales";
+    return hip_status(w4::launch_awq_scales(Xcal, M, K, alpha_num, alpha_den, s,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+int awq_fold_weight(const float *W, int64_t K, int64_t N, const float *s, float *W_out,
+                    void *stream) {
+    if (!W || !s || !W_out) return W4_ERR_NULL;
+    if (!shape_ok(1, K, N)) return W4_ERR_SHAPE;
+    if (!aligned(W, 4) || !aligned(s, 4) || !aligned(W_out, 4)) return W4_ERR_ALIGN;
+    g_last_path = "awq_fold";
+    return hip_status(
+        w4::launch_awq_fold(W, K, N, s, W_out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int awq_quantize_act(const float *X, int64_t M, int64_t K, const float *s, int8_t *Xq, float *sx,
+                     void *stream) {
+    if (!X || !s || !Xq || !sx) return W4_ERR_NULL;
+    if (M < 1 || K < 1 || M > 0x7FFFFFFF || K > ((int64_t)1 << 40) / M) return W4_ERR_SHAPE;
+    if (!aligned(X, 4) || !aligned(sx, 4) || !aligned(s, 4)) return W4_ERR_ALIGN;
+    g_last_path = "awq_quant_act";
+    return hip_status(w4::launch_quant_act(X, M, K, Xq, sx, false,
+                                           reinterpret_cast<hipStream_t>(stream), s));
+}
+
+int awq_scale_act_bf16(const uint16_t *X_bf16, int64_t M, int64_t K, const float *s,
+                       uint16_t *X_out, void *stream) {
+    if (!X_bf16 || !s || !X_out) return W4_ERR_NULL;
+    if (M < 1 || K < 1 || K > ((int64_t)1 << 40) / M) return W4_ERR_SHAPE;
+    if (!aligned(X_bf16, 2) || !aligned(X_out, 2) || !aligned(s, 4)) return W4_ERR_ALIGN;
+    g_last_path = "awq_scale_bf16";
+    return hip_status(w4::launch_awq_scale_bf16(X_bf16, M, K, s, X_out,
+                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
 int w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N, const uint8_t *packed,

@@ -36,7 +36,10 @@ bool gemv_dot4_ok(int64_t M, int64_t K, bool w8) {
     return M >= 1 && M <= 4 && K % 32 == 0 && K <= (w8 ? kDot4MaxKW8 : kDot4MaxK);
 }
 
-template <int M, int ROWS, int UB, bool FUSED, Out OUT, bool W8>
+// DIV (with FUSED): the activations are divided by per-column divisors
+// (a.act_div) before their quantization -- the activation side of AWQ-style
+// channel scaling.
+template <int M, int ROWS, int UB, bool FUSED, Out OUT, bool W8, bool DIV = false>
 __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
     constexpr int T = 16 * ROWS;  // threads
     constexpr int KPC = W8 ? 16 : 32;  // codes per 16-byte chunk
@@ -53,6 +56,7 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
 
     // (1) activations: group g = t + T*i holds k = 8g .. 8g+7 of each row.
     float4 xa[M][NG], xb[M][NG];
+    float4 da[DIV ? NG : 1], db[DIV ? NG : 1];
     uint2 xn[M][NG];
     if (FUSED) {
         const auto rx = make_rsrc(a.X, (int64_t)M * K * 4);
@@ -65,6 +69,17 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
                 xa[m][i] = bloadf4(rx, off);
                 xb[m][i] = bloadf4(rx, off + 16);
             }
+        if (DIV) {
+            // divisors of the thread's 8-groups (out-of-range groups read 0
+            // and are replaced by 1 where they are used)
+            const auto rd = make_rsrc(a.act_div, (int64_t)K * 4);
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                const int g = t + T * i;
+                da[i] = bloadf4(rd, g < G8 ? 32 * g : kOOB);
+                db[i] = bloadf4(rd, g < G8 ? 32 * g + 16 : kOOB);
+            }
+        }
     } else {
         const auto rq = make_rsrc(a.Xq, (int64_t)M * K);
 #pragma unroll
@@ -97,6 +112,23 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
 
     // (3) activations -> int8 P8 layout in LDS, scales in registers.
     float sxm[M];
+    if (FUSED && DIV) {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            if (t + T * i >= G8) da[i] = db[i] = float4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                xa[m][i].x = xa[m][i].x / da[i].x;
+                xa[m][i].y = xa[m][i].y / da[i].y;
+                xa[m][i].z = xa[m][i].z / da[i].z;
+                xa[m][i].w = xa[m][i].w / da[i].w;
+                xb[m][i].x = xb[m][i].x / db[i].x;
+                xb[m][i].y = xb[m][i].y / db[i].y;
+                xb[m][i].z = xb[m][i].z / db[i].z;
+                xb[m][i].w = xb[m][i].w / db[i].w;
+            }
+        }
+    }
     if (FUSED) {
 #pragma unroll
         for (int m = 0; m < M; ++m) {
@@ -231,6 +263,9 @@ static void go_dot4(const W4A8Args &a, hipStream_t st) {
     if (a.out == Out::I32)
         launch_main(k_gemv_dot4<M, ROWS, UB, false, Out::I32, W8>, grid, dim3(16 * ROWS), shm, st,
                     a);
+    else if (a.X && a.act_div)
+        launch_main(k_gemv_dot4<M, ROWS, UB, true, Out::Y, W8, true>, grid, dim3(16 * ROWS), shm,
+                    st, a);
     else if (a.X)
         launch_main(k_gemv_dot4<M, ROWS, UB, true, Out::Y, W8>, grid, dim3(16 * ROWS), shm, st, a);
     else

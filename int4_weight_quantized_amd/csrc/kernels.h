@@ -45,6 +45,7 @@ struct W4A8Args {
     Out out;
     bool w8;    // 8-bit weight codes (W8A8): natural-layout activations, no unpacking
     bool relu;  // ReLU after dequantization and bias (Out::Y only)
+    const float *act_div;  // per-column divisors of X before quantization (AWQ), or NULL
 };
 
 hipError_t launch_quant_weight_sym(const float *W, int64_t K, int64_t N, uint8_t *packed,
@@ -58,8 +59,17 @@ hipError_t launch_quant_weight_asym(const float *W, int64_t K, int64_t N, int64_
 hipError_t launch_dequant_weight(const uint8_t *packed, const float *scales, const float *zeros,
                                  int64_t K, int64_t N, int64_t group, const float *delta,
                                  float *W, hipStream_t st);
+// div (nullable): per-column divisors applied before quantization (AWQ).
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx, bool p8,
-                            hipStream_t st);
+                            hipStream_t st, const float *div = nullptr);
+// AWQ-style channel scaling: power-of-two scales from calibration rows, the
+// weight fold W diag(s) and the bf16 activation division.
+hipError_t launch_awq_scales(const float *Xcal, int64_t M, int64_t K, int num, int den, float *s,
+                             hipStream_t st);
+hipError_t launch_awq_fold(const float *W, int64_t K, int64_t N, const float *s, float *Wout,
+                           hipStream_t st);
+hipError_t launch_awq_scale_bf16(const uint16_t *X, int64_t M, int64_t K, const float *s,
+                                 uint16_t *Xout, hipStream_t st);
 hipError_t launch_to_p8(const int8_t *Xq, int64_t M, int64_t K, int8_t *out, hipStream_t st);
 
 // M <= 4, K % 32 == 0, K <= 8192 (4096 for 8-bit weights), 16-byte aligned: VALU

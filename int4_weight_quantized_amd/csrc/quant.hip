@@ -309,23 +309,38 @@ hipError_t launch_quant_weight_asym(const float *W, int64_t K, int64_t N, int64_
 // One block (256 threads) per row.  Pass 1: absmax; pass 2: codes, 8 per
 // thread-step (re-reading the row from cache).  P8 = true writes the P8 layout
 // (requires K % 8 == 0), otherwise the natural layout.
-template <bool P8>
+// With DIV the row is first divided by a per-column divisor, x' = fl(x / div[k])
+// (the activation side of AWQ-style channel scaling, "INT4" concept entry 4.4).
+template <bool P8, bool DIV>
 __global__ __launch_bounds__(256) void k_quant_act(const float *__restrict__ X, int64_t K,
                                                    int8_t *__restrict__ Xq,
-                                                   float *__restrict__ sx) {
+                                                   float *__restrict__ sx,
+                                                   const float *__restrict__ div) {
     __shared__ float red[4];
     const int64_t m = blockIdx.x;
     const float *row = X + m * K;
-    const bool vec = ((K % 4) == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+    const bool vec = ((K % 4) == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0) &&
+                     (!DIV || (reinterpret_cast<uintptr_t>(div) & 15) == 0);
+    auto dv4 = [&](float4 v, int64_t k0) {
+        if (DIV) {
+            const float4 d = *reinterpret_cast<const float4 *>(div + k0);
+            v.x = v.x / d.x;
+            v.y = v.y / d.y;
+            v.z = v.z / d.z;
+            v.w = v.w / d.w;
+        }
+        return v;
+    };
+    auto ld = [&](int64_t k) { return DIV ? row[k] / div[k] : row[k]; };
     float a = 0.0f;
     if (vec) {
         const float4 *r4 = reinterpret_cast<const float4 *>(row);
         for (int64_t i = threadIdx.x; i < K / 4; i += 256) {
-            float4 v = r4[i];
+            float4 v = dv4(r4[i], 4 * i);
             a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
         }
     } else {
-        for (int64_t i = threadIdx.x; i < K; i += 256) a = fmaxf(a, fabsf(row[i]));
+        for (int64_t i = threadIdx.x; i < K; i += 256) a = fmaxf(a, fabsf(ld(i)));
     }
     a = block_max(a, red);
     const float s = (a == 0.0f) ? 0.0f : a / 127.0f;
@@ -337,8 +352,8 @@ __global__ __launch_bounds__(256) void k_quant_act(const float *__restrict__ X, 
             const int64_t k0 = g * 8;
             int q[8];
             if (vec && k0 + 8 <= K) {
-                const float4 v0 = reinterpret_cast<const float4 *>(row + k0)[0];
-                const float4 v1 = reinterpret_cast<const float4 *>(row + k0)[1];
+                const float4 v0 = dv4(reinterpret_cast<const float4 *>(row + k0)[0], k0);
+                const float4 v1 = dv4(reinterpret_cast<const float4 *>(row + k0)[1], k0 + 4);
                 q[0] = code(v0.x);
                 q[1] = code(v0.y);
                 q[2] = code(v0.z);
@@ -349,7 +364,7 @@ __global__ __launch_bounds__(256) void k_quant_act(const float *__restrict__ X, 
                 q[7] = code(v1.w);
             } else {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) q[j] = (k0 + j < K) ? code(row[k0 + j]) : 0;
+                for (int j = 0; j < 8; ++j) q[j] = (k0 + j < K) ? code(ld(k0 + j)) : 0;
             }
             if (P8) {
                 uint2 v;
@@ -375,11 +390,113 @@ __global__ __launch_bounds__(256) void k_quant_act(const float *__restrict__ X, 
 }
 
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx, bool p8,
-                            hipStream_t st) {
-    if (p8)
-        hipLaunchKernelGGL(k_quant_act<true>, dim3((unsigned)M), dim3(256), 0, st, X, K, Xq, sx);
-    else
-        hipLaunchKernelGGL(k_quant_act<false>, dim3((unsigned)M), dim3(256), 0, st, X, K, Xq, sx);
+                            hipStream_t st, const float *div) {
+    const dim3 g((unsigned)M), b(256);
+    if (div) {
+        if (p8)
+            hipLaunchKernelGGL((k_quant_act<true, true>), g, b, 0, st, X, K, Xq, sx, div);
+        else
+            hipLaunchKernelGGL((k_quant_act<false, true>), g, b, 0, st, X, K, Xq, sx, div);
+    } else {
+        if (p8)
+            hipLaunchKernelGGL((k_quant_act<true, false>), g, b, 0, st, X, K, Xq, sx, div);
+        else
+            hipLaunchKernelGGL((k_quant_act<false, false>), g, b, 0, st, X, K, Xq, sx, div);
+    }
+    return hipGetLastError();
+}
+
+// ------------------------------------------ AWQ-style channel scaling
+// ("INT4" concept entry, section 4.4.)  Channel magnitude a_k = max over the
+// calibration rows of |x| (the column-absmax pass above, with the rows of Xcal
+// as its K); E_k = floor(log2 a_k) from the fp32 encoding (-150 for a_k = 0);
+// E_med = the lower median of E over the channels; s_k = 2^e_k with
+// e_k = min(24, max(0, floor(alpha (E_k - E_med)))).  One block: an LDS
+// histogram of E (278 bins), a serial scan for the median, then the scales.
+__device__ __forceinline__ int floor_log2_bits(uint32_t b) {
+    const uint32_t ex = (b >> 23) & 0xFF, man = b & 0x7FFFFF;
+    if (ex) return (int)ex - 127;
+    if (man) return (31 - __builtin_clz(man)) - 149;  // subnormal
+    return -150;                                     // zero
+}
+
+__global__ __launch_bounds__(1024) void k_awq_scales(uint32_t *__restrict__ amax_to_s,
+                                                     int64_t K, int num, int den) {
+    constexpr int kBins = 278;  // E in [-150, 127]
+    __shared__ int hist[kBins];
+    __shared__ int med;
+    for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    for (int64_t k = threadIdx.x; k < K; k += blockDim.x)
+        atomicAdd(&hist[floor_log2_bits(amax_to_s[k]) + 150], 1);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int64_t t = (K - 1) / 2;  // 0-based rank of the lower median
+        int64_t c = 0;
+        int b = 0;
+        for (; b < kBins; ++b) {
+            c += hist[b];
+            if (c > t) break;
+        }
+        med = b - 150;
+    }
+    __syncthreads();
+    for (int64_t k = threadIdx.x; k < K; k += blockDim.x) {
+        const int d = floor_log2_bits(amax_to_s[k]) - med;
+        int e = d > 0 ? (d * num) / den : 0;
+        e = e > 24 ? 24 : e;
+        amax_to_s[k] = (uint32_t)(127 + e) << 23;
+    }
+}
+
+hipError_t launch_awq_scales(const float *Xcal, int64_t M, int64_t K, int num, int den, float *s,
+                             hipStream_t st) {
+    uint32_t *amax = reinterpret_cast<uint32_t *>(s);
+    absmax_pass(Xcal, M, K, amax, st);
+    hipLaunchKernelGGL(k_awq_scales, dim3(1), dim3(1024), 0, st, amax, K, num, den);
+    return hipGetLastError();
+}
+
+// W'[k][n] = fl(W[k][n] * s[k]) (in place allowed).
+__global__ void k_awq_fold(const float *__restrict__ W, int64_t K, int64_t N,
+                           const float *__restrict__ s, float *__restrict__ Wout) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < K * N; i += stride)
+        Wout[i] = W[i] * s[i / N];
+}
+
+static unsigned stride_blocks(int64_t n) {
+    const int64_t b = (n + 255) / 256;
+    return (unsigned)(b < (1 << 20) ? b : (1 << 20));
+}
+
+hipError_t launch_awq_fold(const float *W, int64_t K, int64_t N, const float *s, float *Wout,
+                           hipStream_t st) {
+    hipLaunchKernelGGL(k_awq_fold, dim3(stride_blocks(K * N)), dim3(256), 0, st, W, K, N, s, Wout);
+    return hipGetLastError();
+}
+
+// bf16 activations divided by s: bf16_rne(fl(float(x) / s[k])).
+__global__ void k_awq_scale_bf16(const uint16_t *__restrict__ X, int64_t M, int64_t K,
+                                 const float *__restrict__ s, uint16_t *__restrict__ Xout) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < M * K; i += stride) {
+        const float x = __uint_as_float((uint32_t)X[i] << 16);
+        const float v = x / s[i % K];
+        uint32_t u = __float_as_uint(v);
+        if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) {
+            Xout[i] = (uint16_t)((u >> 16) | 0x0040u);  // NaN stays a quiet NaN
+            continue;
+        }
+        u += 0x7FFFu + ((u >> 16) & 1u);
+        Xout[i] = (uint16_t)(u >> 16);
+    }
+}
+
+hipError_t launch_awq_scale_bf16(const uint16_t *X, int64_t M, int64_t K, const float *s,
+                                 uint16_t *Xout, hipStream_t st) {
+    hipLaunchKernelGGL(k_awq_scale_bf16, dim3(stride_blocks(M * K)), dim3(256), 0, st, X, M, K, s,
+                       Xout);
     return hipGetLastError();
 }
 

@@ -43,7 +43,8 @@ def test_header_declares_the_boundary():
                  "w4a8_linear_q", "w4a8_matmul_i32", "w4a8_workspace_bytes",
                  "w8_quantize_weight", "w8a8_workspace_bytes", "w8a8_linear",
                  "w8a8_matmul_i32", "w4a8_linear_act", "w8a8_linear_act",
-                 "w4_dequantize_weight", "w4_merge_delta",
+                 "w4_dequantize_weight", "w4_merge_delta", "awq_channel_scales",
+                 "awq_fold_weight", "awq_quantize_act", "awq_scale_act_bf16", "w4a8_linear_awq",
                  "w4_status_string", "w4_last_path"]:
         assert want in names, names
 
@@ -165,6 +166,25 @@ def test_dequant_merge_checks(w4):
     assert m(FAKE, FAKE, FAKE, 256, 4, 1, 128, FAKE, FAKE, FAKE, None, FAKE, None) == W4_ERR_NULL
     assert m(FAKE, FAKE, None, 4, 4, 0, 0, FAKE, FAKE, FAKE, None, FAKE + 1, None) == W4_ERR_ALIGN
     assert m(FAKE, FAKE, None, 4, 4, 9, 0, FAKE, FAKE, FAKE, None, FAKE, None) == W4_ERR_SCHEME
+
+
+def test_awq_checks(w4):
+    L = w4.lib()
+    assert L.awq_channel_scales(None, 4, 8, 1, 2, FAKE, None) == W4_ERR_NULL
+    assert L.awq_channel_scales(FAKE, 0, 8, 1, 2, FAKE, None) == W4_ERR_SHAPE
+    assert L.awq_channel_scales(FAKE, 4, 8, 1, 0, FAKE, None) == W4_ERR_ARG
+    assert L.awq_channel_scales(FAKE, 4, 8, -1, 2, FAKE, None) == W4_ERR_ARG
+    assert L.awq_channel_scales(FAKE, 4, 8, 1, 2, FAKE + 2, None) == W4_ERR_ALIGN
+    assert L.awq_fold_weight(FAKE, 4, 8, None, FAKE, None) == W4_ERR_NULL
+    assert L.awq_fold_weight(FAKE, 4, 0, FAKE, FAKE, None) == W4_ERR_SHAPE
+    assert L.awq_quantize_act(FAKE, 2, 8, None, FAKE, FAKE, None) == W4_ERR_NULL
+    assert L.awq_scale_act_bf16(FAKE + 1, 2, 8, FAKE, FAKE, None) == W4_ERR_ALIGN
+    ws = w4.w4a8_workspace_bytes(2, 64, 8)
+    f = L.w4a8_linear_awq
+    assert f(FAKE, 2, 64, 8, FAKE, FAKE, None, None, 0, FAKE, FAKE, ws, None) == W4_ERR_NULL
+    assert f(FAKE, 2, 64, 8, FAKE, FAKE, FAKE + 4, None, 0, FAKE, FAKE, ws, None) == W4_ERR_ALIGN
+    assert f(FAKE, 2, 64, 8, FAKE, FAKE, FAKE, None, 5, FAKE, FAKE, ws, None) == W4_ERR_ARG
+    assert f(FAKE, 2, 64, 8, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, 0, None) == W4_ERR_WORKSPACE
 
 
 def test_w4a16_checks(w4):
