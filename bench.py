@@ -18,8 +18,10 @@ Also reported in the same line:
                 the kernel's dispatch) against the 8 TB/s HBM peak;
   parts         the other workloads (Gemma M=8, 7B-class M=1/16/64, the
                 4096^3 prefill in int8 TOPS, the same layers with int8
-                weights (W8A8), the 70B-class W4A16 layer) and the weight
-                quantizers, each with per-kernel durations;
+                weights (W8A8), 7B-class decode with AWQ-style channel
+                scaling, the 70B-class W4A16 layer, and the offline weight
+                transforms: dequantization, LoRA merge, AWQ fold) and the
+                weight quantizers, each with per-kernel durations;
   cpu_baseline  the CPU oracle on a bounded sample of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-parts]
@@ -136,6 +138,72 @@ class W4A8Case:
         c = i % self.copies
         f = self.w4.w8a8_linear if self.w8 else self.w4.w4a8_linear
         f(self.x, self.P[c], self.S[c], Y=self.y, workspace=self.ws)
+
+
+class AwqCase(W4A8Case):
+    """A W4A8 layer with AWQ-style channel scaling: scales from the layer's
+    own input rows (alpha 1/4), weights quantized from W diag(s), the
+    division by s fused into the activation quantization."""
+
+    def __init__(self, w4, torch, name, shape_name, M):
+        import workloads
+        super().__init__(w4, torch, name, shape_name, M)
+        dev = torch.device("cuda")
+        self.s = w4.awq_channel_scales(self.x, (1, 4))
+        W = torch.from_numpy(workloads.generate(shape_name, M=M)["W"]).to(dev)
+        p, sw, _ = w4.w4_quantize_weight(w4.awq_fold_weight(W, self.s), "sym")
+        del W
+        self.P = [p] + [p.clone() for _ in range(self.copies - 1)]
+        self.S = [sw] + [sw.clone() for _ in range(self.copies - 1)]
+        self.bytes += 4 * self.K  # the channel scales
+
+    def step(self, i):
+        c = i % self.copies
+        self.w4.w4a8_linear_awq(self.x, self.P[c], self.S[c], self.s, Y=self.y, workspace=self.ws)
+
+
+def offline_parts(w4, torch, hip):
+    """Offline weight transforms on the 7B-class layer [4096, 11008], timed with
+    events: dequantization, the LoRA merge (dequantize + add delta + requantize)
+    and the AWQ fold; each reads / writes the fp32 weights once or twice."""
+    import workloads
+    dev = torch.device("cuda")
+    d = workloads.generate("mlp7b", M=1)
+    W = torch.from_numpy(d["W"]).to(dev)
+    K, N = W.shape
+    p, s, _ = w4.w4_quantize_weight(W, "sym")
+    delta = torch.randn(K, 16, device=dev) @ torch.randn(16, N, device=dev) * 1e-3
+    work = torch.empty_like(W)
+    Wd = torch.empty_like(W)
+    po, so = torch.empty_like(p), torch.empty_like(s)
+    sc = torch.ones(K, device=dev)
+
+    def timed(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        a, b = hip.event(), hip.event()
+        st = torch.cuda.current_stream().cuda_stream
+        hip.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.h.hipEventRecord(a, st)
+        for _ in range(reps):
+            fn()
+        hip.h.hipEventRecord(b, st)
+        ms = hip.elapsed_ms(a, b) / reps
+        hip.destroy(a)
+        hip.destroy(b)
+        return ms
+
+    fp32 = 4 * K * N
+    res = []
+    ms = timed(lambda: w4.w4_dequantize_weight(p, s, None, K, "sym", W=Wd))
+    res.append({"workload": "dequant_weight_7b", "ms": round(ms, 4),
+                "GBps": round((fp32 + p.numel() + 4 * N) / ms / 1e6, 1)})
+    ms = timed(lambda: w4.w4_merge_delta(p, s, None, delta, "sym", work=work))
+    res.append({"workload": "lora_merge_7b", "ms": round(ms, 4),
+                "note": "dequantize + add delta (one kernel), then absmax, codes, scales"})
+    ms = timed(lambda: w4.awq_fold_weight(W, sc, W_out=Wd))
+    res.append({"workload": "awq_fold_7b", "ms": round(ms, 4), "GBps": round(2 * fp32 / ms / 1e6, 1)})
+    return res
 
 
 class W4A16Case:
@@ -364,6 +432,23 @@ def main():
         w4a8_part("w8a8_mlp7b_m1", "mlp7b", 1, "hbm", w8=True)
         w4a8_part("w8a8_mlp7b_m16", "mlp7b", 16, "hbm", w8=True)
         w4a8_part("w8a8_prefill_4096", "prefill", None, "mfma", rotate=False, w8=True)
+        for name, M in (("awq_mlp7b_m1", 1), ("awq_mlp7b_m16", 16)):
+            log(f"part: {name}")
+            c = AwqCase(w4, torch, name, "mlp7b", M)
+            st = graph_step_time(torch, c, 200, 10)
+            p = w4.w4_last_path()
+            ka, km = kernel_time(torch, hip, w4, c, 100)
+            parts.append({"workload": name, "M": c.M, "K": c.K, "N": c.N, "product_kernel": p,
+                          "step_us": round(st * 1e6, 3), "kernel_us_avg": round(ka * 1e6, 3),
+                          "algorithmic_bytes": c.bytes,
+                          "GBps_kernel": round(c.bytes / ka / 1e9, 1),
+                          "GBps_step": round(c.bytes / st / 1e9, 1),
+                          "frac_hbm_kernel": round(c.bytes / ka / 1e9 / HBM_PEAK_GBS, 4),
+                          "rotating_weight_copies": c.copies})
+            del c
+            torch.cuda.empty_cache()
+        log("part: offline weight transforms")
+        parts.extend(offline_parts(w4, torch, hip))
         log("part: w4a16_70b_m16")
         c = W4A16Case(w4, torch)
         st = graph_step_time(torch, c, 50, 5)
