@@ -14,6 +14,8 @@ arrays.  The formulas and their sources are documented there:
 * the toy model's ReLU on a Dense output (after the bias);
 * weight dequantization and the lossy LoRA merge (dequantize, add the delta,
   requantize) -- Keras guide, "Limitations";
+* the GPU-shuffled ("prepacked") W4A16 layout and its inverse -- a pure
+  rearrangement, defined here (the pages fix no such layout);
 * AWQ-style activation-aware channel scaling (calibration magnitudes ->
   power-of-two channel scales, W diag(s), x / s) -- "INT4" concept entry,
   section 4.4;
@@ -68,6 +70,8 @@ def _load():
             "orc_matmul_w8_i32": [_P, _P, _I, _I, _I, _P],
             "orc_w8a8_linear": [_P, _I, _I, _I, _P, _P, _P, _P],
             "orc_relu": [_P, _I],
+            "orc_w4a16_prepack": [_P, _P, _P, _I, _I, _P, _P],
+            "orc_w4a16_unprepack": [_P, _P, _I, _I, _P, _P, _P],
             "orc_awq_channel_scales": [_P, _I, _I, ctypes.c_int, ctypes.c_int, _P],
             "orc_awq_scale_bf16": [_P, _I, _I, _P, _P],
             "orc_awq_fold_weight": [_P, _I, _I, _P, _P],
@@ -313,6 +317,29 @@ def merge_delta(packed, scales, zeros, K: int, delta: np.ndarray, group: int = 0
                                    _ptr(None if zeros is None else _f32(zeros)), K, N, group,
                                    _ptr(delta), _ptr(po), _ptr(so), _ptr(zo)), "merge_delta")
     return po, so, zo
+
+
+def w4a16_prepack(packed, scales, zeros, K: int):
+    """Canonical W4A16 tensors -> (wpp uint8 [N16/16, K/128, 16, 64], szpp fp32 [N16/16, K/256, 16, 4])."""
+    packed = np.ascontiguousarray(packed, np.uint8)
+    N = packed.shape[0]
+    nb = (N + 15) // 16
+    wpp = np.zeros((nb, K // 128, 16, 64), np.uint8)
+    szpp = np.zeros((nb, K // 256, 16, 4), np.float32)
+    _check(_load().orc_w4a16_prepack(_ptr(packed), _ptr(_f32(scales)), _ptr(_f32(zeros)), K, N,
+                                     _ptr(wpp), _ptr(szpp)), "w4a16_prepack")
+    return wpp, szpp
+
+
+def w4a16_unprepack(wpp, szpp, K: int, N: int):
+    """Inverse of w4a16_prepack on the first N channels."""
+    packed = np.zeros((N, K // 2), np.uint8)
+    scales = np.zeros((N, K // 128), np.float32)
+    zeros = np.zeros((N, K // 128), np.float32)
+    _check(_load().orc_w4a16_unprepack(_ptr(np.ascontiguousarray(wpp, np.uint8)),
+                                       _ptr(_f32(szpp)), K, N, _ptr(packed), _ptr(scales),
+                                       _ptr(zeros)), "w4a16_unprepack")
+    return packed, scales, zeros
 
 
 def bf16_rne(x: np.ndarray) -> np.ndarray:

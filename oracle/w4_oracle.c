@@ -466,6 +466,66 @@ int orc_merge_delta(const uint8_t *packed, const float *scales, const float *zer
     return rc;
 }
 
+/* A second, GPU-shuffled layout of the W4A16 weights (the survey's
+ * "prepacked" format; the pages define none, they only pack two codes per
+ * byte).  It is a pure rearrangement of the canonical packed bytes and group
+ * tables, defined for group 128, K % 512 == 0; channels are padded to
+ * N16 = 16 * ceil(N / 16) with zero bytes / zero table entries:
+ *   wpp [N16/16][K/128][16][64] bytes:
+ *     wpp[b][t][c][16 p + i] = packed[16 b + c][64 t + 16 (p ^ ((c / 2) % 4)) + i]
+ *   szpp [N16/16][K/256][16][4] fp32:
+ *     szpp[b][u][c] = { scales[n][2u], zeros[n][2u], scales[n][2u+1], zeros[n][2u+1] },
+ *     n = 16 b + c.
+ * orc_w4a16_unprepack is the inverse on the first N channels. */
+int orc_w4a16_prepack(const uint8_t *packed, const float *scales, const float *zeros, int64_t K,
+                      int64_t N, uint8_t *wpp, float *szpp) {
+    if (K < 1 || N < 1 || K % 512 != 0) return ORC_ERR_SHAPE;
+    const int64_t KB = K / 2, S = K / 128, G = K / 128, NB = (N + 15) / 16;
+    for (int64_t b = 0; b < NB; ++b)
+        for (int64_t t = 0; t < S; ++t)
+            for (int64_t c = 0; c < 16; ++c) {
+                const int64_t n = 16 * b + c;
+                for (int64_t p = 0; p < 4; ++p)
+                    for (int64_t i = 0; i < 16; ++i) {
+                        const int64_t chunk = p ^ ((c / 2) % 4);
+                        uint8_t v = 0;
+                        if (n < N) v = packed[n * KB + 64 * t + 16 * chunk + i];
+                        wpp[((b * S + t) * 16 + c) * 64 + 16 * p + i] = v;
+                    }
+            }
+    for (int64_t b = 0; b < NB; ++b)
+        for (int64_t u = 0; u < G / 2; ++u)
+            for (int64_t c = 0; c < 16; ++c) {
+                const int64_t n = 16 * b + c;
+                float *e = szpp + ((b * (G / 2) + u) * 16 + c) * 4;
+                e[0] = n < N ? scales[n * G + 2 * u] : 0.0f;
+                e[1] = n < N ? zeros[n * G + 2 * u] : 0.0f;
+                e[2] = n < N ? scales[n * G + 2 * u + 1] : 0.0f;
+                e[3] = n < N ? zeros[n * G + 2 * u + 1] : 0.0f;
+            }
+    return ORC_OK;
+}
+
+int orc_w4a16_unprepack(const uint8_t *wpp, const float *szpp, int64_t K, int64_t N,
+                        uint8_t *packed, float *scales, float *zeros) {
+    if (K < 1 || N < 1 || K % 512 != 0) return ORC_ERR_SHAPE;
+    const int64_t KB = K / 2, S = K / 128, G = K / 128;
+    for (int64_t n = 0; n < N; ++n) {
+        const int64_t b = n / 16, c = n % 16;
+        for (int64_t k2 = 0; k2 < KB; ++k2) {
+            const int64_t t = k2 / 64, chunk = (k2 % 64) / 16, i = k2 % 16;
+            const int64_t p = chunk ^ ((c / 2) % 4);
+            packed[n * KB + k2] = wpp[((b * S + t) * 16 + c) * 64 + 16 * p + i];
+        }
+        for (int64_t g = 0; g < G; ++g) {
+            const float *e = szpp + ((b * (G / 2) + g / 2) * 16 + c) * 4;
+            scales[n * G + g] = e[2 * (g % 2)];
+            zeros[n * G + g] = e[2 * (g % 2) + 1];
+        }
+    }
+    return ORC_OK;
+}
+
 /* Round-to-nearest-even of an fp32 value to the bf16 format (the upper 16 bits
  * of the fp32 encoding).  NaN is kept quiet. */
 uint16_t orc_bf16_rne(float f) {

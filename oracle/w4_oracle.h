@@ -112,6 +112,15 @@ int orc_merge_delta(const uint8_t *packed, const float *scales, const float *zer
                     int64_t K, int64_t N, int64_t group, const float *delta,
                     uint8_t *packed_out, float *scales_out, float *zeros_out);
 
+/* GPU-shuffled W4A16 layout (group 128, K % 512 == 0, channels padded to a
+ * multiple of 16): wpp [N16/16][K/128][16][64] bytes with 16-byte chunk p of
+ * channel c holding canonical chunk p ^ ((c/2) % 4); szpp [N16/16][K/256][16][4]
+ * fp32 = (scale, zero) of groups 2u and 2u+1. */
+int orc_w4a16_prepack(const uint8_t *packed, const float *scales, const float *zeros, int64_t K,
+                      int64_t N, uint8_t *wpp, float *szpp);
+int orc_w4a16_unprepack(const uint8_t *wpp, const float *szpp, int64_t K, int64_t N,
+                        uint8_t *packed, float *scales, float *zeros);
+
 /* fp32 -> bf16 round-half-to-even (bit pattern). */
 uint16_t orc_bf16_rne(float f);
 
