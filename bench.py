@@ -213,7 +213,10 @@ def offline_parts(w4, torch, hip):
 
 
 class W4A16Case:
-    def __init__(self, w4, torch, copies=None):
+    """The 70B-class W4A16 layer; with prepacked=True the weights and tables
+    are converted once (offline) to the GPU-shuffled layout."""
+
+    def __init__(self, w4, torch, copies=None, prepacked=False):
         import numpy as np
         import workloads
         d = workloads.w4a16_inputs()
@@ -230,16 +233,25 @@ class W4A16Case:
         del W
         wbytes = p.numel() + 8 * s.numel()
         self.copies = copies or max(1, math.ceil(ROTATE_BYTES / wbytes))
+        self.prepacked = prepacked
+        if prepacked:
+            self.name = "w4a16_70b_m16_prepacked"
+            p, s = w4.w4a16_prepack(p, s, z)
+            z = None
+            torch.cuda.synchronize()
         self.P = [p] + [p.clone() for _ in range(self.copies - 1)]
         self.Sc = [s] + [s.clone() for _ in range(self.copies - 1)]
-        self.Z = [z] + [z.clone() for _ in range(self.copies - 1)]
+        self.Z = [z] * self.copies if z is None else [z] + [z.clone() for _ in range(self.copies - 1)]
         self.y = torch.empty((self.M, self.N), dtype=torch.float32, device=dev)
         self.bytes = w4a16_bytes(self.M, self.K, self.N, self.g)
         self.ops = 2 * self.M * self.N * self.K
 
     def step(self, i):
         c = i % self.copies
-        self.w4.w4a16_linear(self.x, self.P[c], self.Sc[c], self.Z[c], self.g, Y=self.y)
+        if self.prepacked:
+            self.w4.w4a16_linear_prepacked(self.x, self.P[c], self.Sc[c], self.N, Y=self.y)
+        else:
+            self.w4.w4a16_linear(self.x, self.P[c], self.Sc[c], self.Z[c], self.g, Y=self.y)
 
 
 def graph_step_time(torch, case, steps, warmup, hip=None):
@@ -346,7 +358,8 @@ def main():
     ap.add_argument("--no-parts", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None,
                     help="run one workload's product kernel (for profilers): gemma_m1, gemma_m8, "
-                         "mlp7b_m1, mlp7b_m16, mlp7b_m64, prefill, w4a16, w8a8_gemma_m1, "
+                         "mlp7b_m1, mlp7b_m16, mlp7b_m64, prefill, w4a16, w4a16_prepacked, "
+                         "w8a8_gemma_m1, "
                          "w8a8_mlp7b_m1, w8a8_prefill; or copy (a 64 MiB device copy, for "
                          "counter calibration)")
     ap.add_argument("--launches", type=int, default=200)
@@ -381,8 +394,11 @@ def main():
                  "prefill": ("prefill", None)}
         w8 = args.only.startswith("w8a8_")
         key = args.only[5:] if w8 else args.only
-        case = (W4A16Case(w4, torch, copies=args.copies) if args.only == "w4a16"
-                else W4A8Case(w4, torch, args.only, *specs[key], copies=args.copies, w8=w8))
+        if args.only.startswith("w4a16"):
+            case = W4A16Case(w4, torch, copies=args.copies,
+                             prepacked=args.only == "w4a16_prepacked")
+        else:
+            case = W4A8Case(w4, torch, args.only, *specs[key], copies=args.copies, w8=w8)
         for i in range(args.warmup + args.steps):
             case.step(i)
         torch.cuda.synchronize()
@@ -475,22 +491,23 @@ def main():
             torch.cuda.empty_cache()
         log("part: offline weight transforms")
         parts.extend(offline_parts(w4, torch, hip))
-        log("part: w4a16_70b_m16")
-        c = W4A16Case(w4, torch)
-        st = graph_step_time(torch, c, 50, 5)
-        p = w4.w4_last_path()
-        ka, km = kernel_time(torch, hip, w4, c, 50)
-        parts.append({"workload": c.name, "M": c.M, "K": c.K, "N": c.N, "group": c.g,
-                      "product_kernel": p, "step_us": round(st * 1e6, 3),
-                      "kernel_us_avg": round(ka * 1e6, 3), "algorithmic_bytes": c.bytes,
-                      "GBps_kernel": round(c.bytes / ka / 1e9, 1),
-                      "GBps_step": round(c.bytes / st / 1e9, 1),
-                      "frac_hbm_kernel": round(c.bytes / ka / 1e9 / HBM_PEAK_GBS, 4),
-                      "TFLOPS_kernel": round(c.ops / ka / 1e12, 2),
-                      "rotating_weight_copies": c.copies,
-                      "weight_quantize_ms": round(c.quant_s * 1e3, 3)})
-        del c
-        torch.cuda.empty_cache()
+        for pp in (False, True):
+            log(f"part: w4a16_70b_m16{' prepacked' if pp else ''}")
+            c = W4A16Case(w4, torch, prepacked=pp)
+            st = graph_step_time(torch, c, 50, 5)
+            p = w4.w4_last_path()
+            ka, km = kernel_time(torch, hip, w4, c, 50)
+            parts.append({"workload": c.name, "M": c.M, "K": c.K, "N": c.N, "group": c.g,
+                          "product_kernel": p, "step_us": round(st * 1e6, 3),
+                          "kernel_us_avg": round(ka * 1e6, 3), "algorithmic_bytes": c.bytes,
+                          "GBps_kernel": round(c.bytes / ka / 1e9, 1),
+                          "GBps_step": round(c.bytes / st / 1e9, 1),
+                          "frac_hbm_kernel": round(c.bytes / ka / 1e9 / HBM_PEAK_GBS, 4),
+                          "TFLOPS_kernel": round(c.ops / ka / 1e12, 2),
+                          "rotating_weight_copies": c.copies,
+                          "weight_quantize_ms": round(c.quant_s * 1e3, 3)})
+            del c
+            torch.cuda.empty_cache()
         pre = [p for p in parts if p["workload"] == "prefill_4096"][0]
         out["prefill_int8"] = {"metric": "int8 TOPS (M=4096 prefill GEMM)",
                                "TOPS_kernel": pre["TOPS_kernel"], "TOPS_step": pre["TOPS_step"],

@@ -270,6 +270,42 @@ int w4a16_linear(const uint16_t *X_bf16, int64_t M, int64_t K, int64_t N,
                  const uint8_t *packed, const float *scales, const float *zeros,
                  int64_t group_size, float *Y, void *stream);
 
+/* ---- A second, GPU-shuffled layout of the W4A16 weights (group 128,
+ * K % 512 == 0).  The pages only pack two codes per byte; this layout is a
+ * pure rearrangement of the canonical arrays into the order the W4A16
+ * kernel consumes them, so that every load reads contiguous bytes:
+ *   wpp  [N16/16][K/128][16][64] bytes, N16 = 16 * ceil(N / 16):
+ *        wpp[b][t][c][16 p + i] = packed[16 b + c][64 t + 16 (p ^ ((c / 2) % 4)) + i]
+ *        (zero bytes for the padding channels N .. N16 - 1);
+ *   szpp [N16/16][K/256][16][4] fp32:
+ *        szpp[b][u][c] = (scales[n][2u], zeros[n][2u], scales[n][2u+1], zeros[n][2u+1]),
+ *        n = 16 b + c (zeros for padding channels).
+ * w4a16_unprepack inverts it exactly (round-trip identity on the first N
+ * channels).  All arrays are device memory; wpp, szpp and packed 16-byte
+ * aligned.  group_size must be 128 and K % 512 == 0, else W4_ERR_SHAPE. */
+
+/* Sizes of the shuffled arrays (bytes of wpp, floats of szpp); 0 when the
+ * shape is not supported. */
+int64_t w4a16_prepacked_weight_bytes(int64_t K, int64_t N);
+int64_t w4a16_prepacked_table_floats(int64_t K, int64_t N);
+
+/* Canonical (packed [N][K/2], scales, zeros [N][K/128]) -> (wpp, szpp).
+ * Returns W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN or W4_ERR_HIP. */
+int w4a16_prepack(const uint8_t *packed, const float *scales, const float *zeros,
+                  int64_t K, int64_t N, int64_t group_size, uint8_t *wpp, float *szpp,
+                  void *stream);
+
+/* (wpp, szpp) -> the canonical arrays of the first N channels. */
+int w4a16_unprepack(const uint8_t *wpp, const float *szpp, int64_t K, int64_t N,
+                    int64_t group_size, uint8_t *packed, float *scales, float *zeros,
+                    void *stream);
+
+/* w4a16_linear on the shuffled layout: the same products in the same order
+ * (bit-identical outputs), with contiguous weight and table loads.  X_bf16
+ * 16-byte aligned.  Returns as w4a16_linear. */
+int w4a16_linear_prepacked(const uint16_t *X_bf16, int64_t M, int64_t K, int64_t N,
+                           const uint8_t *wpp, const float *szpp, float *Y, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *w4_status_string(int status);
 

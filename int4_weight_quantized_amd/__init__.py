@@ -19,6 +19,8 @@ functions carry the C names:
 * ``w8a8_linear_act``     -- the same with a fused activation (ReLU);
 * ``w8a8_matmul_i32``     -- its exact int32 accumulators alone;
 * ``w4a16_linear``        -- the weight-only forward with bf16 activations;
+* ``w4a16_prepack``, ``w4a16_unprepack``, ``w4a16_linear_prepacked`` -- the
+  GPU-shuffled W4A16 layout, its inverse and the forward on it;
 * ``awq_channel_scales``, ``awq_fold_weight``, ``awq_quantize_act``,
   ``awq_scale_act_bf16``, ``w4a8_linear_awq`` -- AWQ-style activation-aware
   channel scaling (power-of-two scales from calibration activations).
@@ -78,6 +80,11 @@ def lib():
             "w4a8_matmul_i32": ([_P, _P, _I, _I, _I, _P, _P, _Z, _P], ctypes.c_int),
             "w4a16_linear": ([_P, _I, _I, _I, _P, _P, _P, _I, _P, _P], ctypes.c_int),
             "w8_quantize_weight": ([_P, _I, _I, _P, _P, _P], ctypes.c_int),
+            "w4a16_prepacked_weight_bytes": ([_I, _I], ctypes.c_int64),
+            "w4a16_prepacked_table_floats": ([_I, _I], ctypes.c_int64),
+            "w4a16_prepack": ([_P, _P, _P, _I, _I, _I, _P, _P, _P], ctypes.c_int),
+            "w4a16_unprepack": ([_P, _P, _I, _I, _I, _P, _P, _P, _P], ctypes.c_int),
+            "w4a16_linear_prepacked": ([_P, _I, _I, _I, _P, _P, _P, _P], ctypes.c_int),
             "awq_channel_scales": ([_P, _I, _I, ctypes.c_int, ctypes.c_int, _P, _P], ctypes.c_int),
             "awq_fold_weight": ([_P, _I, _I, _P, _P, _P], ctypes.c_int),
             "awq_quantize_act": ([_P, _I, _I, _P, _P, _P, _P], ctypes.c_int),
@@ -439,6 +446,55 @@ def w4a8_linear_awq(X: torch.Tensor, packed: torch.Tensor, sw: torch.Tensor, s: 
                                _dev(workspace, "workspace", torch.uint8), workspace.numel(),
                                _stream(stream))
     _check("w4a8_linear_awq", rc)
+    return Y
+
+
+def w4a16_prepack(packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                  group_size: int = 128, stream=None):
+    """Canonical W4A16 tensors -> (wpp uint8, szpp fp32), the GPU-shuffled layout."""
+    N, KB = packed.shape
+    K = 2 * KB
+    nw = int(lib().w4a16_prepacked_weight_bytes(K, N))
+    nt = int(lib().w4a16_prepacked_table_floats(K, N))
+    if nw == 0 or group_size != 128:
+        raise ValueError("the shuffled layout needs group_size 128 and K % 512 == 0")
+    wpp = torch.empty((nw,), dtype=torch.uint8, device=packed.device)
+    szpp = torch.empty((nt,), dtype=torch.float32, device=packed.device)
+    rc = lib().w4a16_prepack(_dev(packed, "packed", torch.uint8),
+                             _dev(scales, "scales", torch.float32),
+                             _dev(zeros, "zeros", torch.float32), K, N, group_size,
+                             _dev(wpp, "wpp", torch.uint8), _dev(szpp, "szpp", torch.float32),
+                             _stream(stream))
+    _check("w4a16_prepack", rc)
+    return wpp, szpp
+
+
+def w4a16_unprepack(wpp: torch.Tensor, szpp: torch.Tensor, K: int, N: int,
+                    group_size: int = 128, stream=None):
+    """(wpp, szpp) -> canonical (packed [N, K/2], scales, zeros [N, K/128])."""
+    dev = wpp.device
+    packed = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, K // 128), dtype=torch.float32, device=dev)
+    zeros = torch.empty((N, K // 128), dtype=torch.float32, device=dev)
+    rc = lib().w4a16_unprepack(_dev(wpp, "wpp", torch.uint8), _dev(szpp, "szpp", torch.float32),
+                               K, N, group_size, _dev(packed, "packed", torch.uint8),
+                               _dev(scales, "scales", torch.float32),
+                               _dev(zeros, "zeros", torch.float32), _stream(stream))
+    _check("w4a16_unprepack", rc)
+    return packed, scales, zeros
+
+
+def w4a16_linear_prepacked(X_bf16: torch.Tensor, wpp: torch.Tensor, szpp: torch.Tensor, N: int,
+                           Y=None, stream=None) -> torch.Tensor:
+    """The W4A16 forward on the shuffled layout; X_bf16 [M, K] bf16 / 16-bit patterns."""
+    M, K = X_bf16.shape
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X_bf16.device)
+    rc = lib().w4a16_linear_prepacked(_dev(X_bf16, "X_bf16", X_bf16.dtype), M, K, N,
+                                      _dev(wpp, "wpp", torch.uint8),
+                                      _dev(szpp, "szpp", torch.float32),
+                                      _dev(Y, "Y", torch.float32), _stream(stream))
+    _check("w4a16_linear_prepacked", rc)
     return Y
 
 

@@ -393,6 +393,56 @@ int w8a8_matmul_i32(const int8_t *Xq, const int8_t *Wq, int64_t M, int64_t K, in
                          reinterpret_cast<hipStream_t>(stream));
 }
 
+static bool prepacked_shape_ok(int64_t K, int64_t N, int64_t group_size) {
+    return group_size == 128 && K % 512 == 0 && shape_ok(1, K, N);
+}
+
+int64_t w4a16_prepacked_weight_bytes(int64_t K, int64_t N) {
+    if (!prepacked_shape_ok(K, N, 128)) return 0;
+    return ((N + 15) / 16) * 16 * (K / 2);
+}
+
+int64_t w4a16_prepacked_table_floats(int64_t K, int64_t N) {
+    if (!prepacked_shape_ok(K, N, 128)) return 0;
+    return ((N + 15) / 16) * 16 * (K / 128) * 2;
+}
+
+int w4a16_prepack(const uint8_t *packed, const float *scales, const float *zeros, int64_t K,
+                  int64_t N, int64_t group_size, uint8_t *wpp, float *szpp, void *stream) {
+    if (!packed || !scales || !zeros || !wpp || !szpp) return W4_ERR_NULL;
+    if (!prepacked_shape_ok(K, N, group_size)) return W4_ERR_SHAPE;
+    if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(zeros, 4) || !aligned(wpp, 16) ||
+        !aligned(szpp, 16))
+        return W4_ERR_ALIGN;
+    g_last_path = "w4a16_prepack";
+    return hip_status(w4::launch_w4a16_prepack(packed, scales, zeros, K, N, wpp, szpp,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+int w4a16_unprepack(const uint8_t *wpp, const float *szpp, int64_t K, int64_t N,
+                    int64_t group_size, uint8_t *packed, float *scales, float *zeros,
+                    void *stream) {
+    if (!packed || !scales || !zeros || !wpp || !szpp) return W4_ERR_NULL;
+    if (!prepacked_shape_ok(K, N, group_size)) return W4_ERR_SHAPE;
+    if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(zeros, 4) || !aligned(wpp, 16) ||
+        !aligned(szpp, 16))
+        return W4_ERR_ALIGN;
+    g_last_path = "w4a16_unprepack";
+    return hip_status(w4::launch_w4a16_unprepack(wpp, szpp, K, N, packed, scales, zeros,
+                                                 reinterpret_cast<hipStream_t>(stream)));
+}
+
+int w4a16_linear_prepacked(const uint16_t *X_bf16, int64_t M, int64_t K, int64_t N,
+                           const uint8_t *wpp, const float *szpp, float *Y, void *stream) {
+    if (!X_bf16 || !wpp || !szpp || !Y) return W4_ERR_NULL;
+    if (!shape_ok(M, K, N) || !prepacked_shape_ok(K, N, 128)) return W4_ERR_SHAPE;
+    if (!aligned(X_bf16, 16) || !aligned(wpp, 16) || !aligned(szpp, 16) || !aligned(Y, 4))
+        return W4_ERR_ALIGN;
+    g_last_path = "w4a16_lds_prepacked";
+    return hip_status(w4::launch_w4a16_prepacked(X_bf16, M, K, N, wpp, szpp, Y,
+                                                 reinterpret_cast<hipStream_t>(stream)));
+}
+
 int w4a16_linear(const uint16_t *X_bf16, int64_t M, int64_t K, int64_t N, const uint8_t *packed,
                  const float *scales, const float *zeros, int64_t group_size, float *Y,
                  void *stream) {

@@ -95,6 +95,14 @@ bool w4a16_lds_ok(int64_t K, int64_t group);
 hipError_t launch_w4a16_lds(const uint16_t *X, int64_t M, int64_t K, int64_t N,
                             const uint8_t *packed, const float *scales, const float *zeros,
                             float *Y, hipStream_t st);
+// The same kernel on the GPU-shuffled layout (wpp, szpp from launch_w4a16_prepack).
+hipError_t launch_w4a16_prepacked(const uint16_t *X, int64_t M, int64_t K, int64_t N,
+                                  const uint8_t *wpp, const float *szpp, float *Y,
+                                  hipStream_t st);
+hipError_t launch_w4a16_prepack(const uint8_t *packed, const float *scales, const float *zeros,
+                                int64_t K, int64_t N, uint8_t *wpp, float *szpp, hipStream_t st);
+hipError_t launch_w4a16_unprepack(const uint8_t *wpp, const float *szpp, int64_t K, int64_t N,
+                                  uint8_t *packed, float *scales, float *zeros, hipStream_t st);
 hipError_t launch_w4a16_mfma(const uint16_t *X, int64_t M, int64_t K, int64_t N,
                              const uint8_t *packed, const float *scales, const float *zeros,
                              int64_t group, float *Y, hipStream_t st);

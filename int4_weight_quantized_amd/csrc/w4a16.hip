@@ -271,27 +271,34 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_mfma(const uint16_t *__restric
 constexpr int kLSteps = 2;   // 128-k steps per stage
 constexpr int kLStages = 3;  // ring depth per half
 
-template <int WPH>
+// PP: the weights and tables come in the GPU-shuffled layout (see
+// w4a16_prepack below): per 16-channel block, each 128-k step is 1 KB of
+// weights in the LDS order, and each stage's (scale, zero) pairs of its two
+// groups are 256 contiguous bytes; a stage then needs one table with
+// ceil(WPH / 4) loads instead of two tables of 16-byte pieces.
+template <int WPH, bool PP = false>
 struct W4a16Lds {
     static constexpr int kCh = 16 * WPH;                       // channels per block
     static constexpr int kW = kCh * 64 * kLSteps;              // weight bytes per stage
     static constexpr int kX = 4096 * kLSteps;                  // activation bytes per stage
-    static constexpr int kSZ = ((kCh * 16 + 1023) / 1024) * 1024;  // per table, whole KB
-    static constexpr int kStage = kW + kX + 2 * kSZ;
+    static constexpr int kSZ = PP ? ((WPH + 3) / 4) * 1024     // per table, whole KB
+                                  : ((kCh * 16 + 1023) / 1024) * 1024;
+    static constexpr int kTabs = PP ? 1 : 2;
+    static constexpr int kStage = kW + kX + kTabs * kSZ;
     static constexpr int kLoadsW = kW / 1024, kLoadsX = kX / 1024, kLoadsSZ = kSZ / 1024;
-    static constexpr int kLoads = kLoadsW + kLoadsX + 2 * kLoadsSZ;
+    static constexpr int kLoads = kLoadsW + kLoadsX + kTabs * kLoadsSZ;
     static constexpr int kPerWave = (kLoads + WPH - 1) / WPH;  // every wave issues as many
     static_assert(2 * kLStages * kStage <= 160 * 1024, "ring fits in LDS");
 };
 
-template <int WPH>
+template <int WPH, bool PP>
 __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restrict__ X,
                                                          const uint8_t *__restrict__ packed,
                                                          const float *__restrict__ scales,
                                                          const float *__restrict__ zeros,
                                                          float *__restrict__ Y, int64_t M,
                                                          int64_t K64, int64_t N) {
-    using L = W4a16Lds<WPH>;
+    using L = W4a16Lds<WPH, PP>;
     __shared__ __align__(16) uint8_t ring[2 * kLStages * L::kStage];  // [half][stage]
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int half = wave / WPH, wl = wave % WPH;
@@ -305,10 +312,16 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
 
     // Descriptors cover exactly this block's channels / rows: channels past N
     // and rows past M read zeros (their outputs are not stored).
-    const v4i rw = buffer_desc(packed + n0 * KB, (int64_t)cols * KB);
+    // (Shuffled layout: this block's 16-channel blocks blk0 .. blk0 + nblk - 1.)
+    const int blk0 = (int)blockIdx.x * WPH;
+    const int nblk = (int)min((int64_t)WPH, (N + 15) / 16 - blk0);
+    const v4i rw = PP ? buffer_desc(packed + (int64_t)blk0 * G * 1024, (int64_t)nblk * G * 1024)
+                      : buffer_desc(packed + n0 * KB, (int64_t)cols * KB);
     const v4i rx = buffer_desc(X + m0 * K, (int64_t)rowsm * K * 2);
-    const v4i rs = buffer_desc(scales + n0 * G, (int64_t)cols * G * 4);
-    const v4i rz = buffer_desc(zeros + n0 * G, (int64_t)cols * G * 4);
+    const v4i rs = PP ? buffer_desc(scales + (int64_t)blk0 * (G / 2) * 64,
+                                    (int64_t)nblk * (G / 2) * 256)
+                      : buffer_desc(scales + n0 * G, (int64_t)cols * G * 4);
+    const v4i rz = PP ? rs : buffer_desc(zeros + n0 * G, (int64_t)cols * G * 4);
 
     const int T = G / (2 * kLSteps);    // stages per half
     const int s0 = half * T * kLSteps;  // first step of this half
@@ -331,11 +344,20 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
             const int q = min(wl + WPH * i, L::kLoads - 1);
             if (q < L::kLoadsW) {
                 const int j = q / WPH, c = 16 * (q % WPH) + lane / 4;
-                dma16(rw, base + q * 1024, c * KB + 16 * sw4, (step + j) * 64);
+                if (PP)  // 1 KB of block q % WPH, step + j, already in LDS order
+                    dma16(rw, base + q * 1024, (q % WPH) * G * 1024 + lane * 16, (step + j) * 1024);
+                else
+                    dma16(rw, base + q * 1024, c * KB + 16 * sw4, (step + j) * 64);
             } else if (q < L::kLoadsW + L::kLoadsX) {
                 const int qq = q - L::kLoadsW, j = qq / 4, pk = qq % 4, r = lane / 4;
                 dma16(rx, base + L::kW + qq * 1024, r * K * 2 + 64 * pk + 16 * (sw4 ^ pk),
                       (step + j) * 256);
+            } else if (PP) {
+                // 256 B of (scale, zero) pairs per 16-channel block: lane / 16
+                // picks the block (4 per load), lane % 16 the channel
+                const int qq = q - L::kLoadsW - L::kLoadsX, bq = 4 * qq + lane / 16;
+                dma16(rs, base + L::kW + L::kX + qq * 1024, bq * (G / 2) * 256 + (lane % 16) * 16,
+                      (step / 2) * 256);
             } else {
                 const int qq = q - L::kLoadsW - L::kLoadsX;
                 const int tab = qq / L::kLoadsSZ, part = qq % L::kLoadsSZ;
@@ -353,12 +375,18 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
 
     auto compute = [&](int t) {
         const uint8_t *sb = hbase + (t % kLStages) * L::kStage;
-        // scales / zero points of the quad holding this stage's groups
-        const float4 sc4 = *reinterpret_cast<const float4 *>(sb + L::kW + L::kX + ch * 16);
-        const float4 zp4 = *reinterpret_cast<const float4 *>(sb + L::kW + L::kX + L::kSZ + ch * 16);
-        const int g0 = (s0 + kLSteps * t) % 4;   // 0 or 2
-        const float scs[2] = {g0 ? sc4.z : sc4.x, g0 ? sc4.w : sc4.y};
-        const float zps[2] = {g0 ? zp4.z : zp4.x, g0 ? zp4.w : zp4.y};
+        float scs[2], zps[2];
+        if (PP) {  // (scale, zero) of the stage's two groups
+            const float4 e = *reinterpret_cast<const float4 *>(sb + L::kW + L::kX + ch * 16);
+            scs[0] = e.x, zps[0] = e.y, scs[1] = e.z, zps[1] = e.w;
+        } else {   // scales / zero points of the quad holding this stage's groups
+            const float4 sc4 = *reinterpret_cast<const float4 *>(sb + L::kW + L::kX + ch * 16);
+            const float4 zp4 =
+                *reinterpret_cast<const float4 *>(sb + L::kW + L::kX + L::kSZ + ch * 16);
+            const int g0 = (s0 + kLSteps * t) % 4;  // 0 or 2
+            scs[0] = g0 ? sc4.z : sc4.x, scs[1] = g0 ? sc4.w : sc4.y;
+            zps[0] = g0 ? zp4.z : zp4.x, zps[1] = g0 ? zp4.w : zp4.y;
+        }
         bool ok = true;
 #pragma unroll
         for (int j = 0; j < kLSteps; ++j)
@@ -426,31 +454,117 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
 
 bool w4a16_lds_ok(int64_t K, int64_t group) { return group == 128 && K % (256 * kLSteps) == 0; }
 
-template <int WPH>
+template <int WPH, bool PP>
 static void go_w4a16_lds(const uint16_t *X, int64_t M, int64_t K, int64_t N, const uint8_t *packed,
                          const float *scales, const float *zeros, float *Y, hipStream_t st) {
     const int64_t mblocks = (M + 15) / 16;
     for (int64_t mb0 = 0; mb0 < mblocks; mb0 += 65535) {
         const int64_t cnt = (mblocks - mb0) < 65535 ? (mblocks - mb0) : 65535;
         dim3 grid((unsigned)((N + 16 * WPH - 1) / (16 * WPH)), (unsigned)cnt);
-        launch_main(k_w4a16_lds<WPH>, grid, dim3(128 * WPH), 0, st, X + mb0 * 16 * K, packed,
+        launch_main(k_w4a16_lds<WPH, PP>, grid, dim3(128 * WPH), 0, st, X + mb0 * 16 * K, packed,
                     scales, zeros, Y + mb0 * 16 * N, M - mb0 * 16, K, N);
     }
 }
 
 // Waves per half: enough channels per block that the channel blocks of one
 // 16-row block fit in one round over the 256 CUs (at most 7 waves per half).
-hipError_t launch_w4a16_lds(const uint16_t *X, int64_t M, int64_t K, int64_t N,
-                            const uint8_t *packed, const float *scales, const float *zeros,
-                            float *Y, hipStream_t st) {
+template <bool PP>
+static void go_w4a16_wph(const uint16_t *X, int64_t M, int64_t K, int64_t N, const uint8_t *packed,
+                         const float *scales, const float *zeros, float *Y, hipStream_t st) {
     const int64_t groups16 = (N + 15) / 16;
     const int64_t wph = (groups16 + 255) / 256;
     switch (wph <= 1 ? 1 : wph <= 2 ? 2 : wph <= 4 ? 4 : 7) {
-        case 1: go_w4a16_lds<1>(X, M, K, N, packed, scales, zeros, Y, st); break;
-        case 2: go_w4a16_lds<2>(X, M, K, N, packed, scales, zeros, Y, st); break;
-        case 4: go_w4a16_lds<4>(X, M, K, N, packed, scales, zeros, Y, st); break;
-        default: go_w4a16_lds<7>(X, M, K, N, packed, scales, zeros, Y, st); break;
+        case 1: go_w4a16_lds<1, PP>(X, M, K, N, packed, scales, zeros, Y, st); break;
+        case 2: go_w4a16_lds<2, PP>(X, M, K, N, packed, scales, zeros, Y, st); break;
+        case 4: go_w4a16_lds<4, PP>(X, M, K, N, packed, scales, zeros, Y, st); break;
+        default: go_w4a16_lds<7, PP>(X, M, K, N, packed, scales, zeros, Y, st); break;
     }
+}
+
+hipError_t launch_w4a16_lds(const uint16_t *X, int64_t M, int64_t K, int64_t N,
+                            const uint8_t *packed, const float *scales, const float *zeros,
+                            float *Y, hipStream_t st) {
+    go_w4a16_wph<false>(X, M, K, N, packed, scales, zeros, Y, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a16_prepacked(const uint16_t *X, int64_t M, int64_t K, int64_t N,
+                                  const uint8_t *wpp, const float *szpp, float *Y,
+                                  hipStream_t st) {
+    go_w4a16_wph<true>(X, M, K, N, wpp, szpp, nullptr, Y, st);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------ shuffled-layout conversion
+// wpp[b][t][c][16 p + i] = packed[16 b + c][64 t + 16 (p ^ ((c / 2) % 4)) + i]
+// (zero for padding channels); szpp[b][u][c] = (s, z) of groups 2u, 2u + 1.
+// One thread per 16-byte unit of the destination (prepack) or of the
+// canonical arrays (unprepack).  K % 512 == 0, 16-byte aligned arrays.
+__global__ void k_w4a16_prepack(const uint8_t *__restrict__ packed,
+                                const float *__restrict__ scales,
+                                const float *__restrict__ zeros, int64_t K, int64_t N,
+                                uint8_t *__restrict__ wpp, float *__restrict__ szpp) {
+    const int64_t S = K / 128, KB = K / 2, NB = (N + 15) / 16;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t u = i0; u < NB * S * 64; u += stride) {
+        const int64_t p = u % 4, c = (u / 4) % 16, t = (u / 64) % S, b = u / (64 * S);
+        const int64_t n = 16 * b + c, chunk = p ^ ((c / 2) % 4);
+        uint4 v = {0u, 0u, 0u, 0u};
+        if (n < N) v = *reinterpret_cast<const uint4 *>(packed + n * KB + 64 * t + 16 * chunk);
+        reinterpret_cast<uint4 *>(wpp)[u] = v;
+    }
+    for (int64_t e = i0; e < NB * (S / 2) * 16; e += stride) {
+        const int64_t c = e % 16, uu = (e / 16) % (S / 2), b = e / (16 * (S / 2));
+        const int64_t n = 16 * b + c;
+        float4 v = {0.f, 0.f, 0.f, 0.f};
+        if (n < N)
+            v = float4{scales[n * S + 2 * uu], zeros[n * S + 2 * uu], scales[n * S + 2 * uu + 1],
+                       zeros[n * S + 2 * uu + 1]};
+        reinterpret_cast<float4 *>(szpp)[e] = v;
+    }
+}
+
+__global__ void k_w4a16_unprepack(const uint8_t *__restrict__ wpp,
+                                  const float *__restrict__ szpp, int64_t K, int64_t N,
+                                  uint8_t *__restrict__ packed, float *__restrict__ scales,
+                                  float *__restrict__ zeros) {
+    const int64_t S = K / 128, KB = K / 2;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t u = i0; u < N * (KB / 16); u += stride) {
+        const int64_t n = u / (KB / 16), off = (u % (KB / 16)) * 16;
+        const int64_t b = n / 16, c = n % 16, t = off / 64, chunk = (off % 64) / 16;
+        const int64_t p = chunk ^ ((c / 2) % 4);
+        reinterpret_cast<uint4 *>(packed)[u] =
+            *reinterpret_cast<const uint4 *>(wpp + ((b * S + t) * 16 + c) * 64 + 16 * p);
+    }
+    for (int64_t e = i0; e < N * S; e += stride) {
+        const int64_t n = e / S, g = e % S, b = n / 16, c = n % 16;
+        const float *src = szpp + ((b * (S / 2) + g / 2) * 16 + c) * 4 + 2 * (g % 2);
+        scales[e] = src[0];
+        zeros[e] = src[1];
+    }
+}
+
+static unsigned conv_blocks(int64_t n) {
+    const int64_t b = (n + 255) / 256;
+    return (unsigned)(b < 4096 ? (b > 0 ? b : 1) : 4096);
+}
+
+hipError_t launch_w4a16_prepack(const uint8_t *packed, const float *scales, const float *zeros,
+                                int64_t K, int64_t N, uint8_t *wpp, float *szpp, hipStream_t st) {
+    const int64_t units = ((N + 15) / 16) * (K / 128) * 64;
+    hipLaunchKernelGGL(k_w4a16_prepack, dim3(conv_blocks(units)), dim3(256), 0, st, packed, scales,
+                       zeros, K, N, wpp, szpp);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a16_unprepack(const uint8_t *wpp, const float *szpp, int64_t K, int64_t N,
+                                  uint8_t *packed, float *scales, float *zeros, hipStream_t st) {
+    const int64_t units = N * (K / 32);
+    hipLaunchKernelGGL(k_w4a16_unprepack, dim3(conv_blocks(units)), dim3(256), 0, st, wpp, szpp, K,
+                       N, packed, scales, zeros);
     return hipGetLastError();
 }
 

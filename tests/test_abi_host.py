@@ -45,6 +45,8 @@ def test_header_declares_the_boundary():
                  "w8a8_matmul_i32", "w4a8_linear_act", "w8a8_linear_act",
                  "w4_dequantize_weight", "w4_merge_delta", "awq_channel_scales",
                  "awq_fold_weight", "awq_quantize_act", "awq_scale_act_bf16", "w4a8_linear_awq",
+                 "w4a16_prepack", "w4a16_unprepack", "w4a16_linear_prepacked",
+                 "w4a16_prepacked_weight_bytes", "w4a16_prepacked_table_floats",
                  "w4_status_string", "w4_last_path"]:
         assert want in names, names
 
@@ -185,6 +187,26 @@ def test_awq_checks(w4):
     assert f(FAKE, 2, 64, 8, FAKE, FAKE, FAKE + 4, None, 0, FAKE, FAKE, ws, None) == W4_ERR_ALIGN
     assert f(FAKE, 2, 64, 8, FAKE, FAKE, FAKE, None, 5, FAKE, FAKE, ws, None) == W4_ERR_ARG
     assert f(FAKE, 2, 64, 8, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, 0, None) == W4_ERR_WORKSPACE
+
+
+def test_prepacked_checks(w4):
+    L = w4.lib()
+    assert L.w4a16_prepacked_weight_bytes(8192, 28672) == 28672 * 4096
+    assert L.w4a16_prepacked_weight_bytes(512, 37) == 48 * 256
+    assert L.w4a16_prepacked_table_floats(512, 37) == 48 * 4 * 2
+    assert L.w4a16_prepacked_weight_bytes(256, 16) == 0            # K % 512 != 0
+    p = L.w4a16_prepack
+    assert p(None, FAKE, FAKE, 512, 16, 128, FAKE, FAKE, None) == W4_ERR_NULL
+    assert p(FAKE, FAKE, FAKE, 512, 16, 64, FAKE, FAKE, None) == W4_ERR_SHAPE
+    assert p(FAKE, FAKE, FAKE, 768, 16, 128, FAKE, FAKE, None) == W4_ERR_SHAPE
+    assert p(FAKE + 4, FAKE, FAKE, 512, 16, 128, FAKE, FAKE, None) == W4_ERR_ALIGN
+    u = L.w4a16_unprepack
+    assert u(FAKE, None, 512, 16, 128, FAKE, FAKE, FAKE, None) == W4_ERR_NULL
+    assert u(FAKE, FAKE, 512, 16, 128, FAKE, FAKE, FAKE + 2, None) == W4_ERR_ALIGN
+    f = L.w4a16_linear_prepacked
+    assert f(FAKE, 1, 512, 16, None, FAKE, FAKE, None) == W4_ERR_NULL
+    assert f(FAKE, 1, 384, 16, FAKE, FAKE, FAKE, None) == W4_ERR_SHAPE
+    assert f(FAKE + 2, 1, 512, 16, FAKE, FAKE, FAKE, None) == W4_ERR_ALIGN
 
 
 def test_w4a16_checks(w4):
