@@ -75,13 +75,15 @@ int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const floa
     // Activations for the MFMA paths: P8 layout in the workspace (natural
     // layout for 8-bit weights, which then use pre-quantized input as is).
     if (fast) {
+        // the MFMA GEMV takes the codes chunk-major, the GEMM row-major
+        const bool step = M <= 64;
         if (src == Src::FP32) {
-            e = launch_quant_act(X, M, K, ws_q, ws_s, !w8, st, act_div);
+            e = launch_quant_act(X, M, K, ws_q, ws_s, !w8, st, act_div, step);
             if (e != hipSuccess) return W4_ERR_HIP;
             a.sx = ws_s;
             a.Xq = ws_q;
-        } else if (!w8) {
-            e = launch_to_p8(Xq, M, K, ws_q, st);
+        } else if (!w8 || step) {
+            e = launch_to_p8(Xq, M, K, ws_q, st, !w8, step);
             if (e != hipSuccess) return W4_ERR_HIP;
             a.Xq = ws_q;
         }

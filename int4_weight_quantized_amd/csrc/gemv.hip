@@ -315,7 +315,10 @@ hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st) {
 // decode-batch layer has few output-channel blocks.
 // Per 128-k step a lane loads 16 packed bytes (32 codes) of one channel:
 //   lane l: channel n0 + 16*nb + l%16, codes k = 128*s + 32*(l/16) + [0, 32)
-// and the matching 2 x 16 P8 activation bytes of row 16*mb + l%16, which
+// and the matching 2 x 16 P8 activation bytes of row 16*mb + l%16 (the
+// activations are stored chunk-major, so one load reads 16 consecutive rows
+// x 16 bytes of four chunks; rows past M read other chunks' rows or zeros
+// and only feed outputs that are not stored), which
 // feed two v_mfma_i32_16x16x64_i8 (the first 16 and the last 16 codes of each
 // lane).  The weight and activation operands use identical k slots per lane,
 // so the order in which the MFMA consumes the slots does not matter.
@@ -351,7 +354,9 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) boff[nb] = (16 * nb + r16) * KB + kq * 16 * WL;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) aoff[mb] = (16 * mb + r16) * K + kq * 32;
+    for (int mb = 0; mb < MB; ++mb) aoff[mb] = (2 * kq * (int)M + 16 * mb + r16) * 16;
+    // activations are chunk-major, [K/16][M][16]: chunk c = 8 s + 2 kq + half
+    const int achunk = (int)M * 16, astep = 8 * achunk;
 
     v4i acc[MB][NB];
 #pragma unroll
@@ -369,9 +374,9 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args a) {
                 wr[d][nb][h] = bload16(rb, ok ? boff[nb] + 64 * WL * ss + 16 * h : kOOB);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const int o = ok ? aoff[mb] + 128 * ss : kOOB;
+            const int o = ok ? aoff[mb] + astep * ss : kOOB;
             xr0[d][mb] = bload16(ra, o);
-            xr1[d][mb] = bload16(ra, o + 16);
+            xr1[d][mb] = bload16(ra, ok ? o + achunk : kOOB);
         }
     };
 #pragma unroll

@@ -60,8 +60,9 @@ hipError_t launch_dequant_weight(const uint8_t *packed, const float *scales, con
                                  int64_t K, int64_t N, int64_t group, const float *delta,
                                  float *W, hipStream_t st);
 // div (nullable): per-column divisors applied before quantization (AWQ).
+// step (K % 16 == 0): codes stored chunk-major [K/16][M][16] for the MFMA GEMV.
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx, bool p8,
-                            hipStream_t st, const float *div = nullptr);
+                            hipStream_t st, const float *div = nullptr, bool step = false);
 // AWQ-style channel scaling: power-of-two scales from calibration rows, the
 // weight fold W diag(s) and the bf16 activation division.
 hipError_t launch_awq_scales(const float *Xcal, int64_t M, int64_t K, int num, int den, float *s,
@@ -70,7 +71,9 @@ hipError_t launch_awq_fold(const float *W, int64_t K, int64_t N, const float *s,
                            hipStream_t st);
 hipError_t launch_awq_scale_bf16(const uint16_t *X, int64_t M, int64_t K, const float *s,
                                  uint16_t *Xout, hipStream_t st);
-hipError_t launch_to_p8(const int8_t *Xq, int64_t M, int64_t K, int8_t *out, hipStream_t st);
+// Natural int8 [M][K] -> P8 (p8) and / or chunk-major (step) order.
+hipError_t launch_to_p8(const int8_t *Xq, int64_t M, int64_t K, int8_t *out, hipStream_t st,
+                        bool p8 = true, bool step = false);
 
 // M <= 4, K % 32 == 0, K <= 8192 (4096 for 8-bit weights), 16-byte aligned: VALU
 // dot4 GEMV.  Uses a.X (fused quantization prologue) when non-NULL, else a.Xq
@@ -78,7 +81,8 @@ hipError_t launch_to_p8(const int8_t *Xq, int64_t M, int64_t K, int8_t *out, hip
 bool gemv_dot4_ok(int64_t M, int64_t K, bool w8);
 hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st);
 
-// M <= 64, K % 128 == 0: MFMA GEMV; a.Xq in P8 layout (natural for 8-bit weights).
+// M <= 64, K % 128 == 0: MFMA GEMV; a.Xq chunk-major [K/16][M][16], P8 order
+// inside (natural for 8-bit weights).
 hipError_t launch_gemv_mfma(const W4A8Args &a, hipStream_t st);
 
 // Any M, K % 128 == 0: LDS-tiled MFMA GEMM; a.Xq in P8 layout (natural for

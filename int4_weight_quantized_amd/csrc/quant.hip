@@ -311,7 +311,11 @@ hipError_t launch_quant_weight_asym(const float *W, int64_t K, int64_t N, int64_
 // (requires K % 8 == 0), otherwise the natural layout.
 // With DIV the row is first divided by a per-column divisor, x' = fl(x / div[k])
 // (the activation side of AWQ-style channel scaling, "INT4" concept entry 4.4).
-template <bool P8, bool DIV>
+// STEP (K % 16 == 0): the codes are stored chunk-major, [K/16][M][16] (the 16
+// codes of one 16-k chunk of all rows together), the order in which the MFMA
+// GEMV loads them: one load instruction reads 16 consecutive rows x 16 bytes
+// of four chunks.
+template <bool P8, bool DIV, bool STEP>
 __global__ __launch_bounds__(256) void k_quant_act(const float *__restrict__ X, int64_t K,
                                                    int8_t *__restrict__ Xq,
                                                    float *__restrict__ sx,
@@ -366,7 +370,18 @@ __global__ __launch_bounds__(256) void k_quant_act(const float *__restrict__ X, 
 #pragma unroll
                 for (int j = 0; j < 8; ++j) q[j] = (k0 + j < K) ? code(ld(k0 + j)) : 0;
             }
-            if (P8) {
+            if (STEP) {
+                uint2 v;
+                if (P8) {
+                    v.x = pack4_i8(q[0], q[2], q[4], q[6]);
+                    v.y = pack4_i8(q[1], q[3], q[5], q[7]);
+                } else {
+                    v.x = pack4_i8(q[0], q[1], q[2], q[3]);
+                    v.y = pack4_i8(q[4], q[5], q[6], q[7]);
+                }
+                const int64_t M = gridDim.x;
+                *reinterpret_cast<uint2 *>(Xq + (k0 / 16) * (M * 16) + m * 16 + k0 % 16) = v;
+            } else if (P8) {
                 uint2 v;
                 v.x = pack4_i8(q[0], q[2], q[4], q[6]);
                 v.y = pack4_i8(q[1], q[3], q[5], q[7]);
@@ -389,19 +404,28 @@ __global__ __launch_bounds__(256) void k_quant_act(const float *__restrict__ X, 
     }
 }
 
-hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx, bool p8,
-                            hipStream_t st, const float *div) {
+template <bool P8, bool STEP>
+static void go_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx,
+                         hipStream_t st, const float *div) {
     const dim3 g((unsigned)M), b(256);
-    if (div) {
+    if (div)
+        hipLaunchKernelGGL((k_quant_act<P8, true, STEP>), g, b, 0, st, X, K, Xq, sx, div);
+    else
+        hipLaunchKernelGGL((k_quant_act<P8, false, STEP>), g, b, 0, st, X, K, Xq, sx, div);
+}
+
+hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx, bool p8,
+                            hipStream_t st, const float *div, bool step) {
+    if (step) {
         if (p8)
-            hipLaunchKernelGGL((k_quant_act<true, true>), g, b, 0, st, X, K, Xq, sx, div);
+            go_quant_act<true, true>(X, M, K, Xq, sx, st, div);
         else
-            hipLaunchKernelGGL((k_quant_act<false, true>), g, b, 0, st, X, K, Xq, sx, div);
+            go_quant_act<false, true>(X, M, K, Xq, sx, st, div);
     } else {
         if (p8)
-            hipLaunchKernelGGL((k_quant_act<true, false>), g, b, 0, st, X, K, Xq, sx, div);
+            go_quant_act<true, false>(X, M, K, Xq, sx, st, div);
         else
-            hipLaunchKernelGGL((k_quant_act<false, false>), g, b, 0, st, X, K, Xq, sx, div);
+            go_quant_act<false, false>(X, M, K, Xq, sx, st, div);
     }
     return hipGetLastError();
 }
@@ -501,19 +525,37 @@ hipError_t launch_awq_scale_bf16(const uint16_t *X, int64_t M, int64_t K, const 
 }
 
 // Natural int8 [M][K] -> P8 layout (K % 8 == 0, 8-byte aligned input).
-__global__ void k_to_p8(const int8_t *__restrict__ in, int64_t total8, int8_t *__restrict__ out) {
+// (With STEP: into the chunk-major order of k_quant_act<.., STEP>; P8 = false
+// only moves the 8-byte groups.)
+template <bool P8, bool STEP>
+__global__ void k_to_p8(const int8_t *__restrict__ in, int64_t M, int64_t K,
+                        int8_t *__restrict__ out) {
+    const int64_t total8 = M * K / 8;
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= total8) return;
     uint2 v = reinterpret_cast<const uint2 *>(in)[i];
-    uint2 r;
-    natural_to_p8(v.x, v.y, r.x, r.y);
-    reinterpret_cast<uint2 *>(out)[i] = r;
+    uint2 r = v;
+    if (P8) natural_to_p8(v.x, v.y, r.x, r.y);
+    if (STEP) {
+        const int64_t m = i / (K / 8), k0 = (i % (K / 8)) * 8;
+        *reinterpret_cast<uint2 *>(out + (k0 / 16) * (M * 16) + m * 16 + k0 % 16) = r;
+    } else {
+        reinterpret_cast<uint2 *>(out)[i] = r;
+    }
 }
 
-hipError_t launch_to_p8(const int8_t *Xq, int64_t M, int64_t K, int8_t *out, hipStream_t st) {
+hipError_t launch_to_p8(const int8_t *Xq, int64_t M, int64_t K, int8_t *out, hipStream_t st,
+                        bool p8, bool step) {
     const int64_t total8 = M * K / 8;
-    hipLaunchKernelGGL(k_to_p8, dim3((unsigned)((total8 + 255) / 256)), dim3(256), 0, st, Xq,
-                       total8, out);
+    const dim3 g((unsigned)((total8 + 255) / 256)), b(256);
+    if (step) {
+        if (p8)
+            hipLaunchKernelGGL((k_to_p8<true, true>), g, b, 0, st, Xq, M, K, out);
+        else
+            hipLaunchKernelGGL((k_to_p8<false, true>), g, b, 0, st, Xq, M, K, out);
+    } else {
+        hipLaunchKernelGGL((k_to_p8<true, false>), g, b, 0, st, Xq, M, K, out);
+    }
     return hipGetLastError();
 }
 
