@@ -71,6 +71,8 @@ def _load():
             "orc_w8a8_linear": [_P, _I, _I, _I, _P, _P, _P, _P],
             "orc_relu": [_P, _I],
             "orc_w4a16_prepack": [_P, _P, _P, _I, _I, _P, _P],
+            "orc_w4_prepack_weights": [_P, _I, _I, _P],
+            "orc_w4_unprepack_weights": [_P, _I, _I, _P],
             "orc_w4a16_unprepack": [_P, _P, _I, _I, _P, _P, _P],
             "orc_awq_channel_scales": [_P, _I, _I, ctypes.c_int, ctypes.c_int, _P],
             "orc_awq_scale_bf16": [_P, _I, _I, _P, _P],
@@ -317,6 +319,22 @@ def merge_delta(packed, scales, zeros, K: int, delta: np.ndarray, group: int = 0
                                    _ptr(None if zeros is None else _f32(zeros)), K, N, group,
                                    _ptr(delta), _ptr(po), _ptr(so), _ptr(zo)), "merge_delta")
     return po, so, zo
+
+
+def w4_prepack_weights(packed, K: int) -> np.ndarray:
+    """Packed int4 codes [N, K/2] -> the shuffled tiles uint8 [N16/16, K/128, 16, 64]."""
+    packed = np.ascontiguousarray(packed, np.uint8)
+    N = packed.shape[0]
+    wpp = np.zeros(((N + 15) // 16, K // 128, 16, 64), np.uint8)
+    _check(_load().orc_w4_prepack_weights(_ptr(packed), K, N, _ptr(wpp)), "w4_prepack_weights")
+    return wpp
+
+
+def w4_unprepack_weights(wpp, K: int, N: int) -> np.ndarray:
+    packed = np.zeros((N, K // 2), np.uint8)
+    _check(_load().orc_w4_unprepack_weights(_ptr(np.ascontiguousarray(wpp, np.uint8)), K, N,
+                                            _ptr(packed)), "w4_unprepack_weights")
+    return packed
 
 
 def w4a16_prepack(packed, scales, zeros, K: int):

@@ -477,10 +477,11 @@ int orc_merge_delta(const uint8_t *packed, const float *scales, const float *zer
  *     szpp[b][u][c] = { scales[n][2u], zeros[n][2u], scales[n][2u+1], zeros[n][2u+1] },
  *     n = 16 b + c.
  * orc_w4a16_unprepack is the inverse on the first N channels. */
-int orc_w4a16_prepack(const uint8_t *packed, const float *scales, const float *zeros, int64_t K,
-                      int64_t N, uint8_t *wpp, float *szpp) {
-    if (K < 1 || N < 1 || K % 512 != 0) return ORC_ERR_SHAPE;
-    const int64_t KB = K / 2, S = K / 128, G = K / 128, NB = (N + 15) / 16;
+/* The weight part alone (also used for the W4A8 symmetric codes), defined
+ * for K % 128 == 0. */
+int orc_w4_prepack_weights(const uint8_t *packed, int64_t K, int64_t N, uint8_t *wpp) {
+    if (K < 1 || N < 1 || K % 128 != 0) return ORC_ERR_SHAPE;
+    const int64_t KB = K / 2, S = K / 128, NB = (N + 15) / 16;
     for (int64_t b = 0; b < NB; ++b)
         for (int64_t t = 0; t < S; ++t)
             for (int64_t c = 0; c < 16; ++c) {
@@ -493,6 +494,29 @@ int orc_w4a16_prepack(const uint8_t *packed, const float *scales, const float *z
                         wpp[((b * S + t) * 16 + c) * 64 + 16 * p + i] = v;
                     }
             }
+    return ORC_OK;
+}
+
+int orc_w4_unprepack_weights(const uint8_t *wpp, int64_t K, int64_t N, uint8_t *packed) {
+    if (K < 1 || N < 1 || K % 128 != 0) return ORC_ERR_SHAPE;
+    const int64_t KB = K / 2, S = K / 128;
+    for (int64_t n = 0; n < N; ++n) {
+        const int64_t b = n / 16, c = n % 16;
+        for (int64_t k2 = 0; k2 < KB; ++k2) {
+            const int64_t t = k2 / 64, chunk = (k2 % 64) / 16, i = k2 % 16;
+            const int64_t p = chunk ^ ((c / 2) % 4);
+            packed[n * KB + k2] = wpp[((b * S + t) * 16 + c) * 64 + 16 * p + i];
+        }
+    }
+    return ORC_OK;
+}
+
+int orc_w4a16_prepack(const uint8_t *packed, const float *scales, const float *zeros, int64_t K,
+                      int64_t N, uint8_t *wpp, float *szpp) {
+    if (K < 1 || N < 1 || K % 512 != 0) return ORC_ERR_SHAPE;
+    const int64_t G = K / 128, NB = (N + 15) / 16;
+    const int rc = orc_w4_prepack_weights(packed, K, N, wpp);
+    if (rc != ORC_OK) return rc;
     for (int64_t b = 0; b < NB; ++b)
         for (int64_t u = 0; u < G / 2; ++u)
             for (int64_t c = 0; c < 16; ++c) {
@@ -509,14 +533,11 @@ int orc_w4a16_prepack(const uint8_t *packed, const float *scales, const float *z
 int orc_w4a16_unprepack(const uint8_t *wpp, const float *szpp, int64_t K, int64_t N,
                         uint8_t *packed, float *scales, float *zeros) {
     if (K < 1 || N < 1 || K % 512 != 0) return ORC_ERR_SHAPE;
-    const int64_t KB = K / 2, S = K / 128, G = K / 128;
+    const int64_t G = K / 128;
+    const int rc = orc_w4_unprepack_weights(wpp, K, N, packed);
+    if (rc != ORC_OK) return rc;
     for (int64_t n = 0; n < N; ++n) {
         const int64_t b = n / 16, c = n % 16;
-        for (int64_t k2 = 0; k2 < KB; ++k2) {
-            const int64_t t = k2 / 64, chunk = (k2 % 64) / 16, i = k2 % 16;
-            const int64_t p = chunk ^ ((c / 2) % 4);
-            packed[n * KB + k2] = wpp[((b * S + t) * 16 + c) * 64 + 16 * p + i];
-        }
         for (int64_t g = 0; g < G; ++g) {
             const float *e = szpp + ((b * (G / 2) + g / 2) * 16 + c) * 4;
             scales[n * G + g] = e[2 * (g % 2)];

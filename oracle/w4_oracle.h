@@ -116,6 +116,10 @@ int orc_merge_delta(const uint8_t *packed, const float *scales, const float *zer
  * multiple of 16): wpp [N16/16][K/128][16][64] bytes with 16-byte chunk p of
  * channel c holding canonical chunk p ^ ((c/2) % 4); szpp [N16/16][K/256][16][4]
  * fp32 = (scale, zero) of groups 2u and 2u+1. */
+/* The weight part of that layout alone (K % 128 == 0), for any packed int4
+ * codes (the W4A8 symmetric ones too), and its inverse. */
+int orc_w4_prepack_weights(const uint8_t *packed, int64_t K, int64_t N, uint8_t *wpp);
+int orc_w4_unprepack_weights(const uint8_t *wpp, int64_t K, int64_t N, uint8_t *packed);
 int orc_w4a16_prepack(const uint8_t *packed, const float *scales, const float *zeros, int64_t K,
                       int64_t N, uint8_t *wpp, float *szpp);
 int orc_w4a16_unprepack(const uint8_t *wpp, const float *szpp, int64_t K, int64_t N,

@@ -67,3 +67,21 @@ def test_rejects_unsupported_k(orc):
     p = np.zeros((16, 128), np.uint8)
     with pytest.raises(orc.OracleError):
         orc.w4a16_prepack(p, np.ones((16, 2), np.float32), np.zeros((16, 2), np.float32), 256)
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (37, 384), (5, 1152), (300, 4096)])
+def test_weights_only_roundtrip_and_agreement(orc, N, K):
+    """The weight part alone: its own round trip for K % 128 == 0, and the same
+    bytes as the full W4A16 conversion where both are defined."""
+    rng = np.random.default_rng(N + K)
+    p = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    wpp = orc.w4_prepack_weights(p, K)
+    assert np.array_equal(orc.w4_unprepack_weights(wpp, K, N), p)
+    per_ch = wpp.transpose(0, 2, 1, 3).reshape(-1, K // 2)
+    for n in range(N):
+        assert np.array_equal(np.sort(per_ch[n]), np.sort(p[n]))
+    assert np.array_equal(wpp[0, K // 128 - 1, 3, 0:16], p[3, K // 2 - 64 + 16:K // 2 - 64 + 32])
+    if K % 512 == 0:
+        s = np.ones((N, K // 128), np.float32)
+        w16, _ = orc.w4a16_prepack(p, s, s, K)
+        assert np.array_equal(w16, wpp)
