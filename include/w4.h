@@ -306,6 +306,25 @@ int w4a16_unprepack(const uint8_t *wpp, const float *szpp, int64_t K, int64_t N,
 int w4a16_linear_prepacked(const uint16_t *X_bf16, int64_t M, int64_t K, int64_t N,
                            const uint8_t *wpp, const float *szpp, float *Y, void *stream);
 
+/* ---- The weight part of the same shuffled layout for the W4A8 int4 codes
+ * (K % 128 == 0): wpp [N16/16][K/128][16][64] exactly as above; the
+ * per-channel scales stay [N].  The product kernels then read every weight
+ * tile as contiguous bytes (the decode-batch kernel one 1 KB tile per load).
+ * Callers: decode / prefill layers whose weights are converted once. */
+int64_t w4_prepacked_weight_bytes(int64_t K, int64_t N);  /* 0 if K % 128 != 0 */
+int w4_prepack_weights(const uint8_t *packed, int64_t K, int64_t N, uint8_t *wpp,
+                       void *stream);
+int w4_unprepack_weights(const uint8_t *wpp, int64_t K, int64_t N, uint8_t *packed,
+                         void *stream);
+
+/* w4a8_linear_act on the shuffled codes: the same products and epilogue
+ * (bit-identical outputs).  K % 128 == 0 (else W4_ERR_SHAPE), wpp 16-byte
+ * aligned; other arguments, workspace and return codes as w4a8_linear_act. */
+int w4a8_linear_prepacked(const float *X, int64_t M, int64_t K, int64_t N,
+                          const uint8_t *wpp, const float *sw, const float *bias,
+                          int activation, float *Y, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *w4_status_string(int status);
 

@@ -21,6 +21,8 @@ functions carry the C names:
 * ``w4a16_linear``        -- the weight-only forward with bf16 activations;
 * ``w4a16_prepack``, ``w4a16_unprepack``, ``w4a16_linear_prepacked`` -- the
   GPU-shuffled W4A16 layout, its inverse and the forward on it;
+* ``w4_prepack_weights``, ``w4_unprepack_weights``, ``w4a8_linear_prepacked``
+  -- the same tile layout for the W4A8 int4 codes and the forward on it;
 * ``awq_channel_scales``, ``awq_fold_weight``, ``awq_quantize_act``,
   ``awq_scale_act_bf16``, ``w4a8_linear_awq`` -- AWQ-style activation-aware
   channel scaling (power-of-two scales from calibration activations).
@@ -81,6 +83,11 @@ def lib():
             "w4a16_linear": ([_P, _I, _I, _I, _P, _P, _P, _I, _P, _P], ctypes.c_int),
             "w8_quantize_weight": ([_P, _I, _I, _P, _P, _P], ctypes.c_int),
             "w4a16_prepacked_weight_bytes": ([_I, _I], ctypes.c_int64),
+            "w4_prepacked_weight_bytes": ([_I, _I], ctypes.c_int64),
+            "w4_prepack_weights": ([_P, _I, _I, _P, _P], ctypes.c_int),
+            "w4_unprepack_weights": ([_P, _I, _I, _P, _P], ctypes.c_int),
+            "w4a8_linear_prepacked": ([_P, _I, _I, _I, _P, _P, _P, ctypes.c_int, _P, _P, _Z, _P],
+                                      ctypes.c_int),
             "w4a16_prepacked_table_floats": ([_I, _I], ctypes.c_int64),
             "w4a16_prepack": ([_P, _P, _P, _I, _I, _I, _P, _P, _P], ctypes.c_int),
             "w4a16_unprepack": ([_P, _P, _I, _I, _I, _P, _P, _P, _P], ctypes.c_int),
@@ -446,6 +453,46 @@ def w4a8_linear_awq(X: torch.Tensor, packed: torch.Tensor, sw: torch.Tensor, s: 
                                _dev(workspace, "workspace", torch.uint8), workspace.numel(),
                                _stream(stream))
     _check("w4a8_linear_awq", rc)
+    return Y
+
+
+def w4_prepack_weights(packed: torch.Tensor, stream=None) -> torch.Tensor:
+    """Packed int4 codes [N, K/2] -> the shuffled tiles (uint8, flat)."""
+    N, KB = packed.shape
+    K = 2 * KB
+    nb = int(lib().w4_prepacked_weight_bytes(K, N))
+    if nb == 0:
+        raise ValueError("the shuffled layout needs K % 128 == 0")
+    wpp = torch.empty((nb,), dtype=torch.uint8, device=packed.device)
+    rc = lib().w4_prepack_weights(_dev(packed, "packed", torch.uint8), K, N,
+                                  _dev(wpp, "wpp", torch.uint8), _stream(stream))
+    _check("w4_prepack_weights", rc)
+    return wpp
+
+
+def w4_unprepack_weights(wpp: torch.Tensor, K: int, N: int, stream=None) -> torch.Tensor:
+    packed = torch.empty((N, K // 2), dtype=torch.uint8, device=wpp.device)
+    rc = lib().w4_unprepack_weights(_dev(wpp, "wpp", torch.uint8), K, N,
+                                    _dev(packed, "packed", torch.uint8), _stream(stream))
+    _check("w4_unprepack_weights", rc)
+    return packed
+
+
+def w4a8_linear_prepacked(X: torch.Tensor, wpp: torch.Tensor, sw: torch.Tensor, bias=None,
+                          activation=None, Y=None, workspace=None, stream=None) -> torch.Tensor:
+    """The W4A8 forward on the shuffled int4 tiles; N = sw.numel()."""
+    M, K = X.shape
+    N = sw.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    workspace, need = _workspace(M, K, N, X.device, workspace)
+    rc = lib().w4a8_linear_prepacked(_dev(X, "X", torch.float32), M, K, N,
+                                     _dev(wpp, "wpp", torch.uint8), _dev(sw, "sw", torch.float32),
+                                     _opt(bias, "bias", torch.float32), _act(activation),
+                                     _dev(Y, "Y", torch.float32),
+                                     _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                                     _stream(stream))
+    _check("w4a8_linear_prepacked", rc)
     return Y
 
 

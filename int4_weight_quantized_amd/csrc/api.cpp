@@ -40,9 +40,10 @@ int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const floa
                   const uint8_t *packed, const float *sw, const float *bias, int64_t M,
                   int64_t K, int64_t N, float *Y, int32_t *acc, void *workspace,
                   size_t workspace_bytes, hipStream_t st, bool relu = false,
-                  const float *act_div = nullptr) {
+                  const float *act_div = nullptr, bool pp = false) {
     using namespace w4;
     W4A8Args a{};
+    a.pp = pp;
     a.w8 = w8;
     a.relu = relu;
     a.act_div = act_div;
@@ -60,7 +61,9 @@ int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const floa
     a.out = acc ? Out::I32 : Out::Y;
 
     const bool aligned16 = aligned(packed, 16) && (src == Src::FP32 ? aligned(X, 16) : aligned(Xq, 16));
-    const bool fast = aligned16 && (K % 128 == 0);
+    // (the shuffled layout is only accepted with K % 128 == 0 and aligned
+    // tiles: the MFMA paths always apply, whatever the alignment of X)
+    const bool fast = pp || (aligned16 && (K % 128 == 0));
     int8_t *ws_q = reinterpret_cast<int8_t *>(workspace);
     float *ws_s = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) +
                                             round_up((size_t)M * (size_t)K, 256));
@@ -69,7 +72,7 @@ int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const floa
     // Few rows: one VALU GEMV launch (activation quantization fused).
     if (aligned16 && gemv_dot4_ok(M, K, w8)) {
         if (src == Src::FP32) a.X = X;
-        g_last_path = w8 ? "w8_gemv_dot4" : "gemv_dot4";
+        g_last_path = w8 ? "w8_gemv_dot4" : pp ? "gemv_dot4_prepacked" : "gemv_dot4";
         return hip_status(launch_gemv_dot4(a, st));
     }
     // Activations for the MFMA paths: P8 layout in the workspace (natural
@@ -88,10 +91,10 @@ int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const floa
             a.Xq = ws_q;
         }
         if (M <= 64) {
-            g_last_path = w8 ? "w8_gemv_mfma" : "gemv_mfma";
+            g_last_path = w8 ? "w8_gemv_mfma" : pp ? "gemv_mfma_prepacked" : "gemv_mfma";
             return hip_status(launch_gemv_mfma(a, st));
         }
-        g_last_path = w8 ? "w8_gemm_mfma" : "gemm_mfma";
+        g_last_path = w8 ? "w8_gemm_mfma" : pp ? "gemm_mfma_prepacked" : "gemm_mfma";
         return hip_status(launch_gemm_mfma(a, st));
     }
     // Anything else: natural layout, one thread per output.
@@ -311,6 +314,46 @@ int awq_scale_act_bf16(const uint16_t *X_bf16, int64_t M, int64_t K, const float
     g_last_path = "awq_scale_bf16";
     return hip_status(w4::launch_awq_scale_bf16(X_bf16, M, K, s, X_out,
                                                 reinterpret_cast<hipStream_t>(stream)));
+}
+
+int64_t w4_prepacked_weight_bytes(int64_t K, int64_t N) {
+    if (!shape_ok(1, K, N) || K % 128 != 0) return 0;
+    return ((N + 15) / 16) * 16 * (K / 2);
+}
+
+int w4_prepack_weights(const uint8_t *packed, int64_t K, int64_t N, uint8_t *wpp, void *stream) {
+    if (!packed || !wpp) return W4_ERR_NULL;
+    if (!shape_ok(1, K, N) || K % 128 != 0) return W4_ERR_SHAPE;
+    if (!aligned(packed, 16) || !aligned(wpp, 16)) return W4_ERR_ALIGN;
+    g_last_path = "w4_prepack_weights";
+    return hip_status(
+        w4::launch_w4_prepack_weights(packed, K, N, wpp, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int w4_unprepack_weights(const uint8_t *wpp, int64_t K, int64_t N, uint8_t *packed, void *stream) {
+    if (!packed || !wpp) return W4_ERR_NULL;
+    if (!shape_ok(1, K, N) || K % 128 != 0) return W4_ERR_SHAPE;
+    if (!aligned(packed, 16) || !aligned(wpp, 16)) return W4_ERR_ALIGN;
+    g_last_path = "w4_unprepack_weights";
+    return hip_status(w4::launch_w4_unprepack_weights(wpp, K, N, packed,
+                                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+int w4a8_linear_prepacked(const float *X, int64_t M, int64_t K, int64_t N, const uint8_t *wpp,
+                          const float *sw, const float *bias, int activation, float *Y,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    if (!X || !wpp || !sw || !Y) return W4_ERR_NULL;
+    if (!shape_ok(M, K, N) || K % 128 != 0) return W4_ERR_SHAPE;
+    if (activation != W4_ACT_NONE && activation != W4_ACT_RELU) return W4_ERR_ARG;
+    if (!aligned(X, 4) || !aligned(sw, 4) || !aligned(Y, 4) || (bias && !aligned(bias, 4)) ||
+        !aligned(wpp, 16))
+        return W4_ERR_ALIGN;
+    int rc = check_workspace(M, K, workspace, workspace_bytes);
+    if (rc != W4_OK) return rc;
+    return w4a8_dispatch(Src::FP32, false, X, nullptr, nullptr, wpp, sw, bias, M, K, N, Y,
+                         nullptr, workspace, workspace_bytes,
+                         reinterpret_cast<hipStream_t>(stream), activation == W4_ACT_RELU,
+                         nullptr, true);
 }
 
 int w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N, const uint8_t *packed,

@@ -44,7 +44,10 @@ struct GemmStage {
     static constexpr int kBytes = kABytes + kBBytes;
 };
 
-template <Out OUT, bool W8>
+// PP: the int4 codes come in the shuffled tile layout, whose 1 KB tiles (16
+// channels x 128 k, chunks already at their LDS slots) are exactly the weight
+// wave-loads below.
+template <Out OUT, bool W8, bool PP = false>
 __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
     constexpr int kStageBytes = GemmStage<W8>::kBytes;
     // One array per ring stage: each unrolled iteration below names its
@@ -88,7 +91,11 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
     // channel's global chunk (lane%4) ^ ((lane/8)%4).
     // With 8-bit weights the B tile repeats the A pattern (rows = channels,
     // row stride K bytes), so the same per-lane offsets serve both.
-    const v4i rbs = buffer_desc(a.packed + n0 * KB, min((int64_t)kBN, N - n0) * KB);
+    static_assert(!PP || !W8, "shuffled layout of int4 codes");
+    const int64_t ST = K / 128;  // 128-k steps (tiles per 16-channel block)
+    const v4i rbs = PP ? buffer_desc(a.packed + (n0 / 16) * ST * 1024,
+                                     ((min((int64_t)kBN, N - n0) + 15) / 16) * ST * 1024)
+                       : buffer_desc(a.packed + n0 * KB, min((int64_t)kBN, N - n0) * KB);
     const int b_voff = (32 * wave + lane / 4) * (int)KB + (((lane % 4) ^ ((lane / 8) % 4)) * 16);
     auto issue = [&](uint8_t *st, int kt) {
         const uint32_t base = lds_addr(st);
@@ -100,6 +107,11 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
             for (int i = 0; i < 4; ++i)
                 dma16(rbs, base + kABytes + (4 * wave + i) * 1024, a_voff[i % 2],
                       8 * i * (int)K + kt * kBK);
+        } else if (PP) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                dma16(rbs, base + kABytes + (2 * wave + i) * 1024,
+                      (2 * wave + i) * (int)ST * 1024 + lane * 16, kt * 1024);
         } else {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -279,6 +291,13 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
 template <bool W8>
 static void go_gemm(const W4A8Args &a, hipStream_t st) {
     const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
+    if constexpr (!W8) {
+        if (a.pp) {
+            launch_main(k_gemm_mfma<Out::Y, false, true>, dim3((unsigned)tiles), dim3(512), 0, st,
+                        a);
+            return;
+        }
+    }
     if (a.out == Out::I32)
         launch_main(k_gemm_mfma<Out::I32, W8>, dim3((unsigned)tiles), dim3(512), 0, st, a);
     else

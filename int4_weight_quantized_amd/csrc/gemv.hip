@@ -39,7 +39,11 @@ bool gemv_dot4_ok(int64_t M, int64_t K, bool w8) {
 // DIV (with FUSED): the activations are divided by per-column divisors
 // (a.act_div) before their quantization -- the activation side of AWQ-style
 // channel scaling.
-template <int M, int ROWS, int UB, bool FUSED, Out OUT, bool W8, bool DIV = false>
+// PP: the int4 codes come in the shuffled tile layout (ROWS == 16, K % 128 ==
+// 0): chunk c of block row r sits in tile c / 4 at slot (c % 4) ^ ((r / 2) % 4),
+// so the 4 rows of a wave still read 256 contiguous bytes per tile.
+template <int M, int ROWS, int UB, bool FUSED, Out OUT, bool W8, bool DIV = false,
+          bool PP = false>
 __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
     constexpr int T = 16 * ROWS;  // threads
     constexpr int KPC = W8 ? 16 : 32;  // codes per 16-byte chunk
@@ -92,13 +96,18 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
     }
 
     // (2) weights of this block's rows: all UB chunks of the lane.
-    const auto rw = make_rsrc(a.packed + n0 * KB, (int64_t)rows * KB);
+    static_assert(!PP || (ROWS == 16 && !W8), "shuffled int4 tiles of 16 channels");
+    const auto rw = PP ? make_rsrc(a.packed + (n0 / 16) * (int64_t)(K / 128) * 1024,
+                                   (int64_t)(K / 128) * 1024)
+                       : make_rsrc(a.packed + n0 * KB, (int64_t)rows * KB);
     const int rowoff = r * KB;
     uint4 wb[UB];
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
         const int c = j + 16 * u;
-        wb[u] = bload16(rw, c < C ? rowoff + 16 * c : kOOB);
+        const int off = PP ? ((c / 4) * 16 + r) * 64 + 16 * ((c % 4) ^ ((r / 2) % 4))
+                           : rowoff + 16 * c;
+        wb[u] = bload16(rw, c < C ? off : kOOB);
     }
 
     // Epilogue operands, so their latency hides behind the main work.
@@ -260,6 +269,13 @@ template <int M, int ROWS, int UB, bool W8>
 static void go_dot4(const W4A8Args &a, hipStream_t st) {
     dim3 grid((unsigned)((a.N + ROWS - 1) / ROWS));
     const uint32_t shm = (uint32_t)(M * a.K);
+    if constexpr (!W8) {
+        if (a.pp) {  // shuffled layout: fused forward only
+            launch_main(k_gemv_dot4<M, ROWS, UB, true, Out::Y, false, false, true>, grid,
+                        dim3(16 * ROWS), shm, st, a);
+            return;
+        }
+    }
     if (a.out == Out::I32)
         launch_main(k_gemv_dot4<M, ROWS, UB, false, Out::I32, W8>, grid, dim3(16 * ROWS), shm, st,
                     a);
@@ -328,7 +344,9 @@ hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st) {
 // Weights and activations of the next D steps are in flight in a register
 // ring while the current step multiplies.  Rows past M and channels past N
 // read zeros (their outputs are not stored).
-template <int MB, int NB, int D, int W, Out OUT, bool W8>
+// PP: the int4 codes come in the shuffled tile layout: the (nb, step) load of
+// a wave is one contiguous 1 KB tile (lane (r16, kq) takes slot kq ^ ((r16/2)%4)).
+template <int MB, int NB, int D, int W, Out OUT, bool W8, bool PP = false>
 __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args a) {
     constexpr int WL = W8 ? 2 : 1;  // 16-byte weight loads per lane and step
     constexpr int kPairs = MB * NB;                 // 16x16 output blocks
@@ -348,11 +366,17 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args a) {
     for (int t = threadIdx.x; t < kPairs * 4 * kWave; t += 64 * W) red[t] = 0;
     __syncthreads();
 
-    const auto rb = make_rsrc(a.packed + n0 * KB, (int64_t)cols * KB);
+    static_assert(!PP || !W8, "shuffled layout of int4 codes");
+    const auto rb = PP ? make_rsrc(a.packed + (n0 / 16) * (int64_t)S * 1024,
+                                   (int64_t)((cols + 15) / 16) * S * 1024)
+                       : make_rsrc(a.packed + n0 * KB, (int64_t)cols * KB);
     const auto ra = make_rsrc(a.Xq, M * K);
     int boff[NB], aoff[MB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) boff[nb] = (16 * nb + r16) * KB + kq * 16 * WL;
+    for (int nb = 0; nb < NB; ++nb)
+        boff[nb] = PP ? nb * S * 1024 + r16 * 64 + 16 * (kq ^ ((r16 / 2) % 4))
+                      : (16 * nb + r16) * KB + kq * 16 * WL;
+    const int wstep = PP ? 1024 : 64 * WL;  // bytes per 128-k step
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) aoff[mb] = (2 * kq * (int)M + 16 * mb + r16) * 16;
     // activations are chunk-major, [K/16][M][16]: chunk c = 8 s + 2 kq + half
@@ -371,7 +395,7 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args a) {
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int h = 0; h < WL; ++h)
-                wr[d][nb][h] = bload16(rb, ok ? boff[nb] + 64 * WL * ss + 16 * h : kOOB);
+                wr[d][nb][h] = bload16(rb, ok ? boff[nb] + wstep * ss + 16 * h : kOOB);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int o = ok ? aoff[mb] + astep * ss : kOOB;
@@ -476,6 +500,13 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args a) {
 template <int MB, int NB, int D, int W, bool W8>
 static void go_mfma(const W4A8Args &a, hipStream_t st) {
     dim3 grid((unsigned)((a.N + 16 * NB - 1) / (16 * NB)));
+    if constexpr (!W8) {
+        if (a.pp) {
+            launch_main(k_gemv_mfma<MB, NB, D, W, Out::Y, false, true>, grid, dim3(64 * W), 0, st,
+                        a);
+            return;
+        }
+    }
     if (a.out == Out::I32)
         launch_main(k_gemv_mfma<MB, NB, D, W, Out::I32, W8>, grid, dim3(64 * W), 0, st, a);
     else

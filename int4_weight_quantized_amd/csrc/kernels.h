@@ -46,6 +46,7 @@ struct W4A8Args {
     bool w8;    // 8-bit weight codes (W8A8): natural-layout activations, no unpacking
     bool relu;  // ReLU after dequantization and bias (Out::Y only)
     const float *act_div;  // per-column divisors of X before quantization (AWQ), or NULL
+    bool pp;  // int4 weights in the shuffled tile layout (K % 128 == 0; see w4a16.hip)
 };
 
 hipError_t launch_quant_weight_sym(const float *W, int64_t K, int64_t N, uint8_t *packed,
@@ -103,6 +104,10 @@ hipError_t launch_w4a16_lds(const uint16_t *X, int64_t M, int64_t K, int64_t N,
 hipError_t launch_w4a16_prepacked(const uint16_t *X, int64_t M, int64_t K, int64_t N,
                                   const uint8_t *wpp, const float *szpp, float *Y,
                                   hipStream_t st);
+hipError_t launch_w4_prepack_weights(const uint8_t *packed, int64_t K, int64_t N, uint8_t *wpp,
+                                    hipStream_t st);
+hipError_t launch_w4_unprepack_weights(const uint8_t *wpp, int64_t K, int64_t N, uint8_t *packed,
+                                      hipStream_t st);
 hipError_t launch_w4a16_prepack(const uint8_t *packed, const float *scales, const float *zeros,
                                 int64_t K, int64_t N, uint8_t *wpp, float *szpp, hipStream_t st);
 hipError_t launch_w4a16_unprepack(const uint8_t *wpp, const float *szpp, int64_t K, int64_t N,

@@ -499,22 +499,28 @@ hipError_t launch_w4a16_prepacked(const uint16_t *X, int64_t M, int64_t K, int64
 // wpp[b][t][c][16 p + i] = packed[16 b + c][64 t + 16 (p ^ ((c / 2) % 4)) + i]
 // (zero for padding channels); szpp[b][u][c] = (s, z) of groups 2u, 2u + 1.
 // One thread per 16-byte unit of the destination (prepack) or of the
-// canonical arrays (unprepack).  K % 512 == 0, 16-byte aligned arrays.
-__global__ void k_w4a16_prepack(const uint8_t *__restrict__ packed,
-                                const float *__restrict__ scales,
-                                const float *__restrict__ zeros, int64_t K, int64_t N,
-                                uint8_t *__restrict__ wpp, float *__restrict__ szpp) {
+// canonical arrays (unprepack); 16-byte aligned arrays.  The weight part
+// needs K % 128 == 0 (it also serves the W4A8 codes), the tables K % 512 == 0.
+__global__ void k_w4_prepack_weights(const uint8_t *__restrict__ packed, int64_t K, int64_t N,
+                                     uint8_t *__restrict__ wpp) {
     const int64_t S = K / 128, KB = K / 2, NB = (N + 15) / 16;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (int64_t u = i0; u < NB * S * 64; u += stride) {
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < NB * S * 64; u += stride) {
         const int64_t p = u % 4, c = (u / 4) % 16, t = (u / 64) % S, b = u / (64 * S);
         const int64_t n = 16 * b + c, chunk = p ^ ((c / 2) % 4);
         uint4 v = {0u, 0u, 0u, 0u};
         if (n < N) v = *reinterpret_cast<const uint4 *>(packed + n * KB + 64 * t + 16 * chunk);
         reinterpret_cast<uint4 *>(wpp)[u] = v;
     }
-    for (int64_t e = i0; e < NB * (S / 2) * 16; e += stride) {
+}
+
+__global__ void k_w4a16_prepack_tables(const float *__restrict__ scales,
+                                       const float *__restrict__ zeros, int64_t K, int64_t N,
+                                       float *__restrict__ szpp) {
+    const int64_t S = K / 128, NB = (N + 15) / 16;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < NB * (S / 2) * 16;
+         e += stride) {
         const int64_t c = e % 16, uu = (e / 16) % (S / 2), b = e / (16 * (S / 2));
         const int64_t n = 16 * b + c;
         float4 v = {0.f, 0.f, 0.f, 0.f};
@@ -525,21 +531,25 @@ __global__ void k_w4a16_prepack(const uint8_t *__restrict__ packed,
     }
 }
 
-__global__ void k_w4a16_unprepack(const uint8_t *__restrict__ wpp,
-                                  const float *__restrict__ szpp, int64_t K, int64_t N,
-                                  uint8_t *__restrict__ packed, float *__restrict__ scales,
-                                  float *__restrict__ zeros) {
+__global__ void k_w4_unprepack_weights(const uint8_t *__restrict__ wpp, int64_t K, int64_t N,
+                                       uint8_t *__restrict__ packed) {
     const int64_t S = K / 128, KB = K / 2;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (int64_t u = i0; u < N * (KB / 16); u += stride) {
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < N * (KB / 16);
+         u += stride) {
         const int64_t n = u / (KB / 16), off = (u % (KB / 16)) * 16;
         const int64_t b = n / 16, c = n % 16, t = off / 64, chunk = (off % 64) / 16;
         const int64_t p = chunk ^ ((c / 2) % 4);
         reinterpret_cast<uint4 *>(packed)[u] =
             *reinterpret_cast<const uint4 *>(wpp + ((b * S + t) * 16 + c) * 64 + 16 * p);
     }
-    for (int64_t e = i0; e < N * S; e += stride) {
+}
+
+__global__ void k_w4a16_unprepack_tables(const float *__restrict__ szpp, int64_t K, int64_t N,
+                                         float *__restrict__ scales, float *__restrict__ zeros) {
+    const int64_t S = K / 128;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < N * S; e += stride) {
         const int64_t n = e / S, g = e % S, b = n / 16, c = n % 16;
         const float *src = szpp + ((b * (S / 2) + g / 2) * 16 + c) * 4 + 2 * (g % 2);
         scales[e] = src[0];
@@ -552,19 +562,37 @@ static unsigned conv_blocks(int64_t n) {
     return (unsigned)(b < 4096 ? (b > 0 ? b : 1) : 4096);
 }
 
+hipError_t launch_w4_prepack_weights(const uint8_t *packed, int64_t K, int64_t N, uint8_t *wpp,
+                                    hipStream_t st) {
+    const int64_t units = ((N + 15) / 16) * (K / 128) * 64;
+    hipLaunchKernelGGL(k_w4_prepack_weights, dim3(conv_blocks(units)), dim3(256), 0, st, packed, K,
+                       N, wpp);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4_unprepack_weights(const uint8_t *wpp, int64_t K, int64_t N, uint8_t *packed,
+                                      hipStream_t st) {
+    hipLaunchKernelGGL(k_w4_unprepack_weights, dim3(conv_blocks(N * (K / 32))), dim3(256), 0, st,
+                       wpp, K, N, packed);
+    return hipGetLastError();
+}
+
 hipError_t launch_w4a16_prepack(const uint8_t *packed, const float *scales, const float *zeros,
                                 int64_t K, int64_t N, uint8_t *wpp, float *szpp, hipStream_t st) {
-    const int64_t units = ((N + 15) / 16) * (K / 128) * 64;
-    hipLaunchKernelGGL(k_w4a16_prepack, dim3(conv_blocks(units)), dim3(256), 0, st, packed, scales,
-                       zeros, K, N, wpp, szpp);
+    const hipError_t err = launch_w4_prepack_weights(packed, K, N, wpp, st);
+    if (err != hipSuccess) return err;
+    const int64_t e = ((N + 15) / 16) * (K / 256) * 16;
+    hipLaunchKernelGGL(k_w4a16_prepack_tables, dim3(conv_blocks(e)), dim3(256), 0, st, scales,
+                       zeros, K, N, szpp);
     return hipGetLastError();
 }
 
 hipError_t launch_w4a16_unprepack(const uint8_t *wpp, const float *szpp, int64_t K, int64_t N,
                                   uint8_t *packed, float *scales, float *zeros, hipStream_t st) {
-    const int64_t units = N * (K / 32);
-    hipLaunchKernelGGL(k_w4a16_unprepack, dim3(conv_blocks(units)), dim3(256), 0, st, wpp, szpp, K,
-                       N, packed, scales, zeros);
+    const hipError_t err = launch_w4_unprepack_weights(wpp, K, N, packed, st);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_w4a16_unprepack_tables, dim3(conv_blocks(N * (K / 128))), dim3(256), 0, st,
+                       szpp, K, N, scales, zeros);
     return hipGetLastError();
 }
 

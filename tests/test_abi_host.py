@@ -47,6 +47,8 @@ def test_header_declares_the_boundary():
                  "awq_fold_weight", "awq_quantize_act", "awq_scale_act_bf16", "w4a8_linear_awq",
                  "w4a16_prepack", "w4a16_unprepack", "w4a16_linear_prepacked",
                  "w4a16_prepacked_weight_bytes", "w4a16_prepacked_table_floats",
+                 "w4_prepacked_weight_bytes", "w4_prepack_weights", "w4_unprepack_weights",
+                 "w4a8_linear_prepacked",
                  "w4_status_string", "w4_last_path"]:
         assert want in names, names
 
@@ -207,6 +209,24 @@ def test_prepacked_checks(w4):
     assert f(FAKE, 1, 512, 16, None, FAKE, FAKE, None) == W4_ERR_NULL
     assert f(FAKE, 1, 384, 16, FAKE, FAKE, FAKE, None) == W4_ERR_SHAPE
     assert f(FAKE + 2, 1, 512, 16, FAKE, FAKE, FAKE, None) == W4_ERR_ALIGN
+
+
+def test_w4a8_prepacked_checks(w4):
+    L = w4.lib()
+    assert L.w4_prepacked_weight_bytes(1152, 6912) == 6912 * 576
+    assert L.w4_prepacked_weight_bytes(1152, 37) == 48 * 576
+    assert L.w4_prepacked_weight_bytes(1000, 16) == 0
+    assert L.w4_prepack_weights(None, 128, 16, FAKE, None) == W4_ERR_NULL
+    assert L.w4_prepack_weights(FAKE, 96, 16, FAKE, None) == W4_ERR_SHAPE
+    assert L.w4_prepack_weights(FAKE, 128, 16, FAKE + 8, None) == W4_ERR_ALIGN
+    assert L.w4_unprepack_weights(FAKE, 128, 0, FAKE, None) == W4_ERR_SHAPE
+    ws = w4.w4a8_workspace_bytes(2, 128, 8)
+    f = L.w4a8_linear_prepacked
+    assert f(FAKE, 2, 128, 8, None, FAKE, None, 0, FAKE, FAKE, ws, None) == W4_ERR_NULL
+    assert f(FAKE, 2, 96, 8, FAKE, FAKE, None, 0, FAKE, FAKE, ws, None) == W4_ERR_SHAPE
+    assert f(FAKE, 2, 128, 8, FAKE + 4, FAKE, None, 0, FAKE, FAKE, ws, None) == W4_ERR_ALIGN
+    assert f(FAKE, 2, 128, 8, FAKE, FAKE, None, 3, FAKE, FAKE, ws, None) == W4_ERR_ARG
+    assert f(FAKE, 2, 128, 8, FAKE, FAKE, None, 0, FAKE, FAKE, 0, None) == W4_ERR_WORKSPACE
 
 
 def test_w4a16_checks(w4):

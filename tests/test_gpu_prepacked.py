@@ -89,3 +89,67 @@ def test_linear_prepacked_full_70b():
     yref, absy = oracle.w4a16_linear(d["x_bf16"], pr, sr, zr, 128)
     gamma = K * 2.0**-24 / (1 - K * 2.0**-24)
     assert np.all(np.abs(y[:, cols].astype(np.float64) - yref) <= gamma * absy)
+
+
+# ------------------------------------------- W4A8 on the shuffled int4 tiles
+@pytest.mark.parametrize("K,N", [(128, 16), (1152, 37), (4096, 300)])
+def test_w4_prepack_weights(K, N):
+    rng = np.random.default_rng(K * 3 + N)
+    p = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    wpp = W4.w4_prepack_weights(dev(p))
+    assert np.array_equal(host(wpp), oracle.w4_prepack_weights(p, K).ravel())
+    assert np.array_equal(host(W4.w4_unprepack_weights(wpp, K, N)), p)
+
+
+W4A8_PP = [(1, 1152, 200, "gemv_dot4_prepacked"), (4, 4096, 70, "gemv_dot4_prepacked"),
+           (3, 8192 + 128, 40, "gemv_mfma_prepacked"), (8, 1152, 130, "gemv_mfma_prepacked"),
+           (16, 4096, 96, "gemv_mfma_prepacked"), (64, 512, 33, "gemv_mfma_prepacked"),
+           (100, 384, 260, "gemm_mfma_prepacked"), (300, 1152, 1000, "gemm_mfma_prepacked")]
+
+
+@pytest.mark.parametrize("M,K,N,path", W4A8_PP)
+@pytest.mark.parametrize("relu", [False, True])
+def test_w4a8_linear_prepacked(M, K, N, path, relu):
+    d = workloads.random_case(M + K + 7 * N, M, K, N, outliers=6, bias=True)
+    pref, sref = oracle.quantize_weight_sym(d["W"])
+    yref = oracle.w4a8_linear(d["x"], pref, sref, d["bias"])
+    if relu:
+        yref = oracle.relu(yref)
+    packed, sw, _ = W4.w4_quantize_weight(dev(d["W"]), "sym")
+    wpp = W4.w4_prepack_weights(packed)
+    act = "relu" if relu else None
+    y = host(W4.w4a8_linear_prepacked(dev(d["x"]), wpp, sw, bias=dev(d["bias"]), activation=act))
+    assert W4.w4_last_path() == path
+    assert np.array_equal(y.view(np.uint32), yref.view(np.uint32)), path
+    y0 = host(W4.w4a8_linear_act(dev(d["x"]), packed, sw, bias=dev(d["bias"]), activation=act))
+    assert np.array_equal(y.view(np.uint32), y0.view(np.uint32))
+
+
+def test_w4a8_prepacked_unaligned_x():
+    """X not 16-byte aligned: the MFMA paths still apply (activation kernel)."""
+    d = workloads.random_case(11, 2, 512, 48, outliers=2)
+    packed, sw, _ = W4.w4_quantize_weight(dev(d["W"]), "sym")
+    wpp = W4.w4_prepack_weights(packed)
+    buf = torch.zeros(2 * 512 + 1, dtype=torch.float32, device=DEV)
+    X = buf[1:].view(2, 512)
+    X.copy_(dev(d["x"]))
+    y = host(W4.w4a8_linear_prepacked(X, wpp, sw))
+    assert W4.w4_last_path() == "gemv_mfma_prepacked"
+    pref, sref = oracle.quantize_weight_sym(d["W"])
+    assert np.array_equal(y.view(np.uint32), oracle.w4a8_linear(d["x"], pref, sref).view(np.uint32))
+
+
+@pytest.mark.parametrize("name,M", [("gemma", 1), ("mlp7b", 16), ("prefill", None)])
+def test_w4a8_prepacked_full_workloads(name, M):
+    d = workloads.generate(name, M=M)
+    packed, sw, _ = W4.w4_quantize_weight(dev(d["W"]), "sym")
+    wpp = W4.w4_prepack_weights(packed)
+    X = dev(d["x"])
+    y = host(W4.w4a8_linear_prepacked(X, wpp, sw))
+    y0 = host(W4.w4a8_linear(X, packed, sw))
+    assert np.array_equal(y.view(np.uint32), y0.view(np.uint32))
+    rows = np.arange(min(8, y.shape[0]))
+    cols = np.arange(0, d["N"], max(1, d["N"] // 64))
+    pref, sref = oracle.quantize_weight_sym(np.ascontiguousarray(d["W"][:, cols]))
+    yref = oracle.w4a8_linear(np.ascontiguousarray(d["x"][rows]), pref, sref)
+    assert np.array_equal(y[np.ix_(rows, cols)].view(np.uint32), yref.view(np.uint32))
