@@ -112,7 +112,8 @@ def w4a16_bytes(M, K, N, g):
 class W4A8Case:
     """One W4A8 layer (or, with w8=True, the same layer as W8A8)."""
 
-    def __init__(self, w4, torch, name, shape_name, M, rotate=True, copies=None, w8=False):
+    def __init__(self, w4, torch, name, shape_name, M, rotate=True, copies=None, w8=False,
+                 pp=False):
         import workloads
         d = workloads.generate(shape_name, M=M)
         self.name, self.M, self.K, self.N = name, M if M else d["M"], d["K"], d["N"]
@@ -125,6 +126,9 @@ class W4A8Case:
             p, s = w4.w8_quantize_weight(W)
         else:
             p, s, _ = w4.w4_quantize_weight(W, "sym")
+        self.pp = pp
+        if pp:  # one-time conversion to the shuffled tile layout
+            p = w4.w4_prepack_weights(p)
         torch.cuda.synchronize()
         self.quant_s = time.perf_counter() - t0
         del W
@@ -143,6 +147,10 @@ class W4A8Case:
 
     def step(self, i):
         c = i % self.copies
+        if self.pp:
+            self.w4.w4a8_linear_prepacked(self.x, self.P[c], self.S[c], Y=self.y,
+                                          workspace=self.ws)
+            return
         f = self.w4.w8a8_linear if self.w8 else self.w4.w4a8_linear
         f(self.x, self.P[c], self.S[c], Y=self.y, workspace=self.ws)
 
@@ -360,7 +368,8 @@ def main():
                     help="run one workload's product kernel (for profilers): gemma_m1, gemma_m8, "
                          "mlp7b_m1, mlp7b_m16, mlp7b_m64, prefill, w4a16, w4a16_prepacked, "
                          "w8a8_gemma_m1, "
-                         "w8a8_mlp7b_m1, w8a8_prefill; or copy (a 64 MiB device copy, for "
+                         "w8a8_mlp7b_m1, w8a8_prefill, pp_<W4A8 workload> (shuffled tiles); "
+                         "or copy (a 64 MiB device copy, for "
                          "counter calibration)")
     ap.add_argument("--launches", type=int, default=200)
     ap.add_argument("--copies", type=int, default=0,
@@ -393,12 +402,14 @@ def main():
                  "mlp7b_m16": ("mlp7b", 16), "mlp7b_m64": ("mlp7b", 64),
                  "prefill": ("prefill", None)}
         w8 = args.only.startswith("w8a8_")
-        key = args.only[5:] if w8 else args.only
+        pp = args.only.startswith("pp_")
+        key = args.only[5:] if w8 else args.only[3:] if pp else args.only
         if args.only.startswith("w4a16"):
             case = W4A16Case(w4, torch, copies=args.copies,
                              prepacked=args.only == "w4a16_prepacked")
         else:
-            case = W4A8Case(w4, torch, args.only, *specs[key], copies=args.copies, w8=w8)
+            case = W4A8Case(w4, torch, args.only, *specs[key], copies=args.copies, w8=w8,
+                            pp=pp)
         for i in range(args.warmup + args.steps):
             case.step(i)
         torch.cuda.synchronize()
@@ -441,9 +452,9 @@ def main():
 
     parts = []
     if not args.no_parts:
-        def w4a8_part(name, shape, M, bound, rotate=True, w8=False):
+        def w4a8_part(name, shape, M, bound, rotate=True, w8=False, pp=False):
             log(f"part: {name}")
-            c = W4A8Case(w4, torch, name, shape, M, rotate=rotate, w8=w8)
+            c = W4A8Case(w4, torch, name, shape, M, rotate=rotate, w8=w8, pp=pp)
             st = graph_step_time(torch, c, min(args.steps, 200), 10)
             p = w4.w4_last_path()
             ka, km = kernel_time(torch, hip, w4, c, min(args.launches, 100))
@@ -470,6 +481,12 @@ def main():
         w4a8_part("mlp7b_m16", "mlp7b", 16, "hbm")
         w4a8_part("mlp7b_m64", "mlp7b", 64, "hbm")
         w4a8_part("prefill_4096", "prefill", None, "mfma", rotate=False)
+        w4a8_part("pp_gemma_m1", "gemma", 1, "hbm", pp=True)
+        w4a8_part("pp_gemma_m8", "gemma", 8, "hbm", pp=True)
+        w4a8_part("pp_mlp7b_m1", "mlp7b", 1, "hbm", pp=True)
+        w4a8_part("pp_mlp7b_m16", "mlp7b", 16, "hbm", pp=True)
+        w4a8_part("pp_mlp7b_m64", "mlp7b", 64, "hbm", pp=True)
+        w4a8_part("pp_prefill_4096", "prefill", None, "mfma", rotate=False, pp=True)
         w4a8_part("w8a8_gemma_m1", "gemma", 1, "hbm", w8=True)
         w4a8_part("w8a8_mlp7b_m1", "mlp7b", 1, "hbm", w8=True)
         w4a8_part("w8a8_mlp7b_m16", "mlp7b", 16, "hbm", w8=True)
