@@ -165,14 +165,24 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
                     bh[nb] = v4i{(int)lo16(p0), (int)hi16(p0), (int)lo16(p1), (int)hi16(p1)};
                 }
             }
+            // activation fragments in a rolling window of 4: the read of row
+            // block rb + 4 is issued right after the MFMAs of rb, so three
+            // reads are in flight behind every row block's MFMAs
+            uint4 xa[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+                xa[rb] = *reinterpret_cast<const uint4 *>(st + aoff[h] + rb * 2048);
 #pragma unroll
             for (int rb = 0; rb < 8; ++rb) {
-                const uint4 x = *reinterpret_cast<const uint4 *>(st + aoff[h] + rb * 2048);
+                const uint4 x = xa[rb % 4];
                 const v4i av = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb)
                     acc[rb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bh[nb], acc[rb][nb],
                                                                         0, 0, 0);
+                if (rb + 4 < 8)
+                    xa[rb % 4] = *reinterpret_cast<const uint4 *>(st + aoff[h] + (rb + 4) * 2048);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
