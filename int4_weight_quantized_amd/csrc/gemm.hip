@@ -283,7 +283,11 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
             uint32_t *dst = (OUT == Out::I32) ? reinterpret_cast<uint32_t *>(a.acc + row * N + col)
                                               : reinterpret_cast<uint32_t *>(a.Y + row * N + col);
             if (col + 3 < N && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-                *reinterpret_cast<uint4 *>(dst) = v;
+                // written once and never read back here: a non-temporal store
+                // keeps the output stream from evicting the weight and
+                // activation tiles the other workgroups still read from L2
+                const u32x4 w = {v.x, v.y, v.z, v.w};
+                __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(dst));
             } else {
                 if (col < N) dst[0] = v.x;
                 if (col + 1 < N) dst[1] = v.y;
