@@ -404,9 +404,110 @@ __global__ __launch_bounds__(256) void k_quant_act(const float *__restrict__ X, 
     }
 }
 
+// Register-resident variant for 16-byte aligned rows with K % 8 == 0 and
+// K <= 2048 * NG: thread t owns the 8-groups t, t + 256, ... of its row, issues
+// all of their loads at once, and keeps them in registers between the absmax
+// and the code pass, so the row is read from memory once.  Same codes, scales
+// and layouts as k_quant_act.
+template <bool P8, bool DIV, bool STEP, int NG>
+__global__ __launch_bounds__(256) void k_quant_act_reg(const float *__restrict__ X, int64_t K,
+                                                       int8_t *__restrict__ Xq,
+                                                       float *__restrict__ sx,
+                                                       const float *__restrict__ div) {
+    __shared__ float red[4];
+    const int64_t m = blockIdx.x;
+    const float *row = X + m * K;
+    const int ng = (int)(K / 8);
+    float4 v[NG][2];
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+        const int g = threadIdx.x + 256 * u;
+        if (g < ng) {
+            v[u][0] = reinterpret_cast<const float4 *>(row + 8 * g)[0];
+            v[u][1] = reinterpret_cast<const float4 *>(row + 8 * g)[1];
+        } else {
+            v[u][0] = v[u][1] = float4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    if (DIV) {
+#pragma unroll
+        for (int u = 0; u < NG; ++u) {
+            const int g = threadIdx.x + 256 * u;
+            if (g < ng) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float4 d = reinterpret_cast<const float4 *>(div + 8 * g)[h];
+                    v[u][h].x = v[u][h].x / d.x;
+                    v[u][h].y = v[u][h].y / d.y;
+                    v[u][h].z = v[u][h].z / d.z;
+                    v[u][h].w = v[u][h].w / d.w;
+                }
+            }
+        }
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int u = 0; u < NG; ++u)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            a = fmaxf(a, fmaxf(fmaxf(fabsf(v[u][h].x), fabsf(v[u][h].y)),
+                               fmaxf(fabsf(v[u][h].z), fabsf(v[u][h].w))));
+    a = block_max(a, red);
+    const float s = (a == 0.0f) ? 0.0f : a / 127.0f;
+    if (threadIdx.x == 0) sx[m] = s;
+    auto quantize = [&](auto code) {
+#pragma unroll
+        for (int u = 0; u < NG; ++u) {
+            const int g = threadIdx.x + 256 * u;
+            if (g >= ng) continue;
+            const float4 v0 = v[u][0], v1 = v[u][1];
+            uint2 p;
+            if (P8) {
+                p.x = pack4_i8(code(v0.x), code(v0.z), code(v1.x), code(v1.z));
+                p.y = pack4_i8(code(v0.y), code(v0.w), code(v1.y), code(v1.w));
+            } else {
+                p.x = pack4_i8(code(v0.x), code(v0.y), code(v0.z), code(v0.w));
+                p.y = pack4_i8(code(v1.x), code(v1.y), code(v1.z), code(v1.w));
+            }
+            const int64_t k0 = 8 * (int64_t)g;
+            int8_t *dst = STEP ? Xq + (k0 / 16) * ((int64_t)gridDim.x * 16) + m * 16 + k0 % 16
+                               : Xq + m * K + k0;
+            *reinterpret_cast<uint2 *>(dst) = p;
+        }
+    };
+    if (s >= kFastQuotientMinScale) {  // block-uniform
+        const float rs = 1.0f / s;
+        quantize([&](float x) { return quant_code_fast(x, s, rs, -128.f, 127.f); });
+    } else {
+        quantize([&](float x) { return quant_code(x, s, -128.f, 127.f); });
+    }
+}
+
+template <bool P8, bool DIV, bool STEP>
+static bool go_quant_act_reg(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx,
+                             hipStream_t st, const float *div) {
+    const bool aligned = (reinterpret_cast<uintptr_t>(X) & 15) == 0 &&
+                         (reinterpret_cast<uintptr_t>(Xq) & 7) == 0 &&
+                         (!DIV || (reinterpret_cast<uintptr_t>(div) & 15) == 0);
+    if (!aligned || K % 8 != 0 || K > 2048 * 8) return false;
+    const dim3 g((unsigned)M), b(256);
+    if (K <= 2048)
+        hipLaunchKernelGGL((k_quant_act_reg<P8, DIV, STEP, 1>), g, b, 0, st, X, K, Xq, sx, div);
+    else if (K <= 4096)
+        hipLaunchKernelGGL((k_quant_act_reg<P8, DIV, STEP, 2>), g, b, 0, st, X, K, Xq, sx, div);
+    else if (K <= 8192)
+        hipLaunchKernelGGL((k_quant_act_reg<P8, DIV, STEP, 4>), g, b, 0, st, X, K, Xq, sx, div);
+    else
+        hipLaunchKernelGGL((k_quant_act_reg<P8, DIV, STEP, 8>), g, b, 0, st, X, K, Xq, sx, div);
+    return true;
+}
+
 template <bool P8, bool STEP>
 static void go_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx,
                          hipStream_t st, const float *div) {
+    if (div ? go_quant_act_reg<P8, true, STEP>(X, M, K, Xq, sx, st, div)
+            : go_quant_act_reg<P8, false, STEP>(X, M, K, Xq, sx, st, div))
+        return;
     const dim3 g((unsigned)M), b(256);
     if (div)
         hipLaunchKernelGGL((k_quant_act<P8, true, STEP>), g, b, 0, st, X, K, Xq, sx, div);

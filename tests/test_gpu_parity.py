@@ -135,7 +135,10 @@ def test_quantize_weight_asym_full_70b_slice():
 
 
 # ------------------------------------------------------------ activations
-ACT_SHAPES = [(1, 1), (32, 10), (3, 33), (1, 1152), (8, 1152), (16, 4096), (64, 4096), (5, 1000)]
+# K % 8 == 0 up to 16384 takes the register-resident quantizer (1, 2, 4 or 8
+# groups of 8 per thread); other K, and K > 16384, the two-pass one
+ACT_SHAPES = [(1, 1), (32, 10), (3, 33), (1, 1152), (8, 1152), (16, 4096), (64, 4096), (5, 1000),
+              (4, 2056), (3, 8192), (2, 12296), (2, 16384), (2, 16392)]
 
 
 @pytest.mark.parametrize("M,K", ACT_SHAPES)
@@ -151,6 +154,21 @@ def test_quantize_act(M, K):
     assert np.array_equal(host(xq), xq_ref), report("xq", host(xq), xq_ref)
     assert bits_equal(host(sx), sx_ref)
     assert guards_intact(bufq, pq)
+
+
+@pytest.mark.parametrize("M,K", [(3, 4096), (2, 1152)])
+def test_quantize_act_misaligned(M, K):
+    """fp32 rows starting 4 bytes past a 16-byte boundary and codes starting at
+    an odd address (the two-pass quantizer): same bytes as the oracle."""
+    d = workloads.random_case(M + K, M, K, 1, outliers=3)
+    xref, sref = oracle.quantize_act(d["x"])
+    xb = torch.zeros(M * K + 4, dtype=torch.float32, device=DEV)
+    X = xb[1:1 + M * K].view(M, K)
+    X.copy_(dev(d["x"]))
+    qb = torch.zeros(M * K + 1, dtype=torch.int8, device=DEV)
+    xq = qb[1:].view(M, K)
+    _, sx = W4.a8_quantize_act(X, Xq=xq)
+    assert np.array_equal(host(xq), xref) and bits_equal(host(sx), sref)
 
 
 def _tie_rows(M, K, seed):
