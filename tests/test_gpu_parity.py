@@ -258,7 +258,7 @@ def test_matmul_i32_extremes():
 
 # ----------------------------------------------------------- W4A8 linear
 LIN_CASES = [(1, 1152, 200), (4, 256, 70), (8, 1152, 130), (16, 512, 64), (64, 256, 33),
-             (100, 384, 260), (32, 10, 32), (9, 40, 7)]
+             (100, 384, 260), (300, 256, 516), (32, 10, 32), (9, 40, 7)]
 
 
 @pytest.mark.parametrize("M,K,N", LIN_CASES)
@@ -279,6 +279,48 @@ def test_linear(M, K, N, with_bias):
     xq, sx = oracle.quantize_act(d["x"])
     y2 = W4.w4a8_linear_q(dev(xq), dev(sx), packed, sw, bias=None if b is None else dev(b))
     assert bits_equal(host(y2), yref), W4.w4_last_path()
+
+
+def test_gemm_epilogue_signed_zero():
+    """Scales whose product underflows to zero: y = float(acc) * 0 is -0.0 for a
+    negative sum, and with no bias the output keeps that sign, on the GEMM's
+    interior and edge tiles alike."""
+    M, K, N = 300, 256, 516
+    d = workloads.random_case(77, M, K, N)
+    X = (d["x"] * np.float32(1e-34)).astype(np.float32)
+    W = (d["W"] * np.float32(1e-11)).astype(np.float32)
+    pref, sref = oracle.quantize_weight_sym(W)
+    yref = oracle.w4a8_linear(X, pref, sref)
+    negzero = (yref == 0) & np.signbit(yref)
+    assert negzero.any() and (~negzero).any()
+    packed, sw, _ = W4.w4_quantize_weight(dev(W), "sym")
+    y = W4.w4a8_linear(dev(X), packed, sw)
+    assert W4.w4_last_path() == "gemm_mfma"
+    assert bits_equal(host(y), yref)
+
+
+# decode-batch MFMA GEMV launch widths: the channel blocks per workgroup follow
+# N (4 for N >= 12288, 3 from 9216, 2 from 6144, else 1 on a 256-CU device);
+# ragged N leaves the last workgroup partly outside the layer
+MFMA_WIDTHS = [(16, 256, 12304), (40, 128, 9232), (64, 256, 6160), (9, 128, 3000)]
+
+
+@pytest.mark.parametrize("M,K,N", MFMA_WIDTHS)
+def test_gemv_mfma_widths(M, K, N):
+    d = workloads.random_case(M * 3 + K + N, M, K, N, outliers=4, bias=True)
+    pref, sref = oracle.quantize_weight_sym(d["W"])
+    yref = oracle.w4a8_linear(d["x"], pref, sref, d["bias"])
+    packed, sw, _ = W4.w4_quantize_weight(dev(d["W"]), "sym")
+    bufy, y, py = guarded((M, N), torch.float32)
+    W4.w4a8_linear(dev(d["x"]), packed, sw, bias=dev(d["bias"]), Y=y)
+    assert W4.w4_last_path() == "gemv_mfma"
+    got = host(y)
+    assert bits_equal(got, yref), report("y", got, yref)
+    assert guards_intact(bufy, py)
+    xq, _ = oracle.quantize_act(d["x"])
+    acc = W4.w4a8_matmul_i32(dev(xq), packed)
+    assert W4.w4_last_path() == "gemv_mfma"
+    assert np.array_equal(host(acc), oracle.matmul_i32(xq, pref, K))
 
 
 def _sample(n, k, seed):

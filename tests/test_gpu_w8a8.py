@@ -103,6 +103,7 @@ I32_CASES = [
     (1, 128, 16), (1, 1152, 100), (2, 4096, 33), (3, 96, 17), (4, 1152, 257),  # dot4
     (1, 8192, 40),                                                              # K > 4096: MFMA GEMV
     (5, 128, 16), (8, 1152, 130), (16, 4096, 96), (17, 256, 65), (33, 512, 31), (64, 1152, 200),
+    (16, 256, 12304), (40, 128, 9232), (64, 256, 6160),  # MFMA GEMV, 4 / 3 / 2 channel blocks
     (65, 128, 130), (130, 256, 129), (256, 1152, 384), (300, 512, 1000),       # GEMM
     (1, 10, 32), (32, 10, 32), (32, 32, 1), (6, 96, 20), (3, 7, 5), (70, 200, 9),  # generic
 ]
@@ -133,7 +134,8 @@ def test_w8a8_matmul_extremes(M, K):
 
 # ----------------------------------------------------------- W8A8 linear
 LIN_CASES = [(1, 1152, 200), (1, 4096, 300), (4, 256, 70), (2, 8192, 64), (8, 1152, 130),
-             (16, 512, 64), (64, 256, 33), (100, 384, 260), (32, 10, 32), (9, 40, 7)]
+             (16, 512, 64), (64, 256, 33), (16, 256, 12304), (40, 128, 9232), (100, 384, 260),
+             (32, 10, 32), (9, 40, 7)]
 
 
 @pytest.mark.parametrize("M,K,N", LIN_CASES)
