@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace w4 {
 
 constexpr int kWave = 64;
@@ -157,15 +159,18 @@ __device__ __forceinline__ float wave_min(float v) {
     return v;
 }
 
-// Max over the whole block (blockDim.x a multiple of 64); `red` is LDS with
-// one float per wave.  Every thread gets the result.
+// Max of values >= 0 over a block of kWaves waves; `red` is LDS with one
+// float per wave.  Every thread gets the result.  (The wave count is a
+// compile-time constant so that no launch argument is read after the barrier.)
+template <int kWaves>
 __device__ __forceinline__ float block_max(float v, float *red) {
-    v = wave_max(v);
+    v = wave_max_dpp(v);
     const int w = threadIdx.x / kWave;
     if ((threadIdx.x % kWave) == 0) red[w] = v;
     __syncthreads();
     float r = red[0];
-    for (int i = 1; i < (int)(blockDim.x / kWave); ++i) r = fmaxf(r, red[i]);
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) r = fmaxf(r, red[i]);
     __syncthreads();
     return r;
 }
@@ -250,6 +255,51 @@ __device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {
     if (nblocks % kXcd != 0) return bid;
     const int per = nblocks / kXcd;
     return (bid % kXcd) * per + bid / kXcd;
+}
+
+// Kernel arguments are read from memory by scalar loads that the compiler
+// places where a value is first used; an argument first used late (an output
+// pointer, an epilogue flag) then costs a memory round trip at that point.
+// Passing an argument through arg_now at kernel entry puts its load in the
+// kernel's first batch of argument loads.
+template <typename T>
+__device__ __forceinline__ T arg_now(T v) {
+    static_assert(sizeof(T) <= 8, "scalar kernel arguments only");
+    if constexpr (sizeof(T) == 8) {
+        uint64_t u;
+        __builtin_memcpy(&u, &v, 8);
+        asm volatile("" : "+s"(u));
+        __builtin_memcpy(&v, &u, 8);
+    } else {
+        uint32_t u = 0;
+        __builtin_memcpy(&u, &v, sizeof(T));
+        asm volatile("" : "+s"(u));
+        __builtin_memcpy(&v, &u, sizeof(T));
+    }
+    return v;
+}
+
+// Pointer arguments keep their global address space through the asm (a plain
+// integer round trip would turn their loads and stores into flat ones, which
+// also count against the LDS wait counter).
+template <typename T>
+__device__ __forceinline__ T *arg_now(T *p) {
+    using GlobalPtr = __attribute__((address_space(1))) T *;
+    uint64_t u = (uint64_t)(GlobalPtr)p;
+    asm volatile("" : "+s"(u));
+    return (T *)(GlobalPtr)u;
+}
+
+template <typename... T>
+__device__ __forceinline__ void args_now(T &...v) {
+    ((v = arg_now(v)), ...);
+}
+
+// Every field of the product kernels' argument block, loaded at entry.
+__device__ __forceinline__ W4A8Args args_now(W4A8Args a) {
+    args_now(a.X, a.Xq, a.sx, a.packed, a.sw, a.bias, a.Y, a.acc, a.M, a.K, a.N, a.out, a.w8,
+             a.relu, a.act_div, a.pp);
+    return a;
 }
 
 }  // namespace w4

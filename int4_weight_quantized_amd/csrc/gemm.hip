@@ -48,7 +48,8 @@ struct GemmStage {
 // channels x 128 k, chunks already at their LDS slots) are exactly the weight
 // wave-loads below.
 template <Out OUT, bool W8, bool PP = false>
-__global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
+__global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args args) {
+    const W4A8Args a = args_now(args);
     constexpr int kStageBytes = GemmStage<W8>::kBytes;
     // One array per ring stage: each unrolled iteration below names its
     // stages statically, so the compiler can tell the stage being read from
@@ -59,7 +60,9 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args a) {
 
     const int64_t M = a.M, N = a.N, K = a.K, KB = W8 ? a.K : a.K / 2;
     const int tiles_n = (int)((N + kBN - 1) / kBN);
-    const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
+    // the grid is exactly the tile count (computed here rather than read from
+    // the launch's hidden arguments, which would be a second argument load)
+    const int tile = xcd_swizzle(blockIdx.x, (int)((M + kBM - 1) / kBM) * tiles_n);
     const int64_t m0 = (int64_t)(tile / tiles_n) * kBM;
     const int64_t n0 = (int64_t)(tile % tiles_n) * kBN;
 

@@ -44,7 +44,8 @@ bool gemv_dot4_ok(int64_t M, int64_t K, bool w8) {
 // so the 4 rows of a wave still read 256 contiguous bytes per tile.
 template <int M, int ROWS, int UB, bool FUSED, Out OUT, bool W8, bool DIV = false,
           bool PP = false>
-__global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args a) {
+__global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args args) {
+    const W4A8Args a = args_now(args);
     constexpr int T = 16 * ROWS;  // threads
     constexpr int KPC = W8 ? 16 : 32;  // codes per 16-byte chunk
     // 8-groups of k per thread (K <= 16 * KPC * UB)
@@ -347,7 +348,8 @@ hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st) {
 // PP: the int4 codes come in the shuffled tile layout: the (nb, step) load of
 // a wave is one contiguous 1 KB tile (lane (r16, kq) takes slot kq ^ ((r16/2)%4)).
 template <int MB, int NB, int D, int W, Out OUT, bool W8, bool PP = false>
-__global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args a) {
+__global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
+    const W4A8Args a = args_now(args);
     constexpr int WL = W8 ? 2 : 1;  // 16-byte weight loads per lane and step
     constexpr int kPairs = MB * NB;                 // 16x16 output blocks
     constexpr int kPerWave = (kPairs + W - 1) / W;  // epilogue blocks per wave

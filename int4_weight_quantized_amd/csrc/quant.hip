@@ -320,6 +320,8 @@ __global__ __launch_bounds__(256) void k_quant_act(const float *__restrict__ X, 
                                                    int8_t *__restrict__ Xq,
                                                    float *__restrict__ sx,
                                                    const float *__restrict__ div) {
+    args_now(X, K, Xq, sx, div);
+    const int64_t rows = STEP ? arg_now((int64_t)gridDim.x) : 0;
     __shared__ float red[4];
     const int64_t m = blockIdx.x;
     const float *row = X + m * K;
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(256) void k_quant_act(const float *__restrict__ X, 
     } else {
         for (int64_t i = threadIdx.x; i < K; i += 256) a = fmaxf(a, fabsf(ld(i)));
     }
-    a = block_max(a, red);
+    a = block_max<4>(a, red);
     const float s = (a == 0.0f) ? 0.0f : a / 127.0f;
     if (threadIdx.x == 0) sx[m] = s;
     int8_t *out = Xq + m * K;
@@ -379,8 +381,7 @@ __global__ __launch_bounds__(256) void k_quant_act(const float *__restrict__ X, 
                     v.x = pack4_i8(q[0], q[1], q[2], q[3]);
                     v.y = pack4_i8(q[4], q[5], q[6], q[7]);
                 }
-                const int64_t M = gridDim.x;
-                *reinterpret_cast<uint2 *>(Xq + (k0 / 16) * (M * 16) + m * 16 + k0 % 16) = v;
+                *reinterpret_cast<uint2 *>(Xq + (k0 / 16) * (rows * 16) + m * 16 + k0 % 16) = v;
             } else if (P8) {
                 uint2 v;
                 v.x = pack4_i8(q[0], q[2], q[4], q[6]);
@@ -414,6 +415,8 @@ __global__ __launch_bounds__(256) void k_quant_act_reg(const float *__restrict__
                                                        int8_t *__restrict__ Xq,
                                                        float *__restrict__ sx,
                                                        const float *__restrict__ div) {
+    args_now(X, K, Xq, sx, div);
+    const int64_t rows = STEP ? arg_now((int64_t)gridDim.x) : 0;
     __shared__ float red[4];
     const int64_t m = blockIdx.x;
     const float *row = X + m * K;
@@ -452,7 +455,7 @@ __global__ __launch_bounds__(256) void k_quant_act_reg(const float *__restrict__
         for (int h = 0; h < 2; ++h)
             a = fmaxf(a, fmaxf(fmaxf(fabsf(v[u][h].x), fabsf(v[u][h].y)),
                                fmaxf(fabsf(v[u][h].z), fabsf(v[u][h].w))));
-    a = block_max(a, red);
+    a = block_max<4>(a, red);
     const float s = (a == 0.0f) ? 0.0f : a / 127.0f;
     if (threadIdx.x == 0) sx[m] = s;
     auto quantize = [&](auto code) {
@@ -470,7 +473,7 @@ __global__ __launch_bounds__(256) void k_quant_act_reg(const float *__restrict__
                 p.y = pack4_i8(code(v1.x), code(v1.y), code(v1.z), code(v1.w));
             }
             const int64_t k0 = 8 * (int64_t)g;
-            int8_t *dst = STEP ? Xq + (k0 / 16) * ((int64_t)gridDim.x * 16) + m * 16 + k0 % 16
+            int8_t *dst = STEP ? Xq + (k0 / 16) * (rows * 16) + m * 16 + k0 % 16
                                : Xq + m * K + k0;
             *reinterpret_cast<uint2 *>(dst) = p;
         }
@@ -631,6 +634,7 @@ hipError_t launch_awq_scale_bf16(const uint16_t *X, int64_t M, int64_t K, const 
 template <bool P8, bool STEP>
 __global__ void k_to_p8(const int8_t *__restrict__ in, int64_t M, int64_t K,
                         int8_t *__restrict__ out) {
+    args_now(in, M, K, out);
     const int64_t total8 = M * K / 8;
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= total8) return;

@@ -75,6 +75,7 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_mfma(const uint16_t *__restric
                                                     const float *__restrict__ zeros,
                                                     float *__restrict__ Y, int64_t M, int64_t K64,
                                                     int64_t N, int64_t group) {
+    args_now(X, packed, scales, zeros, Y, M, K64, N, group);
     static_assert(W * NB * kWave * 16 <= 160 * 1024, "partial sums must fit in LDS");
     static_assert(4 % D == 0, "ring depth divides the 4-step scale blocks");
     __shared__ v4f red[W][NB][kWave];
@@ -298,6 +299,7 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
                                                          const float *__restrict__ zeros,
                                                          float *__restrict__ Y, int64_t M,
                                                          int64_t K64, int64_t N) {
+    args_now(X, packed, scales, zeros, Y, M, K64, N);
     using L = W4a16Lds<WPH, PP>;
     __shared__ __align__(16) uint8_t ring[2 * kLStages * L::kStage];  // [half][stage]
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
