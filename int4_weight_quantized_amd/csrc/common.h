@@ -206,6 +206,27 @@ __device__ __forceinline__ int quant_code_fast(float v, float s, float rs, float
     return (int)r;
 }
 
+// An activation row's scale, prepared for quant_code_row.  A scale below
+// kFastQuotientMinScale is multiplied by 2^100 and so is every value of its row
+// (both exact: the scale stays below 2^36 and |x| <= 127.5 s below 2^-57), which
+// keeps the real quotient x / s and brings the scale into the range of the
+// division-free quotient; a zero scale (all-zero row) gets rs = 0, so every
+// code is 0.  One code path for every scale, no per-value division.
+struct RowScale {
+    float pre, s, rs;
+};
+
+__device__ __forceinline__ RowScale row_scale(float s) {
+    const float pre = (s < kFastQuotientMinScale) ? 0x1p100f : 1.0f;
+    const float ss = s * pre;
+    return RowScale{pre, ss, (ss == 0.0f) ? 0.0f : 1.0f / ss};
+}
+
+// clamp(rne(fl(v / s)), -128, 127) for the row scale s behind `q`.
+__device__ __forceinline__ int quant_code_row(float v, const RowScale &q) {
+    return quant_code_fast(v * q.pre, q.s, q.rs, -128.0f, 127.0f);
+}
+
 // ------------------------------------------------------------------ unpack
 // A packed dword holds 8 signed nibbles for k = 0..7 of a group of 8 (byte i:
 // k = 2i low nibble, k = 2i+1 high nibble).  Moving each nibble to the top of

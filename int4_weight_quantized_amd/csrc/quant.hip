@@ -397,12 +397,8 @@ __global__ __launch_bounds__(256) void k_quant_act(const float *__restrict__ X, 
             }
         }
     };
-    if (s >= kFastQuotientMinScale) {  // block-uniform
-        const float rs = 1.0f / s;
-        quantize([&](float v) { return quant_code_fast(v, s, rs, -128.f, 127.f); });
-    } else {
-        quantize([&](float v) { return quant_code(v, s, -128.f, 127.f); });
-    }
+    const RowScale q = row_scale(s);
+    quantize([&](float v) { return quant_code_row(v, q); });
 }
 
 // Register-resident variant for 16-byte aligned rows with K % 8 == 0 and
@@ -478,12 +474,8 @@ __global__ __launch_bounds__(256) void k_quant_act_reg(const float *__restrict__
             *reinterpret_cast<uint2 *>(dst) = p;
         }
     };
-    if (s >= kFastQuotientMinScale) {  // block-uniform
-        const float rs = 1.0f / s;
-        quantize([&](float x) { return quant_code_fast(x, s, rs, -128.f, 127.f); });
-    } else {
-        quantize([&](float x) { return quant_code(x, s, -128.f, 127.f); });
-    }
+    const RowScale q = row_scale(s);
+    quantize([&](float x) { return quant_code_row(x, q); });
 }
 
 template <bool P8, bool DIV, bool STEP>

@@ -171,6 +171,48 @@ def test_quantize_act_misaligned(M, K):
     assert np.array_equal(host(xq), xref) and bits_equal(host(sx), sref)
 
 
+def _tiny_rows(M, K, seed):
+    """Rows whose scales lie below 2^-64 (about 8e-33 and, subnormal, 8e-40),
+    an all-zero row, and rows of ordinary magnitude, with subnormal values
+    scattered in."""
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    for m in range(M):
+        kind = m % 4
+        if kind == 0:
+            X[m] *= np.float32(1e-30)
+        elif kind == 1:
+            X[m] *= np.float32(1e-37)
+        elif kind == 2:
+            X[m] = 0.0
+        X[m, rng.integers(0, K, 3)] = np.float32(1e-44)
+    return X
+
+
+@pytest.mark.parametrize("M,K,N,path", [(1, 1152, 64, "gemv_dot4"), (3, 4096, 40, "gemv_dot4"),
+                                        (4, 1152, 48, "gemv_dot4"), (16, 512, 64, "gemv_mfma"),
+                                        (100, 384, 260, "gemm_mfma")])
+def test_tiny_activation_scales(M, K, N, path):
+    """Row scales below 2^-64 take the rescaled division-free quotient: codes,
+    scales and outputs still match the oracle's IEEE divisions bit for bit."""
+    X = _tiny_rows(M, K, M + K)
+    xq_ref, sx_ref = oracle.quantize_act(X)
+    assert (sx_ref[1::4] < 2.0 ** -126).all() and (sx_ref[0::4] < 2.0 ** -64).all()
+    xq, sx = W4.a8_quantize_act(dev(X))
+    assert np.array_equal(host(xq), xq_ref) and bits_equal(host(sx), sx_ref)
+    xb = torch.zeros(M * K + 1, dtype=torch.float32, device=DEV)   # misaligned rows
+    xm = xb[1:].view(M, K)
+    xm.copy_(dev(X))
+    xq2, sx2 = W4.a8_quantize_act(xm)
+    assert np.array_equal(host(xq2), xq_ref) and bits_equal(host(sx2), sx_ref)
+    W = workloads.random_case(K + N, 1, K, N)["W"]
+    pref, sref = oracle.quantize_weight_sym(W)
+    yref = oracle.w4a8_linear(X, pref, sref)
+    y = W4.w4a8_linear(dev(X), dev(pref), dev(sref))
+    assert W4.w4_last_path() == path
+    assert bits_equal(host(y), yref), report(f"y path={path}", host(y), yref)
+
+
 def _tie_rows(M, K, seed):
     """Activation rows whose values sit on, and one ulp either side of, the
     rounding ties (k + 1/2) * sx of the int8 grid.  Even rows use a power-of-two
