@@ -124,12 +124,13 @@ __device__ __forceinline__ v4i buffer_desc(const void *base, int64_t bytes) {
 // wait-count pass, which cannot tell which ring stage such a load fills,
 // does not drain all outstanding loads before every LDS read; all waits for
 // these loads are explicit (wait_and_barrier).  The asm has no register
-// outputs; it sets M0 itself and declares it clobbered.  On gfx9 an LDS
-// direct load needs one wait state after an SALU write of M0, hence the nop.
+// outputs; the LDS address is an input bound to M0, so the compiler writes M0
+// itself and knows that it holds this value.  On gfx9 an LDS direct load needs
+// one wait state after an SALU write of M0, hence the nop.
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds_base, int voff, int soff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 ::"s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff)
-                 : "memory", "m0");
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_base)
+                 : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
