@@ -60,11 +60,21 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args args) {
 
     const int64_t M = a.M, N = a.N, K = a.K, KB = W8 ? a.K : a.K / 2;
     const int tiles_n = (int)((N + kBN - 1) / kBN);
+    const int tiles_m = (int)((M + kBM - 1) / kBM);
     // the grid is exactly the tile count (computed here rather than read from
     // the launch's hidden arguments, which would be a second argument load)
-    const int tile = xcd_swizzle(blockIdx.x, (int)((M + kBM - 1) / kBM) * tiles_n);
-    const int64_t m0 = (int64_t)(tile / tiles_n) * kBM;
-    const int64_t n0 = (int64_t)(tile % tiles_n) * kBN;
+    const int tile = xcd_swizzle(blockIdx.x, tiles_m * tiles_n);
+    // Tiles in groups of kGroupRows tile rows, walked column by column: the
+    // consecutive tiles one XCD takes form a patch of 4 rows (activation
+    // panels) by several channel columns (weight panels), so each XCD's L2
+    // fetches fewer panels than with whole rows of tiles.
+    constexpr int kGroupRows = 4;
+    const int group = tile / (kGroupRows * tiles_n);
+    const int first_row = group * kGroupRows;
+    const int rows_here = min(kGroupRows, tiles_m - first_row);
+    const int in_group = tile - group * kGroupRows * tiles_n;
+    const int64_t m0 = (int64_t)(first_row + in_group % rows_here) * kBM;
+    const int64_t n0 = (int64_t)(in_group / rows_here) * kBN;
 
     const int t = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
