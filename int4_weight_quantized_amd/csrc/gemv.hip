@@ -16,6 +16,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <atomic>
+
 namespace w4 {
 
 // ------------------------------------------------------------------ dot4
@@ -524,18 +526,20 @@ static void go_mfma(const W4A8Args &a, hipStream_t st) {
 // 7B-class layer takes NB = 3 (230 workgroups; 9.8 -> 8.2 us at M = 16 against
 // NB = 4, 172 workgroups), the Gemma-like layer NB = 2 (216; 5.0 -> 3.8 us at
 // M = 8).
+// CU count per device, cached (atomics: launches may come from several host
+// threads; every writer stores the same value)
 static int device_cus() {
-    static int cus[64];
+    static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] <= 0) {
-        int n = 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n <= 0)
             n = 256;
-        cus[dev] = n;
+        cus[dev].store(n, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return n;
 }
 
 static int mfma_channel_blocks(int64_t N) {
