@@ -155,62 +155,80 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args args) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-    auto compute = [&](const uint8_t *st) {
+    // One k-tile.  The activation fragments stream through a rolling window
+    // of 4 over both halves (the read of the fragment four ahead is issued
+    // right after each row block's MFMAs, across the half boundary); 8-bit
+    // weights read their second-half fragments between the first half's row
+    // blocks (int4 codes are unpacked for both halves up front: spreading the
+    // unpack measured no faster); `after_first` (the DMA issue of a later
+    // tile) runs after the first row block's MFMAs, so that the matrix pipe
+    // starts right after the barrier.
+    auto compute = [&](const uint8_t *st, auto after_first) {
         uint4 wraw[4];
         if (!W8) {
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
                 wraw[nb] = *reinterpret_cast<const uint4 *>(st + boff + nb * 1024);
         }
+        // the 16 codes of each channel block per half (16 * code, or the int8
+        // codes themselves; those of half 1 are read below)
+        v4i b0[4], b1[4];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            // this half's 16 codes of each channel block, unpacked (16 * code),
-            // or the 16 int8 codes themselves
-            v4i bh[4];
+        for (int nb = 0; nb < 4; ++nb) {
+            if (W8) {
+                const uint4 w = *reinterpret_cast<const uint4 *>(st + b8off[0] + nb * 2048);
+                b0[nb] = v4i{(int)w.x, (int)w.y, (int)w.z, (int)w.w};
+            } else {
+                b0[nb] = v4i{(int)lo16(wraw[nb].x), (int)hi16(wraw[nb].x), (int)lo16(wraw[nb].y),
+                             (int)hi16(wraw[nb].y)};
+                b1[nb] = v4i{(int)lo16(wraw[nb].z), (int)hi16(wraw[nb].z), (int)lo16(wraw[nb].w),
+                             (int)hi16(wraw[nb].w)};
+            }
+        }
+        // fragment i = 8 * half + row block
+        auto a_frag = [&](int i) {
+            return *reinterpret_cast<const uint4 *>(st + aoff[i / 8] + (i % 8) * 2048);
+        };
+        uint4 xa[4];
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
+        for (int i = 0; i < 4; ++i) xa[i] = a_frag(i);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int rb = i % 8;
+            const uint4 x = xa[i % 4];
+            const v4i av = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+                acc[rb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, i < 8 ? b0[nb] : b1[nb],
+                                                                    acc[rb][nb], 0, 0, 0);
+            if (i + 4 < 16) xa[i % 4] = a_frag(i + 4);
+            if (i < 8) {
+                const int nb = i / 2;
                 if (W8) {
-                    const uint4 w = *reinterpret_cast<const uint4 *>(st + b8off[h] + nb * 2048);
-                    bh[nb] = v4i{(int)w.x, (int)w.y, (int)w.z, (int)w.w};
-                } else {
-                    const uint32_t p0 = h ? wraw[nb].z : wraw[nb].x;
-                    const uint32_t p1 = h ? wraw[nb].w : wraw[nb].y;
-                    bh[nb] = v4i{(int)lo16(p0), (int)hi16(p0), (int)lo16(p1), (int)hi16(p1)};
+                    if (i % 2 == 0) {
+                        const uint4 w =
+                            *reinterpret_cast<const uint4 *>(st + b8off[1] + nb * 2048);
+                        b1[nb] = v4i{(int)w.x, (int)w.y, (int)w.z, (int)w.w};
+                    }
                 }
             }
-            // activation fragments in a rolling window of 4: the read of row
-            // block rb + 4 is issued right after the MFMAs of rb, so three
-            // reads are in flight behind every row block's MFMAs
-            uint4 xa[4];
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-                xa[rb] = *reinterpret_cast<const uint4 *>(st + aoff[h] + rb * 2048);
-#pragma unroll
-            for (int rb = 0; rb < 8; ++rb) {
-                const uint4 x = xa[rb % 4];
-                const v4i av = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb)
-                    acc[rb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bh[nb], acc[rb][nb],
-                                                                        0, 0, 0);
-                if (rb + 4 < 8)
-                    xa[rb % 4] = *reinterpret_cast<const uint4 *>(st + aoff[h] + (rb + 4) * 2048);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            if (i == 0) after_first();
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     // One ring step: tile kt sits in `cur`; the tile two ahead goes into
     // `nxt2` (the stage read in the previous step).  Before the barrier this
     // thread's loads of tile kt must be complete: at most the 6 loads of tile
     // kt+1 may remain outstanding.  The barrier also guarantees that no wave
-    // still reads `nxt2`.
+    // still reads `nxt2`, so its loads may be issued anywhere in this step.
     auto step = [&](int kt, int KT, const uint8_t *cur, uint8_t *nxt2) {
         if (kt + 1 < KT)
             wait_and_barrier<6>();
         else
             wait_and_barrier<0>();
-        if (kt + 2 < KT) issue(nxt2, kt + 2);
-        compute(cur);
+        compute(cur, [&] {
+            if (kt + 2 < KT) issue(nxt2, kt + 2);
+        });
     };
 
     // 8-bit weights, 2-stage ring: tile kt sits in `cur` and is complete
@@ -218,8 +236,9 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args args) {
     // with the other stage, which receives tile kt+1.
     auto step2 = [&](int kt, int KT, const uint8_t *cur, uint8_t *nxt) {
         wait_and_barrier<0>();
-        if (kt + 1 < KT) issue(nxt, kt + 1);
-        compute(cur);
+        compute(cur, [&] {
+            if (kt + 1 < KT) issue(nxt, kt + 1);
+        });
     };
 
     const int KT = (int)(K / kBK);
