@@ -319,7 +319,7 @@ def kernel_time(torch, hip, w4, case, launches):
 
 def src_digest():
     h = hashlib.sha256()
-    for f in ("gemv.hip", "common.h"):
+    for f in ("gemv.hip", "common.h", "kernels.h"):
         with open(os.path.join(ROOT, "int4_weight_quantized_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
