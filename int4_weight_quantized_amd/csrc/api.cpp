@@ -78,6 +78,13 @@ int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const floa
     // Activations for the MFMA paths: P8 layout in the workspace (natural
     // layout for 8-bit weights, which then use pre-quantized input as is).
     if (fast) {
+        // Few rows of small K: the MFMA GEMV quantizes the activations itself
+        // (one launch instead of two).
+        if (src == Src::FP32 && !act_div && !acc && aligned(X, 16) && gemv_mfma_fused_ok(M, K)) {
+            a.X = X;
+            g_last_path = w8 ? "w8_gemv_mfma_fused" : pp ? "gemv_mfma_fused_prepacked" : "gemv_mfma_fused";
+            return hip_status(launch_gemv_mfma_fused(a, st));
+        }
         // the MFMA GEMV takes the codes chunk-major, the GEMM row-major
         const bool step = M <= 64;
         if (src == Src::FP32) {

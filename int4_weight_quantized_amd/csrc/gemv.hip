@@ -8,7 +8,8 @@
 //    activation quantization (step 3) is fused into the prologue, so one
 //    launch runs steps 3-6.
 //  * k_gemv_mfma  (M <= 64): int8 MFMA 16x16x64 with the weight operand
-//    unpacked in registers; the activations come pre-quantized in P8 layout.
+//    unpacked in registers; the activations come pre-quantized in P8 layout,
+//    or, for M <= 16 and short rows, are quantized in the prologue (G > 0).
 //
 // All global loads are raw buffer loads: out-of-range lanes get zeros from
 // the descriptor's range check instead of an exec-mask branch, so a lane's
@@ -349,9 +350,20 @@ hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st) {
 // read zeros (their outputs are not stored).
 // PP: the int4 codes come in the shuffled tile layout: the (nb, step) load of
 // a wave is one contiguous 1 KB tile (lane (r16, kq) takes slot kq ^ ((r16/2)%4)).
-template <int MB, int NB, int D, int W, Out OUT, bool W8, bool PP = false>
+// G > 0 (fused activation quantization, M <= 16, K <= 512 G, fp32 X): the
+// workgroup quantizes the activation rows itself into LDS, in the same
+// chunk-major layout with 16 rows (rows past M get zero codes): wave w takes
+// rows w and w + 8, lane l the 8-groups l, l + 64, ... of the row, the row
+// absmax is a wave reduction, and the codes and row scales go to LDS before
+// one barrier (the first weight loads are already in flight).  The main loop
+// then reads the activation fragments from LDS.
+template <int MB, int NB, int D, int W, Out OUT, bool W8, bool PP = false, int G = 0>
 __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
     const W4A8Args a = args_now(args);
+    constexpr bool FUSED = G > 0;
+    static_assert(!FUSED || (MB == 1 && W == 8 && OUT == Out::Y), "fused: 16 rows, 8 waves");
+    __shared__ __align__(16) int8_t xs[FUSED ? 16 * 512 * G : 16];  // [K/16][16][16]
+    __shared__ float sxs[16];
     constexpr int WL = W8 ? 2 : 1;  // 16-byte weight loads per lane and step
     constexpr int kPairs = MB * NB;                 // 16x16 output blocks
     constexpr int kPerWave = (kPairs + W - 1) / W;  // epilogue blocks per wave
@@ -368,7 +380,7 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
     const int cols = (int)min((int64_t)(16 * NB), N - n0);
 
     for (int t = threadIdx.x; t < kPairs * 4 * kWave; t += 64 * W) red[t] = 0;
-    __syncthreads();
+    if (!FUSED) __syncthreads();  // (fused: the prologue's barrier covers it)
 
     static_assert(!PP || !W8, "shuffled layout of int4 codes");
     const auto rb = PP ? make_rsrc(a.packed + (n0 / 16) * (int64_t)S * 1024,
@@ -402,15 +414,93 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
                 wr[d][nb][h] = bload16(rb, ok ? boff[nb] + wstep * ss + 16 * h : kOOB);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const int o = ok ? aoff[mb] + astep * ss : kOOB;
-            xr0[d][mb] = bload16(ra, o);
-            xr1[d][mb] = bload16(ra, ok ? o + achunk : kOOB);
+            if (FUSED) {  // from LDS (16 rows per chunk); steps past s1 hold zero weights
+                const int o = (2 * kq * 16 + r16) * 16 + 2048 * min(ss, S - 1);
+                xr0[d][mb] = *reinterpret_cast<const uint4 *>(xs + o);
+                xr1[d][mb] = *reinterpret_cast<const uint4 *>(xs + o + 256);
+            } else {
+                const int o = ok ? aoff[mb] + astep * ss : kOOB;
+                xr0[d][mb] = bload16(ra, o);
+                xr1[d][mb] = bload16(ra, ok ? o + achunk : kOOB);
+            }
         }
     };
+    if constexpr (FUSED) {
+        // weights of the first steps first, then the activation rows
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        fetch(d, s0 + d);
-        __builtin_amdgcn_sched_barrier(0);  // slot 0 oldest, as in the loop below
+        for (int d = 0; d < D; ++d)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int h = 0; h < WL; ++h)
+                    wr[d][nb][h] = bload16(rb, s0 + d < s1 ? boff[nb] + wstep * (s0 + d) + 16 * h : kOOB);
+        __builtin_amdgcn_sched_barrier(0);
+        const auto rx = make_rsrc(a.X, M * K * 4);
+        const int G8 = K / 8;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int m = wave + 8 * pass;
+            if (m < M) {  // wave-uniform
+                float4 va[G], vb[G];
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    const int g = lane + 64 * i;
+                    const int off = g < G8 ? (m * K + 8 * g) * 4 : kOOB;
+                    va[i] = bloadf4(rx, off);
+                    vb[i] = bloadf4(rx, off + 16);
+                }
+                float am = 0.0f;
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    am = fmaxf(am, fmaxf(fmaxf(fabsf(va[i].x), fabsf(va[i].y)),
+                                         fmaxf(fabsf(va[i].z), fabsf(va[i].w))));
+                    am = fmaxf(am, fmaxf(fmaxf(fabsf(vb[i].x), fabsf(vb[i].y)),
+                                         fmaxf(fabsf(vb[i].z), fabsf(vb[i].w))));
+                }
+                am = wave_max_dpp(am);
+                const float sx = (am == 0.0f) ? 0.0f : am / 127.0f;
+                const RowScale q = row_scale(sx);
+                auto code = [&](float v) { return quant_code_row(v, q); };
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    const int g = lane + 64 * i;
+                    if (g < G8) {
+                        const float4 v0 = va[i], v1 = vb[i];
+                        uint2 pq;
+                        if (W8) {
+                            pq.x = pack4_i8(code(v0.x), code(v0.y), code(v0.z), code(v0.w));
+                            pq.y = pack4_i8(code(v1.x), code(v1.y), code(v1.z), code(v1.w));
+                        } else {  // P8: [x0 x2 x4 x6 | x1 x3 x5 x7]
+                            pq.x = pack4_i8(code(v0.x), code(v0.z), code(v1.x), code(v1.z));
+                            pq.y = pack4_i8(code(v0.y), code(v0.w), code(v1.y), code(v1.w));
+                        }
+                        *reinterpret_cast<uint2 *>(xs + (g / 2) * 256 + m * 16 + (g % 2) * 8) = pq;
+                    }
+                }
+                if (lane == 0) sxs[m] = sx;
+            } else {
+                for (int g = lane; g < G8; g += 64)
+                    *reinterpret_cast<uint2 *>(xs + (g / 2) * 256 + m * 16 + (g % 2) * 8) = uint2{0, 0};
+                if (lane == 0) sxs[m] = 0.0f;
+            }
+        }
+        lds_barrier();  // codes, row scales and the zeroed partial sums (weight loads stay in flight)
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int ss = s0 + d;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int o = (2 * kq * 16 + r16) * 16 + 2048 * min(ss, S - 1);
+                xr0[d][mb] = *reinterpret_cast<const uint4 *>(xs + o);
+                xr1[d][mb] = *reinterpret_cast<const uint4 *>(xs + o + 256);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            fetch(d, s0 + d);
+            __builtin_amdgcn_sched_barrier(0);  // slot 0 oldest, as in the loop below
+        }
     }
 
     // Epilogue operands of the output blocks this wave stores, loaded early:
@@ -425,7 +515,9 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
             swc[j] = a.sw[col];
             bc[j] = a.bias ? a.bias[col] : 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sxr[j][i] = a.sx[min((int64_t)(16 * mb + 4 * kq + i), M - 1)];
+            for (int i = 0; i < 4; ++i)
+                sxr[j][i] = FUSED ? sxs[4 * kq + i]
+                                  : a.sx[min((int64_t)(16 * mb + 4 * kq + i), M - 1)];
         }
     }
 
@@ -568,6 +660,46 @@ static void go_mfma_w(const W4A8Args &a, hipStream_t st) {
         case 3: go_mfma_nb<3, W8>(a, st); break;
         default: go_mfma_nb<4, W8>(a, st); break;
     }
+}
+
+// Fused activation quantization (G > 0): worth it while the per-workgroup
+// quantization stays small.  Each wave quantizes ceil(M / 8) rows of K values
+// before its first MFMA; measured against quantizer + GEMV (two launches) the
+// fused kernel is faster up to ceil(M / 8) * K = 3072 (M = 16, K = 1536) and
+// slower from 4096 on (M = 8, K = 4096; M = 16, K = 2048).
+bool gemv_mfma_fused_ok(int64_t M, int64_t K) {
+    return M >= 1 && M <= 16 && K % 128 == 0 && K <= 2048 && ((M + 7) / 8) * K <= 3072;
+}
+
+template <int NB, bool W8>
+static void go_mfma_fused(const W4A8Args &a, hipStream_t st) {
+    constexpr int G = 4;  // K <= 512 G = 2048
+    dim3 grid((unsigned)((a.N + 16 * NB - 1) / (16 * NB)));
+    if constexpr (!W8) {
+        if (a.pp) {
+            launch_main(k_gemv_mfma<1, NB, 1, 8, Out::Y, false, true, G>, grid, dim3(512), 0, st, a);
+            return;
+        }
+    }
+    launch_main(k_gemv_mfma<1, NB, 1, 8, Out::Y, W8, false, G>, grid, dim3(512), 0, st, a);
+}
+
+template <bool W8>
+static void go_mfma_fused_w(const W4A8Args &a, hipStream_t st) {
+    switch (mfma_channel_blocks(a.N)) {
+        case 1: go_mfma_fused<1, W8>(a, st); break;
+        case 2: go_mfma_fused<2, W8>(a, st); break;
+        case 3: go_mfma_fused<3, W8>(a, st); break;
+        default: go_mfma_fused<4, W8>(a, st); break;
+    }
+}
+
+hipError_t launch_gemv_mfma_fused(const W4A8Args &a, hipStream_t st) {
+    if (a.w8)
+        go_mfma_fused_w<true>(a, st);
+    else
+        go_mfma_fused_w<false>(a, st);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemv_mfma(const W4A8Args &a, hipStream_t st) {

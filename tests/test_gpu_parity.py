@@ -190,7 +190,8 @@ def _tiny_rows(M, K, seed):
 
 
 @pytest.mark.parametrize("M,K,N,path", [(1, 1152, 64, "gemv_dot4"), (3, 4096, 40, "gemv_dot4"),
-                                        (4, 1152, 48, "gemv_dot4"), (16, 512, 64, "gemv_mfma"),
+                                        (4, 1152, 48, "gemv_dot4"), (16, 512, 64, "gemv_mfma_fused"),
+                                        (24, 512, 64, "gemv_mfma"),
                                         (100, 384, 260, "gemm_mfma")])
 def test_tiny_activation_scales(M, K, N, path):
     """Row scales below 2^-64 take the rescaled division-free quotient: codes,
@@ -355,7 +356,7 @@ def test_gemv_mfma_widths(M, K, N):
     packed, sw, _ = W4.w4_quantize_weight(dev(d["W"]), "sym")
     bufy, y, py = guarded((M, N), torch.float32)
     W4.w4a8_linear(dev(d["x"]), packed, sw, bias=dev(d["bias"]), Y=y)
-    assert W4.w4_last_path() == "gemv_mfma"
+    assert W4.w4_last_path() == ("gemv_mfma_fused" if M <= 16 else "gemv_mfma")
     got = host(y)
     assert bits_equal(got, yref), report("y", got, yref)
     assert guards_intact(bufy, py)
@@ -363,6 +364,47 @@ def test_gemv_mfma_widths(M, K, N):
     acc = W4.w4a8_matmul_i32(dev(xq), packed)
     assert W4.w4_last_path() == "gemv_mfma"
     assert np.array_equal(host(acc), oracle.matmul_i32(xq, pref, K))
+
+
+# the MFMA GEMV with the activation quantization in its prologue: M <= 16,
+# K <= 2048 and ceil(M / 8) * K <= 3072, rows past M padded to 16; at the
+# bounds and just outside them (the two-launch path runs there)
+FUSED_CASES = [(5, 128, 33, "gemv_mfma_fused"), (8, 1152, 130, "gemv_mfma_fused"),
+               (8, 2048, 70, "gemv_mfma_fused"), (16, 1152, 260, "gemv_mfma_fused"),
+               (9, 1536, 64, "gemv_mfma_fused"), (16, 1536, 50, "gemv_mfma_fused"),
+               (7, 2176, 50, "gemv_mfma"), (9, 2048, 40, "gemv_mfma"),
+               (16, 1664, 40, "gemv_mfma"), (16, 4096, 48, "gemv_mfma")]
+
+
+@pytest.mark.parametrize("M,K,N,path", FUSED_CASES)
+def test_gemv_mfma_fused(M, K, N, path):
+    d = workloads.random_case(M * 11 + K + N, M, K, N, outliers=min(6, K), bias=True)
+    X = d["x"]
+    if M > 6:
+        X[2] = 0.0                                   # all-zero row
+        X[5] *= np.float32(1e-37)                    # scale below 2^-64 (subnormal)
+    pref, sref = oracle.quantize_weight_sym(d["W"])
+    yref = oracle.w4a8_linear(X, pref, sref, d["bias"])
+    packed, sw, _ = W4.w4_quantize_weight(dev(d["W"]), "sym")
+    bufy, y, py = guarded((M, N), torch.float32)
+    W4.w4a8_linear(dev(X), packed, sw, bias=dev(d["bias"]), Y=y)
+    assert W4.w4_last_path() == path
+    got = host(y)
+    assert bits_equal(got, yref), report(f"y path={path}", got, yref)
+    assert guards_intact(bufy, py)
+    yr = host(W4.w4a8_linear_act(dev(X), packed, sw, bias=dev(d["bias"]), activation="relu"))
+    assert bits_equal(yr, oracle.relu(yref))
+    if K % 128 == 0:
+        wpp = W4.w4_prepack_weights(packed)
+        y2 = host(W4.w4a8_linear_prepacked(dev(X), wpp, sw, bias=dev(d["bias"])))
+        want = "gemv_mfma_fused_prepacked" if path == "gemv_mfma_fused" else "gemv_mfma_prepacked"
+        assert W4.w4_last_path() == want
+        assert bits_equal(y2, yref)
+    qref, s8 = oracle.quantize_weight_w8(d["W"])
+    Wq, sw8 = W4.w8_quantize_weight(dev(d["W"]))
+    y8 = host(W4.w8a8_linear(dev(X), Wq, sw8, bias=dev(d["bias"])))
+    assert W4.w4_last_path() == "w8_" + path
+    assert bits_equal(y8, oracle.w8a8_linear(X, qref, s8, d["bias"]))
 
 
 def _sample(n, k, seed):

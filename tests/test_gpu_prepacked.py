@@ -102,11 +102,11 @@ def test_w4_prepack_weights(K, N):
 
 
 W4A8_PP = [(1, 1152, 200, "gemv_dot4_prepacked"), (4, 4096, 70, "gemv_dot4_prepacked"),
-           (3, 8192 + 128, 40, "gemv_mfma_prepacked"), (8, 1152, 130, "gemv_mfma_prepacked"),
+           (3, 8192 + 128, 40, "gemv_mfma_prepacked"), (8, 1152, 130, "gemv_mfma_fused_prepacked"),
            (16, 4096, 96, "gemv_mfma_prepacked"), (64, 512, 33, "gemv_mfma_prepacked"),
            (100, 384, 260, "gemm_mfma_prepacked"), (300, 1152, 1000, "gemm_mfma_prepacked"),
            # the decode-batch kernel's 4, 3 and 2 channel-block widths
-           (16, 256, 12304, "gemv_mfma_prepacked"), (40, 128, 9232, "gemv_mfma_prepacked"),
+           (16, 256, 12304, "gemv_mfma_fused_prepacked"), (40, 128, 9232, "gemv_mfma_prepacked"),
            (64, 256, 6160, "gemv_mfma_prepacked")]
 
 

@@ -161,7 +161,7 @@ def _sample(n, k, seed):
     return np.unique(np.concatenate([[0, n - 1], rng.choice(n, min(n, k) - 2, replace=False)]))
 
 
-@pytest.mark.parametrize("name,M,path", [("gemma", 1, "w8_gemv_dot4"), ("gemma", 8, "w8_gemv_mfma"),
+@pytest.mark.parametrize("name,M,path", [("gemma", 1, "w8_gemv_dot4"), ("gemma", 8, "w8_gemv_mfma_fused"),
                                          ("mlp7b", 1, "w8_gemv_dot4"),
                                          ("mlp7b", 16, "w8_gemv_mfma"),
                                          ("mlp7b", 64, "w8_gemv_mfma"),
