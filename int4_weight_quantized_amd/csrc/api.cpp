@@ -19,6 +19,14 @@ inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? W4_OK : W4_ERR_HIP; }
 
+// Status of a launch; the kernel variant's name is recorded only when the
+// launch succeeded (w4_last_path reports the last successful call).
+int launched(const char *path, hipError_t e) {
+    if (e != hipSuccess) return W4_ERR_HIP;
+    g_last_path = path;
+    return W4_OK;
+}
+
 // Workspace layout: [Xq: M*K bytes, 256-aligned][sx: 4*M bytes, 256-aligned].
 size_t ws_bytes(int64_t M, int64_t K) {
     return round_up((size_t)M * (size_t)K, 256) + round_up(4 * (size_t)M, 256);
@@ -60,7 +68,8 @@ int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const floa
     a.N = N;
     a.out = acc ? Out::I32 : Out::Y;
 
-    const bool aligned16 = aligned(packed, 16) && (src == Src::FP32 ? aligned(X, 16) : aligned(Xq, 16));
+    const bool aligned16 =
+        aligned(packed, 16) && (src == Src::FP32 ? aligned(X, 16) : aligned(Xq, 16));
     // (the shuffled layout is only accepted with K % 128 == 0 and aligned
     // tiles: the MFMA paths always apply, whatever the alignment of X)
     const bool fast = pp || (aligned16 && (K % 128 == 0));
@@ -72,8 +81,8 @@ int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const floa
     // Few rows: one VALU GEMV launch (activation quantization fused).
     if (aligned16 && gemv_dot4_ok(M, K, w8)) {
         if (src == Src::FP32) a.X = X;
-        g_last_path = w8 ? "w8_gemv_dot4" : pp ? "gemv_dot4_prepacked" : "gemv_dot4";
-        return hip_status(launch_gemv_dot4(a, st));
+        return launched(w8 ? "w8_gemv_dot4" : pp ? "gemv_dot4_prepacked" : "gemv_dot4",
+                        launch_gemv_dot4(a, st));
     }
     // Activations for the MFMA paths: P8 layout in the workspace (natural
     // layout for 8-bit weights, which then use pre-quantized input as is).
@@ -82,8 +91,10 @@ int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const floa
         // (one launch instead of two).
         if (src == Src::FP32 && !act_div && !acc && aligned(X, 16) && gemv_mfma_fused_ok(M, K)) {
             a.X = X;
-            g_last_path = w8 ? "w8_gemv_mfma_fused" : pp ? "gemv_mfma_fused_prepacked" : "gemv_mfma_fused";
-            return hip_status(launch_gemv_mfma_fused(a, st));
+            const char *path = w8   ? "w8_gemv_mfma_fused"
+                               : pp ? "gemv_mfma_fused_prepacked"
+                                    : "gemv_mfma_fused";
+            return launched(path, launch_gemv_mfma_fused(a, st));
         }
         // the MFMA GEMV takes the codes chunk-major, the GEMM row-major
         const bool step = M <= 64;
@@ -98,11 +109,11 @@ int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const floa
             a.Xq = ws_q;
         }
         if (M <= 64) {
-            g_last_path = w8 ? "w8_gemv_mfma" : pp ? "gemv_mfma_prepacked" : "gemv_mfma";
-            return hip_status(launch_gemv_mfma(a, st));
+            return launched(w8 ? "w8_gemv_mfma" : pp ? "gemv_mfma_prepacked" : "gemv_mfma",
+                            launch_gemv_mfma(a, st));
         }
-        g_last_path = w8 ? "w8_gemm_mfma" : pp ? "gemm_mfma_prepacked" : "gemm_mfma";
-        return hip_status(launch_gemm_mfma(a, st));
+        return launched(w8 ? "w8_gemm_mfma" : pp ? "gemm_mfma_prepacked" : "gemm_mfma",
+                        launch_gemm_mfma(a, st));
     }
     // Anything else: natural layout, one thread per output.
     if (src == Src::FP32) {
@@ -111,8 +122,7 @@ int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const floa
         a.Xq = ws_q;
         a.sx = ws_s;
     }
-    g_last_path = w8 ? "w8a8_generic" : "w4a8_generic";
-    return hip_status(launch_w4a8_generic(a, st));
+    return launched(w8 ? "w8a8_generic" : "w4a8_generic", launch_w4a8_generic(a, st));
 }
 
 int check_workspace(int64_t M, int64_t K, void *workspace, size_t bytes) {
@@ -163,17 +173,17 @@ int w4_quantize_weight(const float *W, int64_t K, int64_t N, int scheme, int64_t
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (scheme == W4_SYM_PER_CHANNEL) {
         if (group_size != 0 || zeros) return W4_ERR_SHAPE;
-        g_last_path = "quant_weight_sym";
-        return hip_status(w4::launch_quant_weight_sym(W, K, N, packed, scales, st));
+        return launched("quant_weight_sym",
+                        w4::launch_quant_weight_sym(W, K, N, packed, scales, st));
     }
     if (scheme == W4_ASYM_GROUP) {
         if (!zeros) return W4_ERR_NULL;
         if (!aligned(zeros, 4)) return W4_ERR_ALIGN;
         if (group_size < 2 || group_size % 2 != 0 || K % group_size != 0) return W4_ERR_SHAPE;
         if (K / group_size > 65535) return W4_ERR_SHAPE;
-        g_last_path = "quant_weight_asym";
-        return hip_status(
-            w4::launch_quant_weight_asym(W, K, N, group_size, packed, scales, zeros, st));
+        return launched("quant_weight_asym",
+                        w4::launch_quant_weight_asym(
+                            W, K, N, group_size, packed, scales, zeros, st));
     }
     return W4_ERR_SCHEME;
 }
@@ -206,11 +216,11 @@ int w4_dequantize_weight(const uint8_t *packed, const float *scales, const float
     if (rc != W4_OK) return rc;
     if (!W) return W4_ERR_NULL;
     if (!aligned(W, 4)) return W4_ERR_ALIGN;
-    g_last_path = "dequant_weight";
-    return hip_status(w4::launch_dequant_weight(packed, scales,
-                                                scheme == W4_ASYM_GROUP ? zeros : nullptr, K, N,
-                                                group_size, nullptr, W,
-                                                reinterpret_cast<hipStream_t>(stream)));
+    return launched("dequant_weight",
+                    w4::launch_dequant_weight(packed, scales,
+                                              scheme == W4_ASYM_GROUP ? zeros : nullptr, K, N,
+                                              group_size, nullptr, W,
+                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
 int w4_merge_delta(const uint8_t *packed, const float *scales, const float *zeros, int64_t K,
@@ -230,20 +240,21 @@ int w4_merge_delta(const uint8_t *packed, const float *scales, const float *zero
     hipError_t e = w4::launch_dequant_weight(packed, scales, asym ? zeros : nullptr, K, N,
                                              group_size, delta, work, st);
     if (e != hipSuccess) return W4_ERR_HIP;
-    g_last_path = "merge_delta";
     if (asym)
-        return hip_status(w4::launch_quant_weight_asym(work, K, N, group_size, packed_out,
-                                                       scales_out, zeros_out, st));
-    return hip_status(w4::launch_quant_weight_sym(work, K, N, packed_out, scales_out, st));
+        return launched("merge_delta",
+                        w4::launch_quant_weight_asym(work, K, N, group_size, packed_out,
+                                                     scales_out, zeros_out, st));
+    return launched("merge_delta",
+                    w4::launch_quant_weight_sym(work, K, N, packed_out, scales_out, st));
 }
 
 int a8_quantize_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *sx, void *stream) {
     if (!X || !Xq || !sx) return W4_ERR_NULL;
     if (M < 1 || K < 1 || M > 0x7FFFFFFF || K > ((int64_t)1 << 40) / M) return W4_ERR_SHAPE;
     if (!aligned(X, 4) || !aligned(sx, 4)) return W4_ERR_ALIGN;
-    g_last_path = "quant_act";
-    return hip_status(
-        w4::launch_quant_act(X, M, K, Xq, sx, false, reinterpret_cast<hipStream_t>(stream)));
+    return launched("quant_act",
+                    w4::launch_quant_act(
+                        X, M, K, Xq, sx, false, reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t w4a8_workspace_bytes(int64_t M, int64_t K, int64_t N) {
@@ -288,9 +299,9 @@ int awq_channel_scales(const float *Xcal, int64_t M, int64_t K, int alpha_num, i
     if (M < 1 || K < 1 || K > W4_MAX_K || M > ((int64_t)1 << 40) / K) return W4_ERR_SHAPE;
     if (alpha_num < 0 || alpha_num > 1024 || alpha_den < 1 || alpha_den > 1024) return W4_ERR_ARG;
     if (!aligned(Xcal, 4) || !aligned(s, 4)) return W4_ERR_ALIGN;
-    g_last_path = "awq_scales";
-    return hip_status(w4::launch_awq_scales(Xcal, M, K, alpha_num, alpha_den, s,
-                                            reinterpret_cast<hipStream_t>(stream)));
+    return launched("awq_scales",
+                    w4::launch_awq_scales(Xcal, M, K, alpha_num, alpha_den, s,
+                                          reinterpret_cast<hipStream_t>(stream)));
 }
 
 int awq_fold_weight(const float *W, int64_t K, int64_t N, const float *s, float *W_out,
@@ -298,9 +309,8 @@ int awq_fold_weight(const float *W, int64_t K, int64_t N, const float *s, float 
     if (!W || !s || !W_out) return W4_ERR_NULL;
     if (!shape_ok(1, K, N)) return W4_ERR_SHAPE;
     if (!aligned(W, 4) || !aligned(s, 4) || !aligned(W_out, 4)) return W4_ERR_ALIGN;
-    g_last_path = "awq_fold";
-    return hip_status(
-        w4::launch_awq_fold(W, K, N, s, W_out, reinterpret_cast<hipStream_t>(stream)));
+    return launched("awq_fold",
+                    w4::launch_awq_fold(W, K, N, s, W_out, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int awq_quantize_act(const float *X, int64_t M, int64_t K, const float *s, int8_t *Xq, float *sx,
@@ -308,9 +318,9 @@ int awq_quantize_act(const float *X, int64_t M, int64_t K, const float *s, int8_
     if (!X || !s || !Xq || !sx) return W4_ERR_NULL;
     if (M < 1 || K < 1 || M > 0x7FFFFFFF || K > ((int64_t)1 << 40) / M) return W4_ERR_SHAPE;
     if (!aligned(X, 4) || !aligned(sx, 4) || !aligned(s, 4)) return W4_ERR_ALIGN;
-    g_last_path = "awq_quant_act";
-    return hip_status(w4::launch_quant_act(X, M, K, Xq, sx, false,
-                                           reinterpret_cast<hipStream_t>(stream), s));
+    return launched("awq_quant_act",
+                    w4::launch_quant_act(X, M, K, Xq, sx, false,
+                                         reinterpret_cast<hipStream_t>(stream), s));
 }
 
 int awq_scale_act_bf16(const uint16_t *X_bf16, int64_t M, int64_t K, const float *s,
@@ -318,9 +328,9 @@ int awq_scale_act_bf16(const uint16_t *X_bf16, int64_t M, int64_t K, const float
     if (!X_bf16 || !s || !X_out) return W4_ERR_NULL;
     if (M < 1 || K < 1 || K > ((int64_t)1 << 40) / M) return W4_ERR_SHAPE;
     if (!aligned(X_bf16, 2) || !aligned(X_out, 2) || !aligned(s, 4)) return W4_ERR_ALIGN;
-    g_last_path = "awq_scale_bf16";
-    return hip_status(w4::launch_awq_scale_bf16(X_bf16, M, K, s, X_out,
-                                                reinterpret_cast<hipStream_t>(stream)));
+    return launched("awq_scale_bf16",
+                    w4::launch_awq_scale_bf16(X_bf16, M, K, s, X_out,
+                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
 int64_t w4_prepacked_weight_bytes(int64_t K, int64_t N) {
@@ -332,18 +342,18 @@ int w4_prepack_weights(const uint8_t *packed, int64_t K, int64_t N, uint8_t *wpp
     if (!packed || !wpp) return W4_ERR_NULL;
     if (!shape_ok(1, K, N) || K % 128 != 0) return W4_ERR_SHAPE;
     if (!aligned(packed, 16) || !aligned(wpp, 16)) return W4_ERR_ALIGN;
-    g_last_path = "w4_prepack_weights";
-    return hip_status(
-        w4::launch_w4_prepack_weights(packed, K, N, wpp, reinterpret_cast<hipStream_t>(stream)));
+    return launched("w4_prepack_weights",
+                    w4::launch_w4_prepack_weights(
+                        packed, K, N, wpp, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int w4_unprepack_weights(const uint8_t *wpp, int64_t K, int64_t N, uint8_t *packed, void *stream) {
     if (!packed || !wpp) return W4_ERR_NULL;
     if (!shape_ok(1, K, N) || K % 128 != 0) return W4_ERR_SHAPE;
     if (!aligned(packed, 16) || !aligned(wpp, 16)) return W4_ERR_ALIGN;
-    g_last_path = "w4_unprepack_weights";
-    return hip_status(w4::launch_w4_unprepack_weights(wpp, K, N, packed,
-                                                      reinterpret_cast<hipStream_t>(stream)));
+    return launched("w4_unprepack_weights",
+                    w4::launch_w4_unprepack_weights(wpp, K, N, packed,
+                                                    reinterpret_cast<hipStream_t>(stream)));
 }
 
 int w4a8_linear_prepacked(const float *X, int64_t M, int64_t K, int64_t N, const uint8_t *wpp,
@@ -400,9 +410,9 @@ int w8_quantize_weight(const float *W, int64_t K, int64_t N, int8_t *Wq, float *
     if (!W || !Wq || !sw) return W4_ERR_NULL;
     if (!shape_ok(1, K, N)) return W4_ERR_SHAPE;
     if (!aligned(W, 4) || !aligned(sw, 4)) return W4_ERR_ALIGN;
-    g_last_path = "quant_weight_w8";
-    return hip_status(
-        w4::launch_quant_weight_w8(W, K, N, Wq, sw, reinterpret_cast<hipStream_t>(stream)));
+    return launched("quant_weight_w8",
+                    w4::launch_quant_weight_w8(
+                        W, K, N, Wq, sw, reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t w8a8_workspace_bytes(int64_t M, int64_t K, int64_t N) {
@@ -466,9 +476,9 @@ int w4a16_prepack(const uint8_t *packed, const float *scales, const float *zeros
     if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(zeros, 4) || !aligned(wpp, 16) ||
         !aligned(szpp, 16))
         return W4_ERR_ALIGN;
-    g_last_path = "w4a16_prepack";
-    return hip_status(w4::launch_w4a16_prepack(packed, scales, zeros, K, N, wpp, szpp,
-                                               reinterpret_cast<hipStream_t>(stream)));
+    return launched("w4a16_prepack",
+                    w4::launch_w4a16_prepack(packed, scales, zeros, K, N, wpp, szpp,
+                                             reinterpret_cast<hipStream_t>(stream)));
 }
 
 int w4a16_unprepack(const uint8_t *wpp, const float *szpp, int64_t K, int64_t N,
@@ -479,9 +489,9 @@ int w4a16_unprepack(const uint8_t *wpp, const float *szpp, int64_t K, int64_t N,
     if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(zeros, 4) || !aligned(wpp, 16) ||
         !aligned(szpp, 16))
         return W4_ERR_ALIGN;
-    g_last_path = "w4a16_unprepack";
-    return hip_status(w4::launch_w4a16_unprepack(wpp, szpp, K, N, packed, scales, zeros,
-                                                 reinterpret_cast<hipStream_t>(stream)));
+    return launched("w4a16_unprepack",
+                    w4::launch_w4a16_unprepack(wpp, szpp, K, N, packed, scales, zeros,
+                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
 int w4a16_linear_prepacked(const uint16_t *X_bf16, int64_t M, int64_t K, int64_t N,
@@ -490,9 +500,9 @@ int w4a16_linear_prepacked(const uint16_t *X_bf16, int64_t M, int64_t K, int64_t
     if (!shape_ok(M, K, N) || !prepacked_shape_ok(K, N, 128)) return W4_ERR_SHAPE;
     if (!aligned(X_bf16, 16) || !aligned(wpp, 16) || !aligned(szpp, 16) || !aligned(Y, 4))
         return W4_ERR_ALIGN;
-    g_last_path = "w4a16_lds_prepacked";
-    return hip_status(w4::launch_w4a16_prepacked(X_bf16, M, K, N, wpp, szpp, Y,
-                                                 reinterpret_cast<hipStream_t>(stream)));
+    return launched("w4a16_lds_prepacked",
+                    w4::launch_w4a16_prepacked(X_bf16, M, K, N, wpp, szpp, Y,
+                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
 int w4a16_linear(const uint16_t *X_bf16, int64_t M, int64_t K, int64_t N, const uint8_t *packed,
@@ -506,18 +516,17 @@ int w4a16_linear(const uint16_t *X_bf16, int64_t M, int64_t K, int64_t N, const 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (w4::w4a16_lds_ok(K, group_size) && aligned(X_bf16, 16) && aligned(packed, 16) &&
         aligned(scales, 16) && aligned(zeros, 16)) {
-        g_last_path = "w4a16_lds";
-        return hip_status(
-            w4::launch_w4a16_lds(X_bf16, M, K, N, packed, scales, zeros, Y, st));
+        return launched("w4a16_lds",
+                        w4::launch_w4a16_lds(X_bf16, M, K, N, packed, scales, zeros, Y, st));
     }
     if (w4::w4a16_fast_ok(M, K, N, group_size) && aligned(X_bf16, 16) && aligned(packed, 16)) {
-        g_last_path = "w4a16_mfma";
-        return hip_status(
-            w4::launch_w4a16_mfma(X_bf16, M, K, N, packed, scales, zeros, group_size, Y, st));
+        return launched("w4a16_mfma",
+                        w4::launch_w4a16_mfma(
+                            X_bf16, M, K, N, packed, scales, zeros, group_size, Y, st));
     }
-    g_last_path = "w4a16_generic";
-    return hip_status(
-        w4::launch_w4a16_generic(X_bf16, M, K, N, packed, scales, zeros, group_size, Y, st));
+    return launched("w4a16_generic",
+                    w4::launch_w4a16_generic(
+                        X_bf16, M, K, N, packed, scales, zeros, group_size, Y, st));
 }
 
 }  // extern "C"
