@@ -136,7 +136,11 @@ def w4a8_workspace_bytes(M: int, K: int, N: int) -> int:
 
 
 # ------------------------------------------------------------------ helpers
-def _dev(t: torch.Tensor, name: str, dtype) -> int:
+def _dev(t: torch.Tensor, name: str, dtype, shape=None, device=None) -> int:
+    """Device pointer of t after checking what the C side cannot: the kernels
+    take raw pointers and trust the sizes, so every tensor is checked against
+    the exact shape the call implies (and against the device of the call's
+    first operand)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
     if not t.is_cuda:
@@ -145,11 +149,31 @@ def _dev(t: torch.Tensor, name: str, dtype) -> int:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call's operands on {device}")
     return t.data_ptr()
 
 
-def _opt(t, name, dtype):
-    return None if t is None else _dev(t, name, dtype)
+def _opt(t, name, dtype, shape=None, device=None):
+    return None if t is None else _dev(t, name, dtype, shape, device)
+
+
+_HALF_DTYPES = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _half(t: torch.Tensor, name: str, shape=None, device=None) -> int:
+    """bf16 activations, or their 16-bit patterns as int16 / uint16."""
+    if not isinstance(t, torch.Tensor) or t.dtype not in _HALF_DTYPES:
+        raise TypeError(f"{name} must be a bfloat16 (or int16 / uint16 bit-pattern) tensor")
+    return _dev(t, name, t.dtype, shape, device)
+
+
+def _matrix(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor")
+    return t.shape
 
 
 def _stream(stream) -> int:
@@ -177,23 +201,26 @@ def w4_quantize_weight(W: torch.Tensor, scheme: str = "sym", group_size: int = 0
 
     ``scheme="sym"``: scales [N], zeros None.  ``scheme="asym"``: scales and
     zeros [N, K/group_size]."""
-    K, N = W.shape
+    K, N = _matrix(W, "W")
     sch = {"sym": W4_SYM_PER_CHANNEL, "asym": W4_ASYM_GROUP}.get(scheme, -1)
     dev = W.device
     if packed is None:
         packed = torch.empty((N, (K + 1) // 2), dtype=torch.uint8, device=dev)
+    tshape = None
     if sch == W4_ASYM_GROUP and group_size > 0:
-        G = K // group_size
+        tshape = (N, K // group_size)
         if scales is None:
-            scales = torch.empty((N, G), dtype=torch.float32, device=dev)
+            scales = torch.empty(tshape, dtype=torch.float32, device=dev)
         if zeros is None:
-            zeros = torch.empty((N, G), dtype=torch.float32, device=dev)
-    elif scales is None:
-        scales = torch.empty((N,), dtype=torch.float32, device=dev)
+            zeros = torch.empty(tshape, dtype=torch.float32, device=dev)
+    else:
+        tshape = (N,)
+        if scales is None:
+            scales = torch.empty(tshape, dtype=torch.float32, device=dev)
     rc = lib().w4_quantize_weight(_dev(W, "W", torch.float32), K, N, sch, group_size,
-                                  _dev(packed, "packed", torch.uint8),
-                                  _dev(scales, "scales", torch.float32),
-                                  _opt(zeros, "zeros", torch.float32), _stream(stream))
+                                  _dev(packed, "packed", torch.uint8, (N, (K + 1) // 2), dev),
+                                  _dev(scales, "scales", torch.float32, tshape, dev),
+                                  _opt(zeros, "zeros", torch.float32, tshape, dev), _stream(stream))
     _check("w4_quantize_weight", rc)
     return packed, scales, zeros
 
@@ -202,16 +229,29 @@ def _scheme(scheme: str) -> int:
     return {"sym": W4_SYM_PER_CHANNEL, "asym": W4_ASYM_GROUP}.get(scheme, -1)
 
 
+def _table_shape(scheme: str, N: int, K: int, group_size: int):
+    """Shape of the scale / zero-point tables, or None where the C side
+    rejects the arguments anyway (before launching anything)."""
+    if scheme == "sym":
+        return (N,)
+    if group_size > 0 and K % group_size == 0:
+        return (N, K // group_size)
+    return None
+
+
 def w4_dequantize_weight(packed: torch.Tensor, scales: torch.Tensor, zeros, K: int,
                          scheme: str = "sym", group_size: int = 0, W=None, stream=None):
     """packed [N, ceil(K/2)] (+ scales, zeros) -> W [K, N] fp32."""
-    N = packed.shape[0]
+    N = _matrix(packed, "packed")[0]
+    dev = packed.device
+    ts = _table_shape(scheme, N, K, group_size)
     if W is None:
-        W = torch.empty((K, N), dtype=torch.float32, device=packed.device)
-    rc = lib().w4_dequantize_weight(_dev(packed, "packed", torch.uint8),
-                                    _dev(scales, "scales", torch.float32),
-                                    _opt(zeros, "zeros", torch.float32), K, N, _scheme(scheme),
-                                    group_size, _dev(W, "W", torch.float32), _stream(stream))
+        W = torch.empty((K, N), dtype=torch.float32, device=dev)
+    rc = lib().w4_dequantize_weight(_dev(packed, "packed", torch.uint8, (N, (K + 1) // 2)),
+                                    _dev(scales, "scales", torch.float32, ts, dev),
+                                    _opt(zeros, "zeros", torch.float32, ts, dev), K, N,
+                                    _scheme(scheme), group_size,
+                                    _dev(W, "W", torch.float32, (K, N), dev), _stream(stream))
     _check("w4_dequantize_weight", rc)
     return W
 
@@ -221,35 +261,40 @@ def w4_merge_delta(packed: torch.Tensor, scales: torch.Tensor, zeros, delta: tor
                    work=None, stream=None):
     """Requantize dequant(packed) + delta [K, N]; returns (packed, scales, zeros),
     new tensors unless in_place (then the inputs are overwritten)."""
-    K, N = delta.shape
+    K, N = _matrix(delta, "delta")
+    dev = delta.device
+    ts = _table_shape(scheme, N, K, group_size)
     if in_place:
         po, so, zo = packed, scales, zeros
     else:
         po, so = torch.empty_like(packed), torch.empty_like(scales)
         zo = None if zeros is None else torch.empty_like(zeros)
     if work is None:
-        work = torch.empty((K, N), dtype=torch.float32, device=packed.device)
-    rc = lib().w4_merge_delta(_dev(packed, "packed", torch.uint8),
-                              _dev(scales, "scales", torch.float32),
-                              _opt(zeros, "zeros", torch.float32), K, N, _scheme(scheme),
+        work = torch.empty((K, N), dtype=torch.float32, device=dev)
+    pshape = (N, (K + 1) // 2)
+    rc = lib().w4_merge_delta(_dev(packed, "packed", torch.uint8, pshape, dev),
+                              _dev(scales, "scales", torch.float32, ts, dev),
+                              _opt(zeros, "zeros", torch.float32, ts, dev), K, N, _scheme(scheme),
                               group_size, _dev(delta, "delta", torch.float32),
-                              _dev(po, "packed_out", torch.uint8),
-                              _dev(so, "scales_out", torch.float32),
-                              _opt(zo, "zeros_out", torch.float32),
-                              _dev(work, "work", torch.float32), _stream(stream))
+                              _dev(po, "packed_out", torch.uint8, pshape, dev),
+                              _dev(so, "scales_out", torch.float32, ts, dev),
+                              _opt(zo, "zeros_out", torch.float32, ts, dev),
+                              _dev(work, "work", torch.float32, (K, N), dev), _stream(stream))
     _check("w4_merge_delta", rc)
     return po, so, zo
 
 
 def a8_quantize_act(X: torch.Tensor, Xq=None, sx=None, stream=None):
     """X [M, K] fp32 -> (Xq int8 [M, K], sx fp32 [M])."""
-    M, K = X.shape
+    M, K = _matrix(X, "X")
+    dev = X.device
     if Xq is None:
-        Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+        Xq = torch.empty((M, K), dtype=torch.int8, device=dev)
     if sx is None:
-        sx = torch.empty((M,), dtype=torch.float32, device=X.device)
-    rc = lib().a8_quantize_act(_dev(X, "X", torch.float32), M, K, _dev(Xq, "Xq", torch.int8),
-                               _dev(sx, "sx", torch.float32), _stream(stream))
+        sx = torch.empty((M,), dtype=torch.float32, device=dev)
+    rc = lib().a8_quantize_act(_dev(X, "X", torch.float32), M, K,
+                               _dev(Xq, "Xq", torch.int8, (M, K), dev),
+                               _dev(sx, "sx", torch.float32, (M,), dev), _stream(stream))
     _check("a8_quantize_act", rc)
     return Xq, sx
 
@@ -257,15 +302,18 @@ def a8_quantize_act(X: torch.Tensor, Xq=None, sx=None, stream=None):
 def w4a8_linear(X: torch.Tensor, packed: torch.Tensor, sw: torch.Tensor, bias=None, Y=None,
                 workspace=None, stream=None) -> torch.Tensor:
     """Y [M, N] fp32 = dequant(quant(X) . unpack(packed)) (+ bias)."""
-    M, K = X.shape
-    N = packed.shape[0]
+    M, K = _matrix(X, "X")
+    N = _matrix(packed, "packed")[0]
+    dev = X.device
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
     workspace, need = _workspace(M, K, N, X.device, workspace)
     rc = lib().w4a8_linear(_dev(X, "X", torch.float32), M, K, N,
-                           _dev(packed, "packed", torch.uint8), _dev(sw, "sw", torch.float32),
-                           _opt(bias, "bias", torch.float32), _dev(Y, "Y", torch.float32),
-                           _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                           _dev(packed, "packed", torch.uint8, (N, (K + 1) // 2), dev),
+                           _dev(sw, "sw", torch.float32, (N,), dev),
+                           _opt(bias, "bias", torch.float32, (N,), dev),
+                           _dev(Y, "Y", torch.float32, (M, N), dev),
+                           _dev(workspace, "workspace", torch.uint8, None, dev), workspace.numel(),
                            _stream(stream))
     _check("w4a8_linear", rc)
     return Y
@@ -280,62 +328,70 @@ def _act(activation) -> int:
 def w4a8_linear_act(X: torch.Tensor, packed: torch.Tensor, sw: torch.Tensor, bias=None,
                     activation="relu", Y=None, workspace=None, stream=None) -> torch.Tensor:
     """Y [M, N] fp32 = act(dequant(quant(X) . unpack(packed)) (+ bias)), one fused epilogue."""
-    M, K = X.shape
-    N = packed.shape[0]
+    M, K = _matrix(X, "X")
+    N = _matrix(packed, "packed")[0]
+    dev = X.device
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
     workspace, need = _workspace(M, K, N, X.device, workspace)
     rc = lib().w4a8_linear_act(_dev(X, "X", torch.float32), M, K, N,
-                               _dev(packed, "packed", torch.uint8), _dev(sw, "sw", torch.float32),
-                               _opt(bias, "bias", torch.float32), _act(activation),
-                               _dev(Y, "Y", torch.float32),
-                               _dev(workspace, "workspace", torch.uint8), workspace.numel(),
-                               _stream(stream))
+                               _dev(packed, "packed", torch.uint8, (N, (K + 1) // 2), dev),
+                               _dev(sw, "sw", torch.float32, (N,), dev),
+                               _opt(bias, "bias", torch.float32, (N,), dev), _act(activation),
+                               _dev(Y, "Y", torch.float32, (M, N), dev),
+                               _dev(workspace, "workspace", torch.uint8, None, dev),
+                               workspace.numel(), _stream(stream))
     _check("w4a8_linear_act", rc)
     return Y
 
 
 def w4a8_linear_q(Xq: torch.Tensor, sx: torch.Tensor, packed: torch.Tensor, sw: torch.Tensor,
                   bias=None, Y=None, workspace=None, stream=None) -> torch.Tensor:
-    M, K = Xq.shape
-    N = packed.shape[0]
+    M, K = _matrix(Xq, "Xq")
+    N = _matrix(packed, "packed")[0]
+    dev = Xq.device
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
     workspace, need = _workspace(M, K, N, Xq.device, workspace)
-    rc = lib().w4a8_linear_q(_dev(Xq, "Xq", torch.int8), _dev(sx, "sx", torch.float32),
-                             _dev(packed, "packed", torch.uint8), _dev(sw, "sw", torch.float32),
-                             _opt(bias, "bias", torch.float32), M, K, N,
-                             _dev(Y, "Y", torch.float32),
-                             _dev(workspace, "workspace", torch.uint8), workspace.numel(),
-                             _stream(stream))
+    rc = lib().w4a8_linear_q(_dev(Xq, "Xq", torch.int8), _dev(sx, "sx", torch.float32, (M,), dev),
+                             _dev(packed, "packed", torch.uint8, (N, (K + 1) // 2), dev),
+                             _dev(sw, "sw", torch.float32, (N,), dev),
+                             _opt(bias, "bias", torch.float32, (N,), dev), M, K, N,
+                             _dev(Y, "Y", torch.float32, (M, N), dev),
+                             _dev(workspace, "workspace", torch.uint8, None, dev),
+                             workspace.numel(), _stream(stream))
     _check("w4a8_linear_q", rc)
     return Y
 
 
 def w4a8_matmul_i32(Xq: torch.Tensor, packed: torch.Tensor, acc=None, workspace=None,
                     stream=None) -> torch.Tensor:
-    M, K = Xq.shape
-    N = packed.shape[0]
+    M, K = _matrix(Xq, "Xq")
+    N = _matrix(packed, "packed")[0]
+    dev = Xq.device
     if acc is None:
         acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
     workspace, need = _workspace(M, K, N, Xq.device, workspace)
-    rc = lib().w4a8_matmul_i32(_dev(Xq, "Xq", torch.int8), _dev(packed, "packed", torch.uint8),
-                               M, K, N, _dev(acc, "acc", torch.int32),
-                               _dev(workspace, "workspace", torch.uint8), workspace.numel(),
-                               _stream(stream))
+    rc = lib().w4a8_matmul_i32(_dev(Xq, "Xq", torch.int8),
+                               _dev(packed, "packed", torch.uint8, (N, (K + 1) // 2), dev), M, K, N,
+                               _dev(acc, "acc", torch.int32, (M, N), dev),
+                               _dev(workspace, "workspace", torch.uint8, None, dev),
+                               workspace.numel(), _stream(stream))
     _check("w4a8_matmul_i32", rc)
     return acc
 
 
 def w8_quantize_weight(W: torch.Tensor, Wq=None, sw=None, stream=None):
     """W [K, N] fp32 -> (Wq int8 [N, K], sw fp32 [N])."""
-    K, N = W.shape
+    K, N = _matrix(W, "W")
+    dev = W.device
     if Wq is None:
         Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
     if sw is None:
         sw = torch.empty((N,), dtype=torch.float32, device=W.device)
-    rc = lib().w8_quantize_weight(_dev(W, "W", torch.float32), K, N, _dev(Wq, "Wq", torch.int8),
-                                  _dev(sw, "sw", torch.float32), _stream(stream))
+    rc = lib().w8_quantize_weight(_dev(W, "W", torch.float32), K, N,
+                                  _dev(Wq, "Wq", torch.int8, (N, K), dev),
+                                  _dev(sw, "sw", torch.float32, (N,), dev), _stream(stream))
     _check("w8_quantize_weight", rc)
     return Wq, sw
 
@@ -343,15 +399,18 @@ def w8_quantize_weight(W: torch.Tensor, Wq=None, sw=None, stream=None):
 def w8a8_linear(X: torch.Tensor, Wq: torch.Tensor, sw: torch.Tensor, bias=None, Y=None,
                 workspace=None, stream=None) -> torch.Tensor:
     """Y [M, N] fp32 = dequant(quant(X) . Wq^T) (+ bias)."""
-    M, K = X.shape
-    N = Wq.shape[0]
+    M, K = _matrix(X, "X")
+    N = _matrix(Wq, "Wq")[0]
+    dev = X.device
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
     workspace, need = _workspace(M, K, N, X.device, workspace)
-    rc = lib().w8a8_linear(_dev(X, "X", torch.float32), M, K, N, _dev(Wq, "Wq", torch.int8),
-                           _dev(sw, "sw", torch.float32), _opt(bias, "bias", torch.float32),
-                           _dev(Y, "Y", torch.float32),
-                           _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+    rc = lib().w8a8_linear(_dev(X, "X", torch.float32), M, K, N,
+                           _dev(Wq, "Wq", torch.int8, (N, K), dev),
+                           _dev(sw, "sw", torch.float32, (N,), dev),
+                           _opt(bias, "bias", torch.float32, (N,), dev),
+                           _dev(Y, "Y", torch.float32, (M, N), dev),
+                           _dev(workspace, "workspace", torch.uint8, None, dev), workspace.numel(),
                            _stream(stream))
     _check("w8a8_linear", rc)
     return Y
@@ -360,79 +419,89 @@ def w8a8_linear(X: torch.Tensor, Wq: torch.Tensor, sw: torch.Tensor, bias=None, 
 def w8a8_linear_act(X: torch.Tensor, Wq: torch.Tensor, sw: torch.Tensor, bias=None,
                     activation="relu", Y=None, workspace=None, stream=None) -> torch.Tensor:
     """Y [M, N] fp32 = act(dequant(quant(X) . Wq^T) (+ bias)), one fused epilogue."""
-    M, K = X.shape
-    N = Wq.shape[0]
+    M, K = _matrix(X, "X")
+    N = _matrix(Wq, "Wq")[0]
+    dev = X.device
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
     workspace, need = _workspace(M, K, N, X.device, workspace)
-    rc = lib().w8a8_linear_act(_dev(X, "X", torch.float32), M, K, N, _dev(Wq, "Wq", torch.int8),
-                               _dev(sw, "sw", torch.float32), _opt(bias, "bias", torch.float32),
-                               _act(activation), _dev(Y, "Y", torch.float32),
-                               _dev(workspace, "workspace", torch.uint8), workspace.numel(),
-                               _stream(stream))
+    rc = lib().w8a8_linear_act(_dev(X, "X", torch.float32), M, K, N,
+                               _dev(Wq, "Wq", torch.int8, (N, K), dev),
+                               _dev(sw, "sw", torch.float32, (N,), dev),
+                               _opt(bias, "bias", torch.float32, (N,), dev), _act(activation),
+                               _dev(Y, "Y", torch.float32, (M, N), dev),
+                               _dev(workspace, "workspace", torch.uint8, None, dev),
+                               workspace.numel(), _stream(stream))
     _check("w8a8_linear_act", rc)
     return Y
 
 
 def w8a8_matmul_i32(Xq: torch.Tensor, Wq: torch.Tensor, acc=None, workspace=None,
                     stream=None) -> torch.Tensor:
-    M, K = Xq.shape
-    N = Wq.shape[0]
+    M, K = _matrix(Xq, "Xq")
+    N = _matrix(Wq, "Wq")[0]
+    dev = Xq.device
     if acc is None:
         acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
     workspace, need = _workspace(M, K, N, Xq.device, workspace)
-    rc = lib().w8a8_matmul_i32(_dev(Xq, "Xq", torch.int8), _dev(Wq, "Wq", torch.int8), M, K, N,
-                               _dev(acc, "acc", torch.int32),
-                               _dev(workspace, "workspace", torch.uint8), workspace.numel(),
-                               _stream(stream))
+    rc = lib().w8a8_matmul_i32(_dev(Xq, "Xq", torch.int8), _dev(Wq, "Wq", torch.int8, (N, K), dev),
+                               M, K, N, _dev(acc, "acc", torch.int32, (M, N), dev),
+                               _dev(workspace, "workspace", torch.uint8, None, dev),
+                               workspace.numel(), _stream(stream))
     _check("w8a8_matmul_i32", rc)
     return acc
 
 
 def awq_channel_scales(Xcal: torch.Tensor, alpha=(1, 2), s=None, stream=None) -> torch.Tensor:
     """Calibration activations [M, K] fp32 -> power-of-two channel scales s [K]."""
-    M, K = Xcal.shape
+    M, K = _matrix(Xcal, "Xcal")
     if s is None:
         s = torch.empty((K,), dtype=torch.float32, device=Xcal.device)
     rc = lib().awq_channel_scales(_dev(Xcal, "Xcal", torch.float32), M, K, int(alpha[0]),
-                                  int(alpha[1]), _dev(s, "s", torch.float32), _stream(stream))
+                                  int(alpha[1]), _dev(s, "s", torch.float32, (K,), Xcal.device),
+                                  _stream(stream))
     _check("awq_channel_scales", rc)
     return s
 
 
 def awq_fold_weight(W: torch.Tensor, s: torch.Tensor, W_out=None, stream=None) -> torch.Tensor:
     """W [K, N] -> W diag(s) (W_out may be W)."""
-    K, N = W.shape
+    K, N = _matrix(W, "W")
+    dev = W.device
     if W_out is None:
         W_out = torch.empty_like(W)
-    rc = lib().awq_fold_weight(_dev(W, "W", torch.float32), K, N, _dev(s, "s", torch.float32),
-                               _dev(W_out, "W_out", torch.float32), _stream(stream))
+    rc = lib().awq_fold_weight(_dev(W, "W", torch.float32), K, N,
+                               _dev(s, "s", torch.float32, (K,), dev),
+                               _dev(W_out, "W_out", torch.float32, (K, N), dev), _stream(stream))
     _check("awq_fold_weight", rc)
     return W_out
 
 
 def awq_quantize_act(X: torch.Tensor, s: torch.Tensor, Xq=None, sx=None, stream=None):
     """(Xq, sx) of X / s (per column)."""
-    M, K = X.shape
+    M, K = _matrix(X, "X")
+    dev = X.device
     if Xq is None:
-        Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+        Xq = torch.empty((M, K), dtype=torch.int8, device=dev)
     if sx is None:
-        sx = torch.empty((M,), dtype=torch.float32, device=X.device)
-    rc = lib().awq_quantize_act(_dev(X, "X", torch.float32), M, K, _dev(s, "s", torch.float32),
-                                _dev(Xq, "Xq", torch.int8), _dev(sx, "sx", torch.float32),
-                                _stream(stream))
+        sx = torch.empty((M,), dtype=torch.float32, device=dev)
+    rc = lib().awq_quantize_act(_dev(X, "X", torch.float32), M, K,
+                                _dev(s, "s", torch.float32, (K,), dev),
+                                _dev(Xq, "Xq", torch.int8, (M, K), dev),
+                                _dev(sx, "sx", torch.float32, (M,), dev), _stream(stream))
     _check("awq_quantize_act", rc)
     return Xq, sx
 
 
 def awq_scale_act_bf16(X_bf16: torch.Tensor, s: torch.Tensor, X_out=None, stream=None):
     """bf16 (or int16 bit-pattern) activations divided by s per column."""
-    M, K = X_bf16.shape
+    M, K = _matrix(X_bf16, "X_bf16")
+    dev = X_bf16.device
     if X_out is None:
         X_out = torch.empty_like(X_bf16)
-    dt = X_bf16.dtype
-    rc = lib().awq_scale_act_bf16(_dev(X_bf16, "X_bf16", dt), M, K, _dev(s, "s", torch.float32),
-                                  _dev(X_out, "X_out", dt), _stream(stream))
+    rc = lib().awq_scale_act_bf16(_half(X_bf16, "X_bf16"), M, K,
+                                  _dev(s, "s", torch.float32, (K,), dev),
+                                  _half(X_out, "X_out", (M, K), dev), _stream(stream))
     _check("awq_scale_act_bf16", rc)
     return X_out
 
@@ -441,24 +510,27 @@ def w4a8_linear_awq(X: torch.Tensor, packed: torch.Tensor, sw: torch.Tensor, s: 
                     bias=None, activation=None, Y=None, workspace=None,
                     stream=None) -> torch.Tensor:
     """Y = act(dequant(quant(X / s) . unpack(packed)) (+ bias)); packed, sw from W diag(s)."""
-    M, K = X.shape
-    N = packed.shape[0]
+    M, K = _matrix(X, "X")
+    N = _matrix(packed, "packed")[0]
+    dev = X.device
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
     workspace, need = _workspace(M, K, N, X.device, workspace)
     rc = lib().w4a8_linear_awq(_dev(X, "X", torch.float32), M, K, N,
-                               _dev(packed, "packed", torch.uint8), _dev(sw, "sw", torch.float32),
-                               _dev(s, "s", torch.float32), _opt(bias, "bias", torch.float32),
-                               _act(activation), _dev(Y, "Y", torch.float32),
-                               _dev(workspace, "workspace", torch.uint8), workspace.numel(),
-                               _stream(stream))
+                               _dev(packed, "packed", torch.uint8, (N, (K + 1) // 2), dev),
+                               _dev(sw, "sw", torch.float32, (N,), dev),
+                               _dev(s, "s", torch.float32, (K,), dev),
+                               _opt(bias, "bias", torch.float32, (N,), dev), _act(activation),
+                               _dev(Y, "Y", torch.float32, (M, N), dev),
+                               _dev(workspace, "workspace", torch.uint8, None, dev),
+                               workspace.numel(), _stream(stream))
     _check("w4a8_linear_awq", rc)
     return Y
 
 
 def w4_prepack_weights(packed: torch.Tensor, stream=None) -> torch.Tensor:
     """Packed int4 codes [N, K/2] -> the shuffled tiles (uint8, flat)."""
-    N, KB = packed.shape
+    N, KB = _matrix(packed, "packed")
     K = 2 * KB
     nb = int(lib().w4_prepacked_weight_bytes(K, N))
     if nb == 0:
@@ -471,8 +543,11 @@ def w4_prepack_weights(packed: torch.Tensor, stream=None) -> torch.Tensor:
 
 
 def w4_unprepack_weights(wpp: torch.Tensor, K: int, N: int, stream=None) -> torch.Tensor:
+    nb = int(lib().w4_prepacked_weight_bytes(K, N))
+    if nb == 0:
+        raise ValueError("the shuffled layout needs K % 128 == 0")
     packed = torch.empty((N, K // 2), dtype=torch.uint8, device=wpp.device)
-    rc = lib().w4_unprepack_weights(_dev(wpp, "wpp", torch.uint8), K, N,
+    rc = lib().w4_unprepack_weights(_dev(wpp, "wpp", torch.uint8, (nb,)), K, N,
                                     _dev(packed, "packed", torch.uint8), _stream(stream))
     _check("w4_unprepack_weights", rc)
     return packed
@@ -481,17 +556,20 @@ def w4_unprepack_weights(wpp: torch.Tensor, K: int, N: int, stream=None) -> torc
 def w4a8_linear_prepacked(X: torch.Tensor, wpp: torch.Tensor, sw: torch.Tensor, bias=None,
                           activation=None, Y=None, workspace=None, stream=None) -> torch.Tensor:
     """The W4A8 forward on the shuffled int4 tiles; N = sw.numel()."""
-    M, K = X.shape
+    M, K = _matrix(X, "X")
     N = sw.shape[0]
+    dev = X.device
+    nb = int(lib().w4_prepacked_weight_bytes(K, N))
     if Y is None:
-        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
-    workspace, need = _workspace(M, K, N, X.device, workspace)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    workspace, need = _workspace(M, K, N, dev, workspace)
     rc = lib().w4a8_linear_prepacked(_dev(X, "X", torch.float32), M, K, N,
-                                     _dev(wpp, "wpp", torch.uint8), _dev(sw, "sw", torch.float32),
-                                     _opt(bias, "bias", torch.float32), _act(activation),
-                                     _dev(Y, "Y", torch.float32),
-                                     _dev(workspace, "workspace", torch.uint8), workspace.numel(),
-                                     _stream(stream))
+                                     _dev(wpp, "wpp", torch.uint8, (nb,) if nb else None, dev),
+                                     _dev(sw, "sw", torch.float32, (N,), dev),
+                                     _opt(bias, "bias", torch.float32, (N,), dev), _act(activation),
+                                     _dev(Y, "Y", torch.float32, (M, N), dev),
+                                     _dev(workspace, "workspace", torch.uint8, None, dev),
+                                     workspace.numel(), _stream(stream))
     _check("w4a8_linear_prepacked", rc)
     return Y
 
@@ -499,19 +577,20 @@ def w4a8_linear_prepacked(X: torch.Tensor, wpp: torch.Tensor, sw: torch.Tensor, 
 def w4a16_prepack(packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
                   group_size: int = 128, stream=None):
     """Canonical W4A16 tensors -> (wpp uint8, szpp fp32), the GPU-shuffled layout."""
-    N, KB = packed.shape
+    N, KB = _matrix(packed, "packed")
     K = 2 * KB
+    dev = packed.device
     nw = int(lib().w4a16_prepacked_weight_bytes(K, N))
     nt = int(lib().w4a16_prepacked_table_floats(K, N))
     if nw == 0 or group_size != 128:
         raise ValueError("the shuffled layout needs group_size 128 and K % 512 == 0")
-    wpp = torch.empty((nw,), dtype=torch.uint8, device=packed.device)
-    szpp = torch.empty((nt,), dtype=torch.float32, device=packed.device)
+    wpp = torch.empty((nw,), dtype=torch.uint8, device=dev)
+    szpp = torch.empty((nt,), dtype=torch.float32, device=dev)
     rc = lib().w4a16_prepack(_dev(packed, "packed", torch.uint8),
-                             _dev(scales, "scales", torch.float32),
-                             _dev(zeros, "zeros", torch.float32), K, N, group_size,
-                             _dev(wpp, "wpp", torch.uint8), _dev(szpp, "szpp", torch.float32),
-                             _stream(stream))
+                             _dev(scales, "scales", torch.float32, (N, K // 128), dev),
+                             _dev(zeros, "zeros", torch.float32, (N, K // 128), dev), K, N,
+                             group_size, _dev(wpp, "wpp", torch.uint8),
+                             _dev(szpp, "szpp", torch.float32), _stream(stream))
     _check("w4a16_prepack", rc)
     return wpp, szpp
 
@@ -520,11 +599,16 @@ def w4a16_unprepack(wpp: torch.Tensor, szpp: torch.Tensor, K: int, N: int,
                     group_size: int = 128, stream=None):
     """(wpp, szpp) -> canonical (packed [N, K/2], scales, zeros [N, K/128])."""
     dev = wpp.device
+    nw = int(lib().w4a16_prepacked_weight_bytes(K, N))
+    nt = int(lib().w4a16_prepacked_table_floats(K, N))
+    if nw == 0 or group_size != 128:
+        raise ValueError("the shuffled layout needs group_size 128 and K % 512 == 0")
     packed = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
     scales = torch.empty((N, K // 128), dtype=torch.float32, device=dev)
     zeros = torch.empty((N, K // 128), dtype=torch.float32, device=dev)
-    rc = lib().w4a16_unprepack(_dev(wpp, "wpp", torch.uint8), _dev(szpp, "szpp", torch.float32),
-                               K, N, group_size, _dev(packed, "packed", torch.uint8),
+    rc = lib().w4a16_unprepack(_dev(wpp, "wpp", torch.uint8, (nw,)),
+                               _dev(szpp, "szpp", torch.float32, (nt,), dev), K, N, group_size,
+                               _dev(packed, "packed", torch.uint8),
                                _dev(scales, "scales", torch.float32),
                                _dev(zeros, "zeros", torch.float32), _stream(stream))
     _check("w4a16_unprepack", rc)
@@ -534,13 +618,16 @@ def w4a16_unprepack(wpp: torch.Tensor, szpp: torch.Tensor, K: int, N: int,
 def w4a16_linear_prepacked(X_bf16: torch.Tensor, wpp: torch.Tensor, szpp: torch.Tensor, N: int,
                            Y=None, stream=None) -> torch.Tensor:
     """The W4A16 forward on the shuffled layout; X_bf16 [M, K] bf16 / 16-bit patterns."""
-    M, K = X_bf16.shape
+    M, K = _matrix(X_bf16, "X_bf16")
+    dev = X_bf16.device
+    nw = int(lib().w4a16_prepacked_weight_bytes(K, N))
+    nt = int(lib().w4a16_prepacked_table_floats(K, N))
     if Y is None:
-        Y = torch.empty((M, N), dtype=torch.float32, device=X_bf16.device)
-    rc = lib().w4a16_linear_prepacked(_dev(X_bf16, "X_bf16", X_bf16.dtype), M, K, N,
-                                      _dev(wpp, "wpp", torch.uint8),
-                                      _dev(szpp, "szpp", torch.float32),
-                                      _dev(Y, "Y", torch.float32), _stream(stream))
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    rc = lib().w4a16_linear_prepacked(_half(X_bf16, "X_bf16"), M, K, N,
+                                      _dev(wpp, "wpp", torch.uint8, (nw,) if nw else None, dev),
+                                      _dev(szpp, "szpp", torch.float32, (nt,) if nt else None, dev),
+                                      _dev(Y, "Y", torch.float32, (M, N), dev), _stream(stream))
     _check("w4a16_linear_prepacked", rc)
     return Y
 
@@ -548,19 +635,17 @@ def w4a16_linear_prepacked(X_bf16: torch.Tensor, wpp: torch.Tensor, szpp: torch.
 def w4a16_linear(X_bf16: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
                  zeros: torch.Tensor, group_size: int, Y=None, stream=None) -> torch.Tensor:
     """X_bf16 [M, K] (torch.bfloat16, or int16/uint16 bit patterns) -> Y [M, N] fp32."""
-    M, K = X_bf16.shape
-    N = packed.shape[0]
-    if X_bf16.dtype == torch.bfloat16:
-        xptr = _dev(X_bf16, "X_bf16", torch.bfloat16)
-    elif X_bf16.dtype == torch.int16:
-        xptr = _dev(X_bf16, "X_bf16", torch.int16)
-    else:
-        xptr = _dev(X_bf16, "X_bf16", torch.uint16)
+    M, K = _matrix(X_bf16, "X_bf16")
+    N = _matrix(packed, "packed")[0]
+    dev = X_bf16.device
+    xptr = _half(X_bf16, "X_bf16")
+    ts = _table_shape("asym", N, K, group_size)
     if Y is None:
-        Y = torch.empty((M, N), dtype=torch.float32, device=X_bf16.device)
-    rc = lib().w4a16_linear(xptr, M, K, N, _dev(packed, "packed", torch.uint8),
-                            _dev(scales, "scales", torch.float32),
-                            _dev(zeros, "zeros", torch.float32), group_size,
-                            _dev(Y, "Y", torch.float32), _stream(stream))
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    rc = lib().w4a16_linear(xptr, M, K, N,
+                            _dev(packed, "packed", torch.uint8, (N, (K + 1) // 2), dev),
+                            _dev(scales, "scales", torch.float32, ts, dev),
+                            _dev(zeros, "zeros", torch.float32, ts, dev), group_size,
+                            _dev(Y, "Y", torch.float32, (M, N), dev), _stream(stream))
     _check("w4a16_linear", rc)
     return Y
