@@ -378,7 +378,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer shards over output channels with no exchange; see the design notes).",
+              "(the layer shards over output channels with no exchange, so each GPU runs a "
+              "smaller-N layer of the same kind).",
               file=sys.stderr)
         sys.exit(2)
 
