@@ -25,6 +25,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBufFlags = 0x00020000;  // gfx9 raw-buffer descriptor word 3
 constexpr int kMaxRange = 0x7F000000;  // descriptor ranges are capped here
 constexpr int kOOB = 0x7FFF0000;       // an offset beyond every range (plus room for +16 .. +48)
+constexpr int kNonTemporal = 2;       // cache-policy operand of the buffer builtins: nt
 
 // Callers keep every in-range offset below kMaxRange (the kernels rebase the
 // descriptor on the rows a block touches).
@@ -35,6 +36,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Streaming 16-byte load (non-temporal hint): for data a kernel reads exactly
+// once, the packed weights of the decode GEMVs, so that the stream does not
+// displace cache lines that are reused.
+__device__ __forceinline__ uint4 bload16_nt(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal));
 }
 
 __device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, int off) {
