@@ -59,7 +59,7 @@ def _shapes(n, seed):
     return out
 
 
-@pytest.mark.parametrize("M,K,N,bias,relu", _shapes(36, 2025))
+@pytest.mark.parametrize("M,K,N,bias,relu", _shapes(36, 2025) + _shapes(40, 1) + _shapes(40, 2))
 def test_random_layer(M, K, N, bias, relu):
     d = workloads.random_case(M * 131 + K * 7 + N, M, K, N, outliers=min(4, K), bias=bias)
     b = d.get("bias")
