@@ -1,7 +1,8 @@
-"""Seeded random sweep of layer shapes through the C ABI, bit-exact against the
-oracle: M from 1 to 300 (dot4 GEMV, MFMA GEMV of every channel-block width,
-GEMM, generic kernel), K with and without the fast paths' alignment, ragged
-N, random bias and ReLU; W4A8 on both weight layouts and W8A8."""
+"""Seeded random sweep of layer shapes through the C ABI against the oracle:
+M from 1 to 300 (dot4 GEMV, MFMA GEMV of every channel-block width, GEMM,
+generic kernel), K with and without the fast paths' alignment, ragged N,
+random bias and ReLU; W4A8 on both weight layouts and W8A8 bit-exact, and
+W4A16 over random group sizes within the fp32 summation bound."""
 import numpy as np
 import pytest
 import torch
@@ -85,3 +86,39 @@ def test_random_layer(M, K, N, bias, relu):
     Wq, sw8 = W4.w8_quantize_weight(dev(d["W"]))
     y8 = host(W4.w8a8_linear_act(X, Wq, sw8, bias=bb, activation=act))
     assert same_bits(y8, y8ref), f"w8a8 path={W4.w4_last_path()}"
+
+
+def _w4a16_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        g = int(rng.choice([4, 32, 64, 128, 128, 128]))
+        K = g * int(rng.integers(1, 17))
+        if i % 3 == 0:
+            K = 512 * int(rng.integers(1, 5))            # LDS-staged kernel (group 128)
+            g = 128
+        M = int(rng.choice([1, 2, 5, 8, 16, 17, 33, 64]))
+        N = int(rng.integers(1, 400)) if i % 4 else int(rng.integers(1000, 3000))
+        if M * K * N > 1.5e8:
+            M = max(1, int(1.5e8 // (K * N)))
+        out.append((M, K, N, g))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N,g", _w4a16_shapes(40, 7))
+def test_random_w4a16(M, K, N, g):
+    """W4A16 over random shapes and group sizes against the fp64 oracle sum:
+    norm-wise 1e-5 and the elementwise gamma_K bound of the fp32 summation."""
+    rng = np.random.default_rng(M * 977 + K * 13 + N + g)
+    W = (rng.standard_normal((K, N)) * 0.015).astype(np.float32)
+    xb = workloads.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    pref, sref, zref = oracle.quantize_weight_asym(W, g)
+    yref, absy = oracle.w4a16_linear(xb, pref, sref, zref, g)
+    packed, s, z = W4.w4_quantize_weight(dev(W), "asym", g)
+    assert np.array_equal(host(packed), pref)
+    y = host(W4.w4a16_linear(dev(xb.view(np.int16)), packed, s, z, g))
+    u = 2.0 ** -24
+    gamma = K * u / (1 - K * u)
+    diff = np.abs(y.astype(np.float64) - yref)
+    assert np.linalg.norm(diff) <= 1e-5 * np.linalg.norm(yref), W4.w4_last_path()
+    assert np.all(diff <= gamma * absy + 1e-30), W4.w4_last_path()
