@@ -242,3 +242,28 @@ def test_binding_refuses_cpu_tensors(w4):
     import torch
     with pytest.raises(ValueError):
         w4.a8_quantize_act(torch.zeros(2, 8))
+
+
+def test_product_path_has_no_cpu_fallback(tmp_path):
+    """The package never imports the oracle, and without its HIP library
+    every call fails loudly instead of computing anything on the CPU."""
+    import subprocess
+    import sys
+    code = (
+        "import sys\n"
+        "import int4_weight_quantized_amd as w4\n"
+        "w4.lib()\n"
+        "assert not any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules), 'oracle imported'\n"
+        f"w4.LIB_PATH = {str(tmp_path / 'missing.so')!r}\n"
+        "w4._lib = None\n"
+        "try:\n"
+        "    w4.lib()\n"
+        "except RuntimeError as e:\n"
+        "    assert 'missing' in str(e)\n"
+        "else:\n"
+        "    raise AssertionError('no error without the library')\n"
+        "print('ok')\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
