@@ -83,7 +83,11 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args args) {
     const int wm = wave / 4, wn = wave % 4;
 
     // ---- direct-load sources (buffer loads that write LDS; rows past M and
-    // channels past N are outside the descriptors and read as zeros).
+    // channels past N are outside the descriptors and read as zeros).  The
+    // raw-buffer range check covers the per-lane offset (voffset) only, not
+    // the scalar offset, so each lane's row or channel is part of its voffset
+    // and the scalar offset holds only the k-tile's position inside that row
+    // (kt * 128 + 128 <= K bytes: it never leaves the row).
     // LDS A layout: rows r, r+1 (r even) form a 256-byte super-row; the 16
     // chunks (row parity p, chunk c) sit at slot ((8p + c) ^ ((r/2) % 8)).  A
     // 128-bit LDS read is conflict-free when each 16 consecutive lanes use 16
@@ -91,13 +95,13 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args args) {
     // chunk) do.  A: 32 wave-loads of 4 super-rows (1 KB); this wave issues
     // q = 4*wave + i.  Lane s fills slot s%16 of super-row 4q + s/16, i.e.
     // global row 8q + 2(s/16) + (v>>3), chunk v&7, with v = (s%16) ^ ((s/16 + 4q) % 8)
-    // = (s%16) ^ (s/16 + 4*(q%2)) since 4q % 8 = 4*(q%2).
+    // = (s%16) ^ (s/16 + 4*(i%2)) since 4q % 8 = 4*(i%2).
     const v4i ra = buffer_desc(a.Xq + m0 * K, min((int64_t)kBM, M - m0) * K);
-    int a_voff[2];
+    int a_voff[4];
 #pragma unroll
-    for (int qp = 0; qp < 2; ++qp) {
-        const int v = (lane % 16) ^ (lane / 16 + 4 * qp);
-        a_voff[qp] = (32 * wave + 2 * (lane / 16) + (v >> 3)) * (int)K + (v & 7) * 16;
+    for (int i = 0; i < 4; ++i) {
+        const int v = (lane % 16) ^ (lane / 16 + 4 * (i % 2));
+        a_voff[i] = (32 * wave + 8 * i + 2 * (lane / 16) + (v >> 3)) * (int)K + (v & 7) * 16;
     }
     // B: 16 wave-loads of 16 channels x 64 B; this wave issues q = 2*wave + i,
     // i.e. channels 32*wave + 16*i + lane/4.  Stored position lane%4 holds the
@@ -109,17 +113,19 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args args) {
     const v4i rbs = PP ? buffer_desc(a.packed + (n0 / 16) * ST * 1024,
                                      ((min((int64_t)kBN, N - n0) + 15) / 16) * ST * 1024)
                        : buffer_desc(a.packed + n0 * KB, min((int64_t)kBN, N - n0) * KB);
-    const int b_voff = (32 * wave + lane / 4) * (int)KB + (((lane % 4) ^ ((lane / 8) % 4)) * 16);
+    int b_voff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        b_voff[i] = (32 * wave + 16 * i + lane / 4) * (int)KB + (((lane % 4) ^ ((lane / 8) % 4)) * 16);
     auto issue = [&](uint8_t *st, int kt) {
         const uint32_t base = lds_addr(st);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            dma16(ra, base + (4 * wave + i) * 1024, a_voff[i % 2], 8 * i * (int)K + kt * kBK);
+            dma16(ra, base + (4 * wave + i) * 1024, a_voff[i], kt * kBK);
         if (W8) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                dma16(rbs, base + kABytes + (4 * wave + i) * 1024, a_voff[i % 2],
-                      8 * i * (int)K + kt * kBK);
+                dma16(rbs, base + kABytes + (4 * wave + i) * 1024, a_voff[i], kt * kBK);
         } else if (PP) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -128,8 +134,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(W4A8Args args) {
         } else {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                dma16(rbs, base + kABytes + (2 * wave + i) * 1024, b_voff,
-                      16 * i * (int)KB + kt * (kBK / 2));
+                dma16(rbs, base + kABytes + (2 * wave + i) * 1024, b_voff[i], kt * (kBK / 2));
         }
     };
 
