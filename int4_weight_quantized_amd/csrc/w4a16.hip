@@ -10,8 +10,8 @@
 // channel (codes k = 128*s + 32*(l/16) + [0, 32)) and the matching 32 bf16
 // activations of row l%16; the 32 codes feed four MFMAs of 8 codes each.
 //
-// Dequantization in 25 VALU operations per 8 codes: for a zero point z in
-// [-112, 128] the byte 128 + q - z never leaves [0, 255], so one integer add
+// Dequantization in 25 VALU operations per 8 codes: for an integer zero
+// point z in [-112, 128] the byte 128 + q - z never leaves [0, 255], so one integer add
 // per 4 codes forms it in place, v_cvt_f32_ubyte turns it into a float v, and
 //   fma(v, s, -128*s) = fl((v - 128) * s) = fl((q - z) * s)
 // exactly (one rounding of the exact product; 128*s is exact).  Other groups
@@ -61,6 +61,13 @@ __device__ __forceinline__ v4i dequant8_direct(uint32_t w, float s, float zp) {
     }
     return v4i{(int)pk_bf16(fl[0], fh[0]), (int)pk_bf16(fl[1], fh[1]), (int)pk_bf16(fl[2], fh[2]),
                (int)pk_bf16(fl[3], fh[3])};
+}
+
+// A group may take the fast form when its zero point is an integer in
+// [-112, 128] (the byte 128 + q - z then stays in [0, 255]; a fractional zero
+// point must not be truncated there) and 128 * s is finite and exact.
+__device__ __forceinline__ bool fast_group_ok(float s, float zp) {
+    return zp >= -112.0f && zp <= 128.0f && zp == rintf(zp) && fabsf(s) < 0x1p100f;
 }
 
 __device__ __forceinline__ v4f mfma_bf16(uint4 a, v4i b, v4f c) {
@@ -127,7 +134,7 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_mfma(const uint16_t *__restric
         bool ok = true;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-            ok = ok && (zp[nb] >= -112.0f) && (zp[nb] <= 128.0f) && (fabsf(sc[nb]) < 0x1p100f);
+            ok = ok && fast_group_ok(sc[nb], zp[nb]);
         if (__all(ok)) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
@@ -392,7 +399,7 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
         bool ok = true;
 #pragma unroll
         for (int j = 0; j < kLSteps; ++j)
-            ok = ok && (zps[j] >= -112.0f) && (zps[j] <= 128.0f) && (fabsf(scs[j]) < 0x1p100f);
+            ok = ok && fast_group_ok(scs[j], zps[j]);
         const bool fast = __all(ok);
 #pragma unroll
         for (int j = 0; j < kLSteps; ++j) {
