@@ -47,7 +47,7 @@ extern "C" {
 typedef enum {
     W4_OK = 0,
     W4_ERR_NULL = -1,      /* a required pointer is NULL                          */
-    W4_ERR_SHAPE = -2,     /* a size is < 1, or K % group_size != 0, or too large */
+    W4_ERR_SHAPE = -2,     /* a size is < 1, a group_size odd or not dividing K, or too large */
     W4_ERR_ALIGN = -3,     /* a pointer is not aligned to its element size        */
     W4_ERR_SCHEME = -4,    /* unknown quantization scheme                         */
     W4_ERR_WORKSPACE = -5, /* workspace missing or smaller than required          */
@@ -80,7 +80,10 @@ typedef enum {
  *             scales[n] = fl(max_k |W[k][n]| / 7) (0 for an all-zero channel),
  *             code = clamp(rne(fl(W / scale)), -8, 7) (0 where scale is 0);
  *             zeros must be NULL.
- *           W4_ASYM_GROUP: group_size >= 1 with K % group_size == 0; groups of
+ *           W4_ASYM_GROUP: group_size even, >= 2, with K % group_size == 0
+ *             (else W4_ERR_SHAPE): the two codes of a packed byte then never
+ *             belong to two groups, so every group owns whole bytes (K <=
+ *             W4_MAX_K also keeps K / group_size <= 65535); groups of
  *             group_size consecutive k inside one channel; scales and zeros
  *             are [N][K/group_size]:
  *               lo, hi = min, max of the group;
@@ -96,7 +99,8 @@ int w4_quantize_weight(const float *W, int64_t K, int64_t N, int scheme,
 /* Dequantize packed int4 weights back to fp32 (the dequantization step of
  * the LoRA export path, Keras guide "Limitations"; formulas of step 6 and of
  * the weight-only page's quantization principle).
- *   packed, scales, zeros, scheme, group_size as produced by w4_quantize_weight.
+ *   packed, scales, zeros, scheme, group_size as produced by w4_quantize_weight
+ *           (the same group_size rule: even, >= 2, dividing K).
  *   W  [K][N] fp32: fl(code * scale[n]) for W4_SYM_PER_CHANNEL,
  *      fl(fl(code - zero) * scale) for W4_ASYM_GROUP.
  * Returns W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_SCHEME or W4_ERR_HIP. */
@@ -262,7 +266,9 @@ int w8a8_matmul_i32(const int8_t *Xq, const int8_t *Wq, int64_t M, int64_t K, in
  * weights are dequantized at compute time; concept entry 4.5, schemes A/C).
  *   X_bf16  [M][K] bf16 bit patterns.
  *   packed  [N][(K+1)/2] unsigned codes; scales, zeros [N][K/group_size] fp32
- *           from w4_quantize_weight(..., W4_ASYM_GROUP, group_size, ...).
+ *           from w4_quantize_weight(..., W4_ASYM_GROUP, group_size, ...);
+ *           group_size even, >= 2, dividing K, else W4_ERR_SHAPE.  Zero
+ *           points may be any finite value (the quantizer's are integers).
  *   Y       [M][N] fp32 = sum_k x[m][k] * w'[k][n], with
  *           w' = bf16_rne(fl(fl(float(code) - zero) * scale)), products and
  *           sums in fp32 (the summation order is unspecified; the result is

@@ -46,8 +46,9 @@ class QuantizedLayer:
         if self.scheme == "w8_sym":
             return {"packed": ((N, K), torch.int8), "scales": ((N,), torch.float32)}
         if self.scheme == "w4_asym":
-            if g < 2 or K % g:
-                raise ValueError(f"w4_asym needs a group size dividing K (K={K}, group={g})")
+            if g < 2 or g % 2 or K % g:
+                raise ValueError(f"w4_asym needs an even group size >= 2 dividing K "
+                                 f"(K={K}, group={g})")
             return {"packed": ((N, (K + 1) // 2), torch.uint8),
                     "scales": ((N, K // g), torch.float32), "zeros": ((N, K // g), torch.float32)}
         raise ValueError(f"unknown scheme {self.scheme!r}; expected one of {SCHEMES}")

@@ -80,3 +80,16 @@ def test_rejects_bad_inputs(orc, tmp_path):
     save_file({"x.packed": L.packed}, str(tmp_path / "c.safetensors"), metadata={"format": "other"})
     with pytest.raises(ValueError):
         ser.load(str(tmp_path / "c.safetensors"), device="cpu")
+
+
+def test_rejects_group_sizes_the_library_refuses(orc, tmp_path):
+    """The same group rule as the C ABI: even, >= 2, dividing K."""
+    p, s, z = orc.quantize_weight_asym(np.ones((12, 2), np.float32), 3)
+    odd = ser.QuantizedLayer("w4_asym", 12, 2, torch.from_numpy(p), torch.from_numpy(s),
+                             torch.from_numpy(z), group_size=3)
+    with pytest.raises(ValueError, match="even group size"):
+        ser.save(str(tmp_path / "g.safetensors"), {"x": odd})
+    p, s, z = orc.quantize_weight_asym(np.ones((12, 2), np.float32), 4)
+    ok = ser.QuantizedLayer("w4_asym", 12, 2, torch.from_numpy(p), torch.from_numpy(s),
+                            torch.from_numpy(z), group_size=4)
+    ser.save(str(tmp_path / "g.safetensors"), {"x": ok})
