@@ -52,7 +52,9 @@ typedef enum {
     W4_ERR_SCHEME = -4,    /* unknown quantization scheme                         */
     W4_ERR_WORKSPACE = -5, /* workspace missing or smaller than required          */
     W4_ERR_HIP = -6,       /* the HIP runtime reported an error                   */
-    W4_ERR_ARG = -7        /* an enumerated argument has an unknown value         */
+    W4_ERR_ARG = -7,       /* an enumerated argument has an unknown value         */
+    W4_ERR_SCRATCH = -8    /* w4a8_linear_noalloc: the shape needs more scratch
+                              than W4_NOALLOC_SCRATCH_BYTES                       */
 } w4_status;
 
 /* Activation applied to a layer's output after dequantization and bias (the
@@ -167,6 +169,32 @@ int w4a8_linear_act(const float *X, int64_t M, int64_t K, int64_t N,
                     const uint8_t *packed, const float *sw, const float *bias,
                     int activation, float *Y, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/* Size of the fixed device scratch of w4a8_linear_noalloc: 16 MiB + 64 KiB.
+ * It takes every shape with w4a8_workspace_bytes(M, K, N) up to this size
+ * (activation codes and row scales), e.g. a 4096 x 4096 prefill.  Every GPU
+ * the library runs on holds one such array from the library's load until the
+ * process ends. */
+#define W4_NOALLOC_SCRATCH_BYTES (16777216 + 65536)
+
+/* w4a8_linear for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); its scratch is a fixed device array of
+ * W4_NOALLOC_SCRATCH_BYTES per GPU inside the library, whose address is looked
+ * up once per device, on the first call made with that device current.
+ *   X, packed, sw, bias, Y  as w4a8_linear (caller-owned device memory);
+ *   stream  the hipStream_t the kernels run on.
+ * Results are bit-identical to w4a8_linear.  The scratch keeps the last
+ * call's contents, and every call on one GPU uses the same array: calls that
+ * overlap on one GPU (other streams, other host threads) race and must be
+ * serialized by the caller.
+ * Returns W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_HIP, or
+ * W4_ERR_SCRATCH when w4a8_workspace_bytes(M, K, N) exceeds
+ * W4_NOALLOC_SCRATCH_BYTES (nothing is launched then). */
+int w4a8_linear_noalloc(const float *X, int64_t M, int64_t K, int64_t N,
+                        const uint8_t *packed, const float *sw, const float *bias,
+                        float *Y, void *stream);
 
 /* The W4A8 forward from already-quantized activations (Keras guide steps 4-6):
  *   Xq [M][K] int8 and sx [M] fp32 (any values); the rest as w4a8_linear. */

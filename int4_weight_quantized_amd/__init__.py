@@ -12,6 +12,8 @@ functions carry the C names:
 * ``a8_quantize_act``     -- per-row dynamic int8 activations;
 * ``w4a8_linear``         -- the W4A8 forward from fp32 activations;
 * ``w4a8_linear_act``     -- the same with a fused activation (ReLU);
+* ``w4a8_linear_noalloc`` -- ``w4a8_linear`` with the library's fixed device
+  scratch instead of a workspace (for callers that cannot allocate);
 * ``w4a8_linear_q``       -- the W4A8 forward from int8 activations;
 * ``w4a8_matmul_i32``     -- the exact int32 accumulators alone;
 * ``w8_quantize_weight``  -- symmetric per-channel int8 weights (W8A8);
@@ -46,6 +48,7 @@ W4_ASYM_GROUP = 1
 W4_MAX_K = 131071
 W4_ACT_NONE = 0
 W4_ACT_RELU = 1
+W4_NOALLOC_SCRATCH_BYTES = 16777216 + 65536
 _ACTS = {None: W4_ACT_NONE, "none": W4_ACT_NONE, "relu": W4_ACT_RELU}
 
 _P = ctypes.c_void_p
@@ -74,6 +77,7 @@ def lib():
             "a8_quantize_act": ([_P, _I, _I, _P, _P, _P], ctypes.c_int),
             "w4a8_workspace_bytes": ([_I, _I, _I], _Z),
             "w4a8_linear": ([_P, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P], ctypes.c_int),
+            "w4a8_linear_noalloc": ([_P, _I, _I, _I, _P, _P, _P, _P, _P], ctypes.c_int),
             "w4a8_linear_act": ([_P, _I, _I, _I, _P, _P, _P, ctypes.c_int, _P, _P, _Z, _P],
                                 ctypes.c_int),
             "w8a8_linear_act": ([_P, _I, _I, _I, _P, _P, _P, ctypes.c_int, _P, _P, _Z, _P],
@@ -316,6 +320,23 @@ def w4a8_linear(X: torch.Tensor, packed: torch.Tensor, sw: torch.Tensor, bias=No
                            _dev(workspace, "workspace", torch.uint8, None, dev), workspace.numel(),
                            _stream(stream))
     _check("w4a8_linear", rc)
+    return Y
+
+
+def w4a8_linear_noalloc(X: torch.Tensor, packed: torch.Tensor, sw: torch.Tensor,
+                        Y: torch.Tensor, bias=None, stream=None) -> torch.Tensor:
+    """w4a8_linear without a workspace: the library's fixed device scratch
+    (W4_NOALLOC_SCRATCH_BYTES per GPU) serves instead, and nothing is allocated,
+    so the output Y [M, N] fp32 must be passed in.  Calls overlapping on one GPU race."""
+    M, K = _matrix(X, "X")
+    N = _matrix(packed, "packed")[0]
+    dev = X.device
+    rc = lib().w4a8_linear_noalloc(_dev(X, "X", torch.float32), M, K, N,
+                                   _dev(packed, "packed", torch.uint8, (N, (K + 1) // 2), dev),
+                                   _dev(sw, "sw", torch.float32, (N,), dev),
+                                   _opt(bias, "bias", torch.float32, (N,), dev),
+                                   _dev(Y, "Y", torch.float32, (M, N), dev), _stream(stream))
+    _check("w4a8_linear_noalloc", rc)
     return Y
 
 

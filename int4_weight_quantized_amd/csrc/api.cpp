@@ -2,11 +2,19 @@
 // before anything is launched) and dispatch to the gfx950 kernels.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/w4.h"
 #include "kernels.h"
+
+// Device scratch of w4a8_linear_noalloc: the activation-code workspace of the
+// W4A8 paths, held in a fixed array so that the call allocates nothing.  In
+// host code this name stands for a host-side shadow, not a device address:
+// the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[W4_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -125,6 +133,32 @@ int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const floa
     return launched(w8 ? "w8a8_generic" : "w4a8_generic", launch_w4a8_generic(a, st));
 }
 
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept per device (each GPU holds its
+// own copy of the array at its own address).
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+int scratch_address(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return W4_ERR_HIP;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return W4_ERR_HIP;
+            }
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return W4_OK;
+}
+
 int check_workspace(int64_t M, int64_t K, void *workspace, size_t bytes) {
     const size_t need = ws_bytes(M, K);
     if (need == 0) return W4_OK;
@@ -159,6 +193,8 @@ const char *w4_status_string(int status) {
         case W4_ERR_WORKSPACE: return "workspace missing or too small";
         case W4_ERR_HIP: return "HIP runtime error";
         case W4_ERR_ARG: return "unknown value of an enumerated argument";
+        case W4_ERR_SCRATCH:
+            return "the shape needs more scratch than the no-allocation call's fixed buffer holds";
         default: return "unknown status";
     }
 }
@@ -378,6 +414,21 @@ int w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N, const uint8_t *
                 size_t workspace_bytes, void *stream) {
     return w4a8_linear_act(X, M, K, N, packed, sw, bias, W4_ACT_NONE, Y, workspace,
                            workspace_bytes, stream);
+}
+
+int w4a8_linear_noalloc(const float *X, int64_t M, int64_t K, int64_t N, const uint8_t *packed,
+                        const float *sw, const float *bias, float *Y, void *stream) {
+    if (!X || !packed || !sw || !Y) return W4_ERR_NULL;
+    if (!shape_ok(M, K, N)) return W4_ERR_SHAPE;
+    if (ws_bytes(M, K) > (size_t)W4_NOALLOC_SCRATCH_BYTES) return W4_ERR_SCRATCH;
+    void *ws = nullptr;
+    const int rc = scratch_address(&ws);
+    if (rc != W4_OK) return rc;
+    // the same dispatch and kernels as w4a8_linear, with the scratch array as
+    // the workspace (every byte the kernels read from it is written first in
+    // the same call, so nothing needs clearing)
+    return w4a8_linear_act(X, M, K, N, packed, sw, bias, W4_ACT_NONE, Y, ws,
+                           (size_t)W4_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int w4a8_linear_q(const int8_t *Xq, const float *sx, const uint8_t *packed, const float *sw,

@@ -18,6 +18,7 @@ HEADER = os.path.join(ROOT, "include", "w4.h")
 W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_SCHEME, W4_ERR_WORKSPACE, W4_ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6)
 W4_ERR_ARG = -7
+W4_ERR_SCRATCH = -8
 FAKE = 1 << 20  # a non-NULL, 256-aligned address; never dereferenced by these calls
 
 
@@ -48,7 +49,7 @@ def test_header_declares_the_boundary():
                  "w4a16_prepack", "w4a16_unprepack", "w4a16_linear_prepacked",
                  "w4a16_prepacked_weight_bytes", "w4a16_prepacked_table_floats",
                  "w4_prepacked_weight_bytes", "w4_prepack_weights", "w4_unprepack_weights",
-                 "w4a8_linear_prepacked",
+                 "w4a8_linear_prepacked", "w4a8_linear_noalloc",
                  "w4_status_string", "w4_last_path"]:
         assert want in names, names
 
@@ -60,7 +61,7 @@ def test_library_exports_every_declared_symbol(w4):
 
 
 def test_status_strings(w4):
-    for st in range(-7, 1):
+    for st in range(-8, 1):
         assert w4.w4_status_string(st) and w4.w4_status_string(st) != "unknown status"
     assert w4.w4_status_string(-99) == "unknown status"
 
@@ -267,3 +268,17 @@ def test_product_path_has_no_cpu_fallback(tmp_path):
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
                        timeout=300)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
+
+
+def test_noalloc_checks_before_any_hip_call(w4):
+    """The no-allocation call refuses NULL pointers, bad sizes and shapes whose
+    scratch would exceed its fixed buffer on the host, before touching HIP."""
+    f = w4.lib().w4a8_linear_noalloc
+    assert f(None, 1, 64, 8, FAKE, FAKE, None, FAKE, None) == W4_ERR_NULL
+    assert f(FAKE, 1, 64, 8, FAKE, None, None, FAKE, None) == W4_ERR_NULL
+    assert f(FAKE, 0, 64, 8, FAKE, FAKE, None, FAKE, None) == W4_ERR_SHAPE
+    cap = w4.W4_NOALLOC_SCRATCH_BYTES
+    assert w4.w4a8_workspace_bytes(4096, 4096, 4096) <= cap
+    assert w4.w4a8_workspace_bytes(4200, 4096, 8) > cap
+    assert f(FAKE, 4200, 4096, 8, FAKE, FAKE, None, FAKE, None) == W4_ERR_SCRATCH
+    assert f(FAKE, 1 << 20, 64, 8, FAKE, FAKE, None, FAKE, None) == W4_ERR_SCRATCH
