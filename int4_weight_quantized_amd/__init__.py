@@ -40,7 +40,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libw4.so")
+# W4_LIB may name another build of the same sources (the host-sanitizer build
+# of build_hostsan.py).
+LIB_PATH = os.environ.get("W4_LIB") or os.path.join(_HERE, "libw4.so")
 
 W4_OK = 0
 W4_SYM_PER_CHANNEL = 0

@@ -40,7 +40,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libw4oracle.so")
+# W4_ORACLE_LIB may name another build of the same source (the host
+# sanitizer build of build.py --sanitize).
+_LIB_PATH = os.environ.get("W4_ORACLE_LIB") or os.path.join(_HERE, "libw4oracle.so")
 _lib = None
 
 _P = ctypes.c_void_p
