@@ -298,6 +298,75 @@ def graph_step_time(torch, case, steps, warmup, hip=None):
     return dt / steps, ev / steps
 
 
+def region_time(torch, hip, step, est_s, min_launches, min_region_s=2e-3):
+    """Average duration (s) of one launch from HIP events recorded on the
+    replay stream around one replay of a graph of L back-to-back launches,
+    L >= min_launches and L * est_s >= min_region_s (so the graph's own launch
+    latency is spread over at least about 2 ms).  Returns (seconds, L)."""
+    L = max(int(min_launches), int(math.ceil(min_region_s / max(est_s, 1e-7))))
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(L):
+                step(i)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()                      # untimed replay
+    torch.cuda.synchronize()
+    ea, eb = hip.event(), hip.event()
+    stream = torch.cuda.current_stream().cuda_stream
+    hip.record(ea, stream)
+    g.replay()
+    hip.record(eb, stream)
+    torch.cuda.synchronize()
+    sec = hip.elapsed_ms(ea, eb) / 1e3 / L
+    hip.destroy(ea)
+    hip.destroy(eb)
+    del g
+    return sec, L
+
+
+def demangle(name):
+    """Readable form of a kernel symbol (c++filt if present, else as is)."""
+    import shutil
+    import subprocess
+    if name.startswith("_Z") and shutil.which("c++filt"):
+        r = subprocess.run(["c++filt", name], capture_output=True, text=True)
+        if r.returncode == 0 and r.stdout.strip():
+            return r.stdout.strip()
+    return name
+
+
+def platform_probes(torch, hip, w4, head_grid):
+    """The platform references: an empty launch (1 workgroup and the headline
+    kernel's grid) and plain streaming reads of the headline's, the 7B-class
+    layer's and the 70B-class W4A16 layer's algorithmic bytes, each over
+    buffers rotating through more than the Infinity Cache, timed over >= 2 ms
+    of back-to-back graph launches."""
+    out = {}
+    for blocks in (1, head_grid):
+        sec, L = region_time(torch, hip, lambda i: w4.w4_probe_empty(blocks), 2e-6, 200)
+        out[f"empty_launch_{blocks}wg_us"] = round(sec * 1e6, 3)
+    out["empty_launch_launches"] = L
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    reads = []
+    for label, nbytes in (("headline", 4041216), ("mlp7b_m1", 22648832),
+                          ("w4a16_70b", 134217728)):
+        copies = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+        est = nbytes / 5e12 + 2e-6
+        sec, L = region_time(torch, hip, lambda i: w4.w4_probe_read(bufs[i % copies], sink),
+                             est, 20)
+        reads.append({"bytes": nbytes, "as": label, "us": round(sec * 1e6, 3),
+                      "GBps": round(nbytes / sec / 1e9, 1), "launches": L,
+                      "rotating_copies": copies})
+        del bufs
+        torch.cuda.empty_cache()
+    out["plain_read"] = reads
+    return out
+
+
 def kernel_time(torch, hip, w4, case, launches):
     """Average duration (s) of the product kernel, from start/stop events
     attached to each dispatch, over `launches` rotating launches."""
@@ -338,23 +407,123 @@ def load_traffic(kernel_digest):
     return t.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(case, seconds=10.0):
-    """The CPU oracle, as it is, on the headline workload: whole forward calls
-    repeated for about `seconds` on one host thread."""
+def _host_cores():
+    """Threads for the all-cores legs: the CPUs this process may run on, at
+    most 16 (the host share of one GPU on the benchmark boxes)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _run_threads(fns, seconds):
+    """Call fns[i]() repeatedly on thread i until `seconds` have passed (each
+    thread finishes its current call).  The oracle's ctypes calls release the
+    GIL, so the threads run on separate cores.  Returns (calls, wall seconds)."""
+    import threading
+    counts = [0] * len(fns)
+    stop = time.perf_counter() + seconds
+
+    def run(i):
+        while True:
+            fns[i]()
+            counts[i] += 1
+            if time.perf_counter() >= stop:
+                break
+
+    ths = [threading.Thread(target=run, args=(i,)) for i in range(len(fns))]
+    t0 = time.perf_counter()
+    for t in ths:
+        t.start()
+    for t in ths:
+        t.join()
+    return counts, time.perf_counter() - t0
+
+
+def _slices(n, parts):
+    edges = [n * i // parts for i in range(parts + 1)]
+    return [(edges[i], edges[i + 1]) for i in range(parts) if edges[i + 1] > edges[i]]
+
+
+def cpu_baseline(case, seconds=5.0):
+    """The CPU oracle, as it is, on the machine's host cores: the headline layer on
+    one thread and on all cores (threads split the output channels, each
+    calling the oracle's whole forward on its slice), then bounded samples of
+    the 4096^3 prefill (64 of its 4096 rows) and of the 70B-class W4A16 layer
+    (its first 2048 of 28672 output channels) on all cores."""
+    import numpy as np
     import oracle
+    import workloads
+    cores = _host_cores()
+    res = {}
+    # headline, one thread
     pref, sref = oracle.quantize_weight_sym(case.host_W)
-    n, t0 = 0, time.perf_counter()
-    while True:
-        oracle.w4a8_linear(case.host_x, pref, sref)
-        n += 1
-        dt = time.perf_counter() - t0
-        if dt >= seconds:
-            break
-    per = dt / n
-    return {"value": round(case.bytes / per / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{n} calls of the oracle's w4a8_linear on the headline workload "
-                      f"({case.M}x{case.K}x{case.N}), {dt:.1f} s, {per * 1e3:.2f} ms per call"}
+    counts, dt = _run_threads([lambda: oracle.w4a8_linear(case.host_x, pref, sref)], seconds)
+    per = dt / counts[0]
+    single = {"value": round(case.bytes / per / 1e9, 4), "unit": "GB/s", "cores": 1,
+              "sample": f"{counts[0]} calls of the oracle's w4a8_linear on the whole headline "
+                        f"layer ({case.M}x{case.K}x{case.N}), {dt:.1f} s, {per * 1e3:.2f} ms "
+                        f"per call"}
+    # headline, all cores: thread i runs the forward of channels n0..n1
+    sl = _slices(case.N, cores)
+    fns = [(lambda a, b: (lambda: oracle.w4a8_linear(
+        case.host_x, np.ascontiguousarray(pref[a:b]), np.ascontiguousarray(sref[a:b]))))(a, b)
+        for a, b in sl]
+    counts, dt = _run_threads(fns, seconds)
+    layers = sum(c * (b - a) for c, (a, b) in zip(counts, sl)) / case.N
+    res.update({"value": round(case.bytes * layers / dt / 1e9, 4), "unit": "GB/s",
+                "cores": len(sl), "kind": "oracle",
+                "sample": f"the headline layer ({case.M}x{case.K}x{case.N}) with its output "
+                          f"channels split over {len(sl)} threads, each calling the oracle's "
+                          f"w4a8_linear on its slice: {layers:.0f} whole layers in {dt:.1f} s",
+                "single_core": single})
+    # prefill sample, all cores
+    d = workloads.generate("prefill")
+    xs = np.ascontiguousarray(d["x"][:64])
+    pp, ps = oracle.quantize_weight_sym(d["W"])
+    K, N = d["K"], d["N"]
+    sl = _slices(N, cores)
+    fns = [(lambda a, b: (lambda: oracle.w4a8_linear(
+        xs, np.ascontiguousarray(pp[a:b]), np.ascontiguousarray(ps[a:b]))))(a, b) for a, b in sl]
+    counts, dt = _run_threads(fns, seconds)
+    ops = sum(c * 2 * xs.shape[0] * K * (b - a) for c, (a, b) in zip(counts, sl))
+    res["prefill"] = {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": len(sl),
+                      "sample": f"64 of the 4096 rows of the 4096x4096x4096 prefill, output "
+                                f"channels split over {len(sl)} threads (oracle w4a8_linear), "
+                                f"{ops / 1e9:.1f} G int ops in {dt:.1f} s"}
+    del d, pp
+    # W4A16 sample, all cores
+    w = workloads.w4a16_inputs(N=2048)
+    g, M, K = w["group"], w["M"], w["K"]
+    qp, qs, qz = oracle.quantize_weight_asym(w["W"], g)
+    sl = _slices(2048, cores)
+    fns = [(lambda a, b: (lambda: oracle.w4a16_linear(
+        w["x_bf16"], np.ascontiguousarray(qp[a:b]), np.ascontiguousarray(qs[a:b]),
+        np.ascontiguousarray(qz[a:b]), g)))(a, b) for a, b in sl]
+    counts, dt = _run_threads(fns, seconds)
+    cols = sum(c * (b - a) for c, (a, b) in zip(counts, sl))
+    full_n = workloads.SHAPES["w4a16"].N
+    layer_bytes = w4a16_bytes(M, K, full_n, g)
+    res["w4a16"] = {"value": round(layer_bytes * cols / full_n / dt / 1e9, 4), "unit": "GB/s",
+                    "cores": len(sl),
+                    "sample": f"the first 2048 of the 28672 output channels of the 16x8192x28672 "
+                              f"group-128 layer, split over {len(sl)} threads (oracle "
+                              f"w4a16_linear, fp64 sums), {cols} channel-rows in {dt:.1f} s; "
+                              f"value = the layer's bytes x channels done / {full_n} / time"}
+    res["host"] = {"cpu_model": _cpu_model(), "logical_cpus": os.cpu_count(),
+                   "threads_used": cores}
+    return res
 
 
 def main():
@@ -369,8 +538,10 @@ def main():
                          "mlp7b_m1, mlp7b_m16, mlp7b_m64, prefill, w4a16, w4a16_prepacked, "
                          "w8a8_gemma_m1, "
                          "w8a8_mlp7b_m1, w8a8_prefill, pp_<W4A8 workload> (shuffled tiles); "
-                         "or copy (a 64 MiB device copy, for "
-                         "counter calibration)")
+                         "copy (a 64 MiB device copy, for counter calibration); "
+                         "empty (an empty kernel of the headline's grid); read4m, read22m, "
+                         "read134m (plain streaming reads of the headline's, the 7B-class and "
+                         "the 70B-class W4A16 layer's bytes)")
     ap.add_argument("--launches", type=int, default=200)
     ap.add_argument("--copies", type=int, default=0,
                     help="with --only: number of rotating weight copies (0 = enough to exceed "
@@ -389,6 +560,24 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     hip = Hip()
 
+    if args.only == "empty" or (args.only or "").startswith("read"):
+        # platform references for the profilers: an empty launch of the
+        # headline kernel's grid, or plain reads of 4 / 22.6 / 134 MB
+        # (the headline's, the 7B-class layer's and the W4A16 layer's bytes)
+        # over rotating buffers
+        if args.only == "empty":
+            for _ in range(args.warmup + args.steps):
+                w4.w4_probe_empty(432)
+        else:
+            nbytes = {"read4m": 4041216, "read22m": 22648832, "read134m": 134217728}[args.only]
+            copies = max(2, math.ceil(ROTATE_BYTES / nbytes))
+            bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+            sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+            for i in range(args.warmup + args.steps):
+                w4.w4_probe_read(bufs[i % copies], sink)
+        torch.cuda.synchronize()
+        log(f"{args.only}: {args.warmup + args.steps} launches done")
+        return
     if args.only == "copy":
         # a plain device copy of known size (calibrates the HBM byte counters)
         src = torch.ones(64 << 20, dtype=torch.uint8, device="cuda")
@@ -419,12 +608,15 @@ def main():
 
     log("headline: gemma3-1b up-projection, W4A8, M=1")
     head = W4A8Case(w4, torch, "gemma_m1", "gemma", 1)
-    step_s, region_s = graph_step_time(torch, head, args.steps, args.warmup, hip)
+    step_s, steps_region_s = graph_step_time(torch, head, args.steps, args.warmup, hip)
     path = w4.w4_last_path()
+    kernel = demangle(w4.w4_last_kernel())
+    # each step is this one kernel launch: its average launch duration is the
+    # event time of a region of back-to-back launches / launches, over a
+    # region of >= 2 ms so that the graph's own launch latency is amortized
+    region_s, region_launches = region_time(torch, hip, head.step, step_s, args.steps)
     k_avg, k_med = kernel_time(torch, hip, w4, head, args.launches)
     value = head.bytes / step_s / 1e9
-    # the timed region holds only this kernel (one launch per step): its
-    # average launch duration is the region's event time / launches
     achieved = head.bytes / region_s / 1e9
     digest = src_digest()
     out = {
@@ -436,43 +628,64 @@ def main():
                    "M": 1, "K": head.K, "N": head.N, "weights": "int4 symmetric per-channel",
                    "activations": "int8 per-row dynamic", "launch": "hipGraph of all steps",
                    "rotating_weight_copies": head.copies, "product_kernel": path},
-        "roofline": {"bound": "hbm", "kernel": "w4::k_gemv_dot4<1, 16, 3, true, Out::Y, false, false>",
+        "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(digest),
                      "algorithmic_bytes_per_launch": head.bytes,
                      "kernel_us_avg": round(region_s * 1e6, 3),
-                     "timing": "HIP events on the replay stream around the timed graph "
-                               "replay, divided by its launches",
+                     "timing": "HIP events on the replay stream around one replay of a graph "
+                               "of back-to-back launches of this kernel, divided by its launches",
+                     "region_launches": region_launches,
+                     "region_ms": round(region_s * region_launches * 1e3, 3),
+                     "kernel_us_timed_steps_region": round(steps_region_s * 1e6, 3),
                      "kernel_us_dispatch_events_avg": round(k_avg * 1e6, 3),
                      "kernel_us_dispatch_events_median": round(k_med * 1e6, 3),
                      "src_digest": digest},
     }
-    log(f"headline: step {step_s * 1e6:.2f} us, kernel {region_s * 1e6:.2f} us (region events), "
+    log(f"headline: step {step_s * 1e6:.2f} us ({args.steps} steps), kernel "
+        f"{region_s * 1e6:.3f} us (region of {region_launches} launches), "
         f"{k_avg * 1e6:.2f} us (per-dispatch events), {value:.0f} GB/s")
 
+    if not args.no_parts:
+        log("platform: empty launches and plain reads")
+        out["platform"] = platform_probes(torch, hip, w4, (head.N + 15) // 16)
     parts = []
     if not args.no_parts:
         def w4a8_part(name, shape, M, bound, rotate=True, w8=False, pp=False):
             log(f"part: {name}")
             c = W4A8Case(w4, torch, name, shape, M, rotate=rotate, w8=w8, pp=pp)
-            st = graph_step_time(torch, c, min(args.steps, 200), 10)
+            st = graph_step_time(torch, c, 200, 10)
             p = w4.w4_last_path()
+            # one launch when the activation quantization runs inside the
+            # product kernel, else a quantizer launch before it
+            fused = p.startswith(("gemv_dot4", "w8_gemv_dot4")) or "mfma_fused" in p
+            launches = 1 if fused else 2
+            stl, L = region_time(torch, hip, c.step, st, 200)
             ka, km = kernel_time(torch, hip, w4, c, min(args.launches, 100))
             r = {"workload": name, "M": c.M, "K": c.K, "N": c.N, "product_kernel": p,
-                 "step_us": round(st * 1e6, 3), "kernel_us_avg": round(ka * 1e6, 3),
+                 "launches_per_step": launches,
+                 "step_us": round(stl * 1e6, 3), "step_region_launches": L,
+                 "kernel_us_avg": round(ka * 1e6, 3),
                  "algorithmic_bytes": c.bytes, "int_ops": c.ops,
                  "rotating_weight_copies": c.copies,
                  "weight_quantize_ms": round(c.quant_s * 1e3, 3)}
             if bound == "hbm":
-                r["GBps_kernel"] = round(c.bytes / ka / 1e9, 1)
-                r["GBps_step"] = round(c.bytes / st / 1e9, 1)
-                r["frac_hbm_kernel"] = round(c.bytes / ka / 1e9 / HBM_PEAK_GBS, 4)
+                # the step's rate (every launch of the step, fp32 activations
+                # in) is the figure; the product kernel's own rate counts what
+                # that kernel reads: fp32 activations when fused, else the
+                # int8 codes and row scales the quantizer wrote
+                kb = c.bytes if fused else c.bytes - 4 * c.M * c.K + c.M * c.K + 4 * c.M
+                r["GBps_step"] = round(c.bytes / stl / 1e9, 1)
+                r["frac_hbm_step"] = round(c.bytes / stl / 1e9 / HBM_PEAK_GBS, 4)
+                r["product_kernel_bytes"] = kb
+                r["GBps_kernel"] = round(kb / ka / 1e9, 1)
+                r["frac_hbm_kernel"] = round(kb / ka / 1e9 / HBM_PEAK_GBS, 4)
             else:
                 r["TOPS_kernel"] = round(c.ops / ka / 1e12, 1)
-                r["TOPS_step"] = round(c.ops / st / 1e12, 1)
+                r["TOPS_step"] = round(c.ops / stl / 1e12, 1)
                 r["frac_int8_mfma_kernel"] = round(c.ops / ka / 1e12 / INT8_PEAK_TOPS, 4)
-                r["frac_int8_mfma_step"] = round(c.ops / st / 1e12 / INT8_PEAK_TOPS, 4)
+                r["frac_int8_mfma_step"] = round(c.ops / stl / 1e12 / INT8_PEAK_TOPS, 4)
             parts.append(r)
             del c
             torch.cuda.empty_cache()
@@ -497,13 +710,15 @@ def main():
             c = AwqCase(w4, torch, name, "mlp7b", M)
             st = graph_step_time(torch, c, 200, 10)
             p = w4.w4_last_path()
+            st, L = region_time(torch, hip, c.step, st, 200)
             ka, km = kernel_time(torch, hip, w4, c, 100)
             parts.append({"workload": name, "M": c.M, "K": c.K, "N": c.N, "product_kernel": p,
-                          "step_us": round(st * 1e6, 3), "kernel_us_avg": round(ka * 1e6, 3),
+                          "launches_per_step": 1 if p.startswith("gemv_dot4") else 2,
+                          "step_us": round(st * 1e6, 3), "step_region_launches": L,
+                          "kernel_us_avg": round(ka * 1e6, 3),
                           "algorithmic_bytes": c.bytes,
-                          "GBps_kernel": round(c.bytes / ka / 1e9, 1),
                           "GBps_step": round(c.bytes / st / 1e9, 1),
-                          "frac_hbm_kernel": round(c.bytes / ka / 1e9 / HBM_PEAK_GBS, 4),
+                          "frac_hbm_step": round(c.bytes / st / 1e9 / HBM_PEAK_GBS, 4),
                           "rotating_weight_copies": c.copies})
             del c
             torch.cuda.empty_cache()
@@ -514,9 +729,11 @@ def main():
             c = W4A16Case(w4, torch, prepacked=pp)
             st = graph_step_time(torch, c, 50, 5)
             p = w4.w4_last_path()
+            st, L = region_time(torch, hip, c.step, st, 50)
             ka, km = kernel_time(torch, hip, w4, c, 50)
             parts.append({"workload": c.name, "M": c.M, "K": c.K, "N": c.N, "group": c.g,
-                          "product_kernel": p, "step_us": round(st * 1e6, 3),
+                          "product_kernel": p, "launches_per_step": 1,
+                          "step_us": round(st * 1e6, 3), "step_region_launches": L,
                           "kernel_us_avg": round(ka * 1e6, 3), "algorithmic_bytes": c.bytes,
                           "GBps_kernel": round(c.bytes / ka / 1e9, 1),
                           "GBps_step": round(c.bytes / st / 1e9, 1),

@@ -377,6 +377,27 @@ int w4_time_next_kernel(void *start_event, void *stop_event);
  * for its main product (for tests and profiling; never NULL). */
 const char *w4_last_path(void);
 
+/* Device symbol (mangled name) of that kernel, e.g. for naming the kernel a
+ * benchmark timed; "none" before any successful call on this thread.  The
+ * returned string belongs to the HIP runtime. */
+const char *w4_last_kernel(void);
+
+/* ---- Measurement helpers (not part of the method): the platform references
+ * the layer's timings are read against.  Asynchronous on `stream`.
+ *
+ * An empty kernel of `blocks` workgroups of 256 threads (1 <= blocks < 2^31):
+ * its duration in a graph of back-to-back launches is the fixed cost of one
+ * launch.  Returns W4_OK, W4_ERR_SHAPE or W4_ERR_HIP. */
+int w4_probe_empty(int64_t blocks, void *stream);
+
+/* A plain streaming read of `bytes` device bytes at `src` (16-byte aligned;
+ * 16 <= bytes <= 0x7F000000, bytes % 16 == 0), each byte read once with a
+ * 16-byte non-temporal load; `sink` is a device array of 64 uint32 that the
+ * kernel writes only if the data's XOR takes one particular value (it keeps
+ * the loads from being removed).  Returns W4_OK, W4_ERR_NULL, W4_ERR_SHAPE,
+ * W4_ERR_ALIGN or W4_ERR_HIP. */
+int w4_probe_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -112,6 +112,9 @@ def lib():
             "w8a8_matmul_i32": ([_P, _P, _I, _I, _I, _P, _P, _Z, _P], ctypes.c_int),
             "w4_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "w4_last_path": ([], ctypes.c_char_p),
+            "w4_last_kernel": ([], ctypes.c_char_p),
+            "w4_probe_empty": ([_I, _P], ctypes.c_int),
+            "w4_probe_read": ([_P, _I, _P, _P], ctypes.c_int),
             "w4_time_next_kernel": ([_P, _P], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
@@ -129,6 +132,25 @@ def w4_status_string(status: int) -> str:
 def w4_last_path() -> str:
     """Kernel variant of the last call's main product (e.g. "gemv_dot4")."""
     return lib().w4_last_path().decode()
+
+
+def w4_last_kernel() -> str:
+    """Device symbol (mangled) of the last successful call's main kernel."""
+    return lib().w4_last_kernel().decode()
+
+
+def w4_probe_empty(blocks: int, stream=None) -> None:
+    """Launch an empty kernel of `blocks` workgroups (a measurement helper)."""
+    _check("w4_probe_empty", lib().w4_probe_empty(int(blocks), _stream(stream)))
+
+
+def w4_probe_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read every byte of `src` once (a measurement helper); sink: 64 int32."""
+    dev = src.device
+    _check("w4_probe_read", lib().w4_probe_read(_dev(src, "src", src.dtype), src.numel() *
+                                                src.element_size(),
+                                                _dev(sink, "sink", torch.int32, (64,), dev),
+                                                _stream(stream)))
 
 
 def w4_time_next_kernel(start_event: int | None, stop_event: int | None) -> None:

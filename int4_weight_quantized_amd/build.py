@@ -21,7 +21,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libw4.so")
 ARCH = "gfx950"
 
-SOURCES = ["quant.hip", "gemv.hip", "gemm.hip", "w4a16.hip", "generic.hip", "api.cpp"]
+SOURCES = ["quant.hip", "gemv.hip", "gemm.hip", "w4a16.hip", "generic.hip", "probe.hip", "api.cpp"]
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -20,6 +20,9 @@ namespace {
 
 thread_local const char *g_last_path = "none";
 thread_local hipEvent_t g_time_start = nullptr, g_time_stop = nullptr;
+// the kernel the current call launches, and the last one of a successful call
+thread_local const void *g_pending_kernel = nullptr, *g_last_kernel = nullptr;
+thread_local hipStream_t g_pending_stream = nullptr, g_last_stream = nullptr;
 
 inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -32,6 +35,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? W4_OK : W4_ERR_HIP; }
 int launched(const char *path, hipError_t e) {
     if (e != hipSuccess) return W4_ERR_HIP;
     g_last_path = path;
+    g_last_kernel = g_pending_kernel;
+    g_last_stream = g_pending_stream;
     return W4_OK;
 }
 
@@ -169,6 +174,11 @@ int check_workspace(int64_t M, int64_t K, void *workspace, size_t bytes) {
 
 }  // namespace
 
+void w4::note_kernel(const void *kernel, hipStream_t st) {
+    g_pending_kernel = kernel;
+    g_pending_stream = st;
+}
+
 w4::TimingEvents w4::take_timing_events() {
     TimingEvents ev{g_time_start, g_time_stop};
     g_time_start = g_time_stop = nullptr;
@@ -200,6 +210,27 @@ const char *w4_status_string(int status) {
 }
 
 const char *w4_last_path(void) { return g_last_path; }
+
+const char *w4_last_kernel(void) {
+    if (!g_last_kernel) return "none";
+    const char *name = hipKernelNameRefByPtr(g_last_kernel, g_last_stream);
+    return name ? name : "unknown";
+}
+
+int w4_probe_empty(int64_t blocks, void *stream) {
+    if (blocks < 1 || blocks > 0x7FFFFFFF) return W4_ERR_SHAPE;
+    return launched("probe_empty",
+                    w4::launch_probe_empty(blocks, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int w4_probe_read(const void *src, int64_t bytes, uint32_t *sink, void *stream) {
+    if (!src || !sink) return W4_ERR_NULL;
+    if (bytes < 16 || bytes % 16 != 0 || bytes > 0x7F000000) return W4_ERR_SHAPE;
+    if (!aligned(src, 16) || !aligned(sink, 4)) return W4_ERR_ALIGN;
+    return launched("probe_read",
+                    w4::launch_probe_read(static_cast<const uint8_t *>(src), bytes, sink,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
 
 int w4_quantize_weight(const float *W, int64_t K, int64_t N, int scheme, int64_t group_size,
                        uint8_t *packed, float *scales, float *zeros, void *stream) {

@@ -17,11 +17,16 @@ struct TimingEvents {
 };
 TimingEvents take_timing_events();
 
+// Remember which kernel the current call launches (its host stub and stream);
+// the C ABI layer keeps it as the last kernel once the call succeeded.
+void note_kernel(const void *kernel, hipStream_t st);
+
 // Launch a product kernel; if timing events are pending they are attached to
 // this dispatch (recorded when the kernel starts and when it completes).
 template <typename... KArgs, typename... Args>
 inline void launch_main(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shm,
                         hipStream_t st, Args... args) {
+    note_kernel(reinterpret_cast<const void *>(kernel), st);
     const TimingEvents ev = take_timing_events();
     if (ev.start || ev.stop)
         hipExtLaunchKernelGGL(kernel, grid, block, shm, st, ev.start, ev.stop, 0u, KArgs(args)...);
@@ -122,5 +127,9 @@ hipError_t launch_w4a16_mfma(const uint16_t *X, int64_t M, int64_t K, int64_t N,
 hipError_t launch_w4a16_generic(const uint16_t *X, int64_t M, int64_t K, int64_t N,
                                 const uint8_t *packed, const float *scales, const float *zeros,
                                 int64_t group, float *Y, hipStream_t st);
+
+// Measurement helpers (probe.hip): an empty kernel and a plain streaming read.
+hipError_t launch_probe_empty(int64_t blocks, hipStream_t st);
+hipError_t launch_probe_read(const uint8_t *src, int64_t bytes, uint32_t *sink, hipStream_t st);
 
 }  // namespace w4

@@ -1,0 +1,35 @@
+"""The measurement helpers and the kernel-name diagnostic, on the GPU."""
+import pytest
+import torch
+
+import int4_weight_quantized_amd as W4
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def test_last_kernel_names_the_kernel_that_ran():
+    d = workloads.random_case(3, 1, 1152, 64)
+    dev = torch.device("cuda:0")
+    p, s, _ = W4.w4_quantize_weight(torch.from_numpy(d["W"]).to(dev), "sym")
+    W4.w4a8_linear(torch.from_numpy(d["x"]).to(dev), p, s)
+    assert W4.w4_last_path() == "gemv_dot4"
+    assert "k_gemv_dot4" in W4.w4_last_kernel()
+    x16 = torch.from_numpy(workloads.random_case(4, 300, 1024, 256)["x"]).to(dev)
+    p2, s2, _ = W4.w4_quantize_weight(torch.randn(1024, 256, device=dev) * 0.02, "sym")
+    W4.w4a8_linear(x16, p2, s2)
+    assert "k_gemm_mfma" in W4.w4_last_kernel()
+    torch.cuda.synchronize()
+
+
+def test_probes_run():
+    src = torch.ones(4041216, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda:0")
+    W4.w4_probe_read(src, sink)
+    assert W4.w4_last_path() == "probe_read" and "k_probe_read" in W4.w4_last_kernel()
+    W4.w4_probe_empty(432)
+    assert W4.w4_last_path() == "probe_empty"
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0  # XOR of all-ones data is 0: no store
+    with pytest.raises(W4.W4Error):
+        W4.w4_probe_read(src[:15], sink)
