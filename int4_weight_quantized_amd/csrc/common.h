@@ -102,6 +102,23 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
     return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// Max over the 64 lanes of a wave of values >= 0 (no NaN), through their bit
+// patterns: for non-negative floats the unsigned order of the bits is the
+// float order, so each step is one integer max of a DPP-moved operand (no
+// canonicalizing float max).  The result is wave-uniform.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    uint32_t b = __float_as_uint(v);
+    b = max(b, (uint32_t)dpp<kQuadSwap1>((int)b));
+    b = max(b, (uint32_t)dpp<kQuadSwap2>((int)b));
+    b = max(b, (uint32_t)dpp<kRowHalfMirror>((int)b));
+    b = max(b, (uint32_t)dpp<kRowMirror>((int)b));
+    const uint32_t r0 = __builtin_amdgcn_readlane((int)b, 0);
+    const uint32_t r1 = __builtin_amdgcn_readlane((int)b, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane((int)b, 32);
+    const uint32_t r3 = __builtin_amdgcn_readlane((int)b, 48);
+    return __uint_as_float(max(max(r0, r1), max(r2, r3)));
+}
+
 // ------------------------------------------------- direct buffer->LDS loads
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -213,6 +230,31 @@ __device__ __forceinline__ int quant_code_fast(float v, float s, float rs, float
     float r = rintf(quotient_rn(v, s, rs));
     r = fminf(fmaxf(r, lo), hi);
     return (int)r;
+}
+
+// fl(a / 127) for a >= 0 without a division where it is safe: with
+// y = fl(1/127), q = fl(a y), r = fma(-q, 127, a) is exact and fma(r, y, q)
+// is the correctly rounded quotient (Markstein's theorem; checked for every
+// float a in [2^-100, 2^128)).  Smaller a take the IEEE division.
+__device__ __forceinline__ float div127(float a) {
+    constexpr float y = 1.0f / 127.0f;
+    if (a >= 0x1p-100f) {
+        const float q = a * y;
+        const float r = __builtin_fmaf(-q, 127.0f, a);
+        return __builtin_fmaf(r, y, q);
+    }
+    return a / 127.0f;
+}
+
+// Round-half-to-even of t (|t| <= 127.5) to an int8 code in the low byte of
+// the result: t + 1.5 * 2^23 lies in [2^23, 2^24), where fp32 values are the
+// integers, so the add rounds t to the nearest integer, ties to even; the bit
+// pattern of 1.5 * 2^23 ends in a zero byte, so the sum's low byte is that
+// integer modulo 256 (checked for every float t with |t| <= 127.5).  The
+// quotient of a value of a row by the row's absmax scale never leaves that
+// range, so the clamp to [-128, 127] never binds and is not needed.
+__device__ __forceinline__ uint32_t code_in_low_byte(float t) {
+    return __float_as_uint(t + 12582912.0f);
 }
 
 // An activation row's scale, prepared for quant_code_row.  A scale below

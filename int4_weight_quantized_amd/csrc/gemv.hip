@@ -55,41 +55,42 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args args) {
     const W4A8Args a = args_now(args);
     constexpr int T = 16 * ROWS;  // threads
     constexpr int KPC = W8 ? 16 : 32;  // codes per 16-byte chunk
-    // 8-groups of k per thread (K <= 16 * KPC * UB)
+    // 8-groups of k per thread (K <= 16 * KPC * UB): pre-quantized input
     constexpr int NG = (2 * KPC * UB / 16 + ROWS - 1) / ROWS;
+    // 4-groups of k per thread: fp32 input (spread over every thread, so that
+    // the quantization chain each thread runs is as short as it can be)
+    constexpr int NQ = (4 * KPC * UB + T - 1) / T;
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ float red[T / kWave][M];
     int8_t *xs = reinterpret_cast<int8_t *>(smem);
     const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
-    const int K = (int)a.K, KB = W8 ? K : K / 2, C = K / KPC, G8 = K / 8;
+    const int K = (int)a.K, KB = W8 ? K : K / 2, C = K / KPC, G8 = K / 8, G4 = K / 4;
     const int j = t & 15, r = t >> 4;
     const int64_t n0 = (int64_t)blockIdx.x * ROWS;
     const int rows = (int)min((int64_t)ROWS, a.N - n0);
 
-    // (1) activations: group g = t + T*i holds k = 8g .. 8g+7 of each row.
-    float4 xa[M][NG], xb[M][NG];
-    float4 da[DIV ? NG : 1], db[DIV ? NG : 1];
-    uint2 xn[M][NG];
-    if (FUSED) {
+    // (1) activations: fp32 4-group q = t + T*i holds k = 4q .. 4q+3 of each
+    // row; int8 8-group g = t + T*i holds k = 8g .. 8g+7.
+    float4 xv[M][FUSED ? NQ : 1];
+    float4 dv[DIV ? NQ : 1];
+    uint2 xn[M][FUSED ? 1 : NG];
+    if constexpr (FUSED) {
         const auto rx = make_rsrc(a.X, (int64_t)M * K * 4);
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int i = 0; i < NG; ++i) {
-                const int g = t + T * i;
-                const int off = g < G8 ? (m * K + 8 * g) * 4 : kOOB;
-                xa[m][i] = bloadf4(rx, off);
-                xb[m][i] = bloadf4(rx, off + 16);
+            for (int i = 0; i < NQ; ++i) {
+                const int q = t + T * i;
+                xv[m][i] = bloadf4(rx, q < G4 ? (m * K + 4 * q) * 4 : kOOB);
             }
         if (DIV) {
-            // divisors of the thread's 8-groups (out-of-range groups read 0
+            // divisors of the thread's 4-groups (out-of-range groups read 0
             // and are replaced by 1 where they are used)
             const auto rd = make_rsrc(a.act_div, (int64_t)K * 4);
 #pragma unroll
-            for (int i = 0; i < NG; ++i) {
-                const int g = t + T * i;
-                da[i] = bloadf4(rd, g < G8 ? 32 * g : kOOB);
-                db[i] = bloadf4(rd, g < G8 ? 32 * g + 16 : kOOB);
+            for (int i = 0; i < NQ; ++i) {
+                const int q = t + T * i;
+                dv[i] = bloadf4(rd, q < G4 ? 16 * q : kOOB);
             }
         }
     } else {
@@ -129,70 +130,81 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args args) {
 
     // (3) activations -> int8 P8 layout in LDS, scales in registers.
     float sxm[M];
-    if (FUSED && DIV) {
+    if constexpr (FUSED && DIV) {
 #pragma unroll
-        for (int i = 0; i < NG; ++i) {
-            if (t + T * i >= G8) da[i] = db[i] = float4{1.f, 1.f, 1.f, 1.f};
+        for (int i = 0; i < NQ; ++i) {
+            if (t + T * i >= G4) dv[i] = float4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                xa[m][i].x = xa[m][i].x / da[i].x;
-                xa[m][i].y = xa[m][i].y / da[i].y;
-                xa[m][i].z = xa[m][i].z / da[i].z;
-                xa[m][i].w = xa[m][i].w / da[i].w;
-                xb[m][i].x = xb[m][i].x / db[i].x;
-                xb[m][i].y = xb[m][i].y / db[i].y;
-                xb[m][i].z = xb[m][i].z / db[i].z;
-                xb[m][i].w = xb[m][i].w / db[i].w;
+                xv[m][i].x = xv[m][i].x / dv[i].x;
+                xv[m][i].y = xv[m][i].y / dv[i].y;
+                xv[m][i].z = xv[m][i].z / dv[i].z;
+                xv[m][i].w = xv[m][i].w / dv[i].w;
             }
         }
     }
-    if (FUSED) {
+    if constexpr (FUSED) {
+        // row absmax: thread, wave (integer DPP max of the non-negative
+        // values' bits), then the block's waves through LDS
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             float am = 0.0f;
 #pragma unroll
-            for (int i = 0; i < NG; ++i) {
-                am = fmaxf(am, fmaxf(fmaxf(fabsf(xa[m][i].x), fabsf(xa[m][i].y)),
-                                     fmaxf(fabsf(xa[m][i].z), fabsf(xa[m][i].w))));
-                am = fmaxf(am, fmaxf(fmaxf(fabsf(xb[m][i].x), fabsf(xb[m][i].y)),
-                                     fmaxf(fabsf(xb[m][i].z), fabsf(xb[m][i].w))));
-            }
-            am = wave_max_dpp(am);
+            for (int i = 0; i < NQ; ++i)
+                am = fmaxf(am, fmaxf(fmaxf(fabsf(xv[m][i].x), fabsf(xv[m][i].y)),
+                                     fmaxf(fabsf(xv[m][i].z), fabsf(xv[m][i].w))));
+            am = wave_max_nonneg(am);
             if (lane == 0) red[wave][m] = am;
         }
         lds_barrier();
+        // codes of a 4-group (low bytes of c0..c3) into the LDS copy of the
+        // row: P8 order [x0 x2 x4 x6 | x1 x3 x5 x7] inside each 8-group, so
+        // the group's even k go to bytes 2h, 2h+1 and its odd k to bytes
+        // 4+2h, 5+2h of 8-group q/2 (h = q%2); natural order for 8-bit weights
+        auto put = [&](int m, int q, uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {
+            if (W8) {
+                *reinterpret_cast<uint32_t *>(xs + m * K + 4 * q) =
+                    (c0 & 0xFFu) | ((c1 & 0xFFu) << 8) | ((c2 & 0xFFu) << 16) | (c3 << 24);
+            } else {
+                int8_t *g = xs + m * K + 8 * (q >> 1) + 2 * (q & 1);
+                *reinterpret_cast<uint16_t *>(g) = (uint16_t)((c0 & 0xFFu) | ((c2 & 0xFFu) << 8));
+                *reinterpret_cast<uint16_t *>(g + 4) = (uint16_t)((c1 & 0xFFu) | ((c3 & 0xFFu) << 8));
+            }
+        };
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             float am = red[0][m];
 #pragma unroll
             for (int w = 1; w < T / kWave; ++w) am = fmaxf(am, red[w][m]);
-            const float s = (am == 0.0f) ? 0.0f : am / 127.0f;
+            const float s = (am == 0.0f) ? 0.0f : div127(am);
             sxm[m] = s;
-            // codes of the thread's 8-groups, stored P8: [x0 x2 x4 x6 | x1 x3 x5 x7]
-            // (natural order for 8-bit weights)
-            auto quantize = [&](auto code) {
+            if (s >= kFastQuotientMinScale) {  // row-uniform
+                // correctly rounded quotient without a division, rounded by
+                // one add (|v / s| <= 127.5 for every value of the row)
+                const float rs = 1.0f / s;
 #pragma unroll
-                for (int i = 0; i < NG; ++i) {
-                    const int g = t + T * i;
-                    if (g < G8) {
-                        const float4 v0 = xa[m][i], v1 = xb[m][i];
-                        uint2 p;
-                        if (W8) {
-                            p.x = pack4_i8(code(v0.x), code(v0.y), code(v0.z), code(v0.w));
-                            p.y = pack4_i8(code(v1.x), code(v1.y), code(v1.z), code(v1.w));
-                        } else {
-                            p.x = pack4_i8(code(v0.x), code(v0.z), code(v1.x), code(v1.z));
-                            p.y = pack4_i8(code(v0.y), code(v0.w), code(v1.y), code(v1.w));
-                        }
-                        *reinterpret_cast<uint2 *>(xs + m * K + 8 * g) = p;
+                for (int i = 0; i < NQ; ++i) {
+                    const int q = t + T * i;
+                    if (q < G4) {
+                        const float4 v = xv[m][i];
+                        put(m, q, code_in_low_byte(quotient_rn(v.x, s, rs)),
+                            code_in_low_byte(quotient_rn(v.y, s, rs)),
+                            code_in_low_byte(quotient_rn(v.z, s, rs)),
+                            code_in_low_byte(quotient_rn(v.w, s, rs)));
                     }
                 }
-            };
-            if (s >= kFastQuotientMinScale) {  // row-uniform
-                const float rs = 1.0f / s;
-                quantize([&](float v) { return quant_code_fast(v, s, rs, -128.f, 127.f); });
-            } else {
-                quantize([&](float v) { return quant_code(v, s, -128.f, 127.f); });
+            } else {  // zero or tiny scale: IEEE division per value
+#pragma unroll
+                for (int i = 0; i < NQ; ++i) {
+                    const int q = t + T * i;
+                    if (q < G4) {
+                        const float4 v = xv[m][i];
+                        put(m, q, (uint32_t)quant_code(v.x, s, -128.f, 127.f),
+                            (uint32_t)quant_code(v.y, s, -128.f, 127.f),
+                            (uint32_t)quant_code(v.z, s, -128.f, 127.f),
+                            (uint32_t)quant_code(v.w, s, -128.f, 127.f));
+                    }
+                }
             }
         }
     } else {
