@@ -115,6 +115,7 @@ def lib():
             "w4_last_kernel": ([], ctypes.c_char_p),
             "w4_probe_empty": ([_I, _P], ctypes.c_int),
             "w4_probe_read": ([_P, _I, _P, _P], ctypes.c_int),
+            "w4_probe_mfma": ([_I, ctypes.c_int, _P, _P, _P], ctypes.c_int),
             "w4_time_next_kernel": ([_P, _P], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
@@ -149,6 +150,16 @@ def w4_probe_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     dev = src.device
     _check("w4_probe_read", lib().w4_probe_read(_dev(src, "src", src.dtype), src.numel() *
                                                 src.element_size(),
+                                                _dev(sink, "sink", torch.int32, (64,), dev),
+                                                _stream(stream)))
+
+
+def w4_probe_mfma(blocks: int, iters: int, times: torch.Tensor, sink: torch.Tensor,
+                  stream=None) -> None:
+    """Int8 MFMA clock / rate probe (a measurement helper); times: int64 [blocks, 4]."""
+    dev = times.device
+    _check("w4_probe_mfma", lib().w4_probe_mfma(int(blocks), int(iters),
+                                                _dev(times, "times", torch.int64, (blocks, 4)),
                                                 _dev(sink, "sink", torch.int32, (64,), dev),
                                                 _stream(stream)))
 

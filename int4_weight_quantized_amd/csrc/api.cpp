@@ -223,6 +223,14 @@ int w4_probe_empty(int64_t blocks, void *stream) {
                     w4::launch_probe_empty(blocks, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int w4_probe_mfma(int64_t blocks, int iters, uint64_t *times, uint32_t *sink, void *stream) {
+    if (!times || !sink) return W4_ERR_NULL;
+    if (blocks < 1 || blocks > 65536 || iters < 1) return W4_ERR_SHAPE;
+    if (!aligned(times, 8) || !aligned(sink, 4)) return W4_ERR_ALIGN;
+    return launched("probe_mfma", w4::launch_probe_mfma(blocks, iters, times, sink,
+                                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
 int w4_probe_read(const void *src, int64_t bytes, uint32_t *sink, void *stream) {
     if (!src || !sink) return W4_ERR_NULL;
     if (bytes < 16 || bytes % 16 != 0 || bytes > 0x7F000000) return W4_ERR_SHAPE;

@@ -8,6 +8,9 @@
 //    buffer loads, 4 per thread, whole 64-byte pieces per quarter-wave), with
 //    one conditional store so the loads are kept; the best a kernel that only
 //    reads those bytes once can do.
+//  * k_probe_mfma: back-to-back int8 MFMAs on constant operands, timed with
+//    the shader clock and the constant-rate clock: the clock the matrix units
+//    run at under load on this machine, and their rate on such operands.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,6 +34,42 @@ __global__ __launch_bounds__(256) void k_probe_read(const uint8_t *__restrict__ 
 #pragma unroll
     for (int i = 0; i < kProbeUnroll; ++i) x ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
     if (x == 0x9E3779B9u) sink[blockIdx.x % 64] = x;  // data-dependent: keeps the loads
+}
+
+// Matrix-unit clock and rate: 8 waves per workgroup (two per SIMD), each
+// issuing 16 independent v_mfma_i32_16x16x64_i8 per iteration on small
+// constant operands; wave 0 of each workgroup records the shader-clock and
+// the constant 100 MHz counters at its start and end (times[4 b .. 4 b + 3]).
+__global__ __launch_bounds__(512) void k_probe_mfma(int iters, uint64_t *__restrict__ times,
+                                                    uint32_t *__restrict__ sink) {
+    const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    const int lane = threadIdx.x % kWave;
+    const v4i a = {0x01010101 * (lane % 3), 0x02020202, 0x01010101, 0x03030303 * (lane % 2)};
+    const v4i b = {0x10101010, 0x20202020 * (lane % 2), 0x10101010, 0x30303030};
+    v4i acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = v4i{0, 0, 0, 0};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[i], 0, 0, 0);
+    }
+    int x = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x ^= acc[i][0] ^ acc[i][3];
+    const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+        times[4 * blockIdx.x + 0] = c0;
+        times[4 * blockIdx.x + 1] = c1;
+        times[4 * blockIdx.x + 2] = r0;
+        times[4 * blockIdx.x + 3] = r1;
+    }
+    if (x == 0x5A5A5A5A) sink[blockIdx.x % 64] = (uint32_t)x;  // keeps the products
+}
+
+hipError_t launch_probe_mfma(int64_t blocks, int iters, uint64_t *times, uint32_t *sink,
+                             hipStream_t st) {
+    launch_main(k_probe_mfma, dim3((unsigned)blocks), dim3(512), 0, st, iters, times, sink);
+    return hipGetLastError();
 }
 
 hipError_t launch_probe_empty(int64_t blocks, hipStream_t st) {

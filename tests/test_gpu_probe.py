@@ -33,3 +33,14 @@ def test_probes_run():
     assert int(sink.abs().sum()) == 0  # XOR of all-ones data is 0: no store
     with pytest.raises(W4.W4Error):
         W4.w4_probe_read(src[:15], sink)
+
+
+def test_mfma_probe_reports_a_clock():
+    times = torch.zeros((8, 4), dtype=torch.int64, device="cuda:0")
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda:0")
+    W4.w4_probe_mfma(8, 200, times, sink)
+    torch.cuda.synchronize()
+    t = times.cpu().numpy().astype("float64")
+    assert (t[:, 1] > t[:, 0]).all() and (t[:, 3] > t[:, 2]).all()
+    ghz = (t[:, 1] - t[:, 0]) / ((t[:, 3] - t[:, 2]) / 1e8) / 1e9
+    assert ((ghz > 0.3) & (ghz < 5.0)).all(), ghz
