@@ -22,7 +22,6 @@ thread_local const char *g_last_path = "none";
 thread_local hipEvent_t g_time_start = nullptr, g_time_stop = nullptr;
 // the kernel the current call launches, and the last one of a successful call
 thread_local const void *g_pending_kernel = nullptr, *g_last_kernel = nullptr;
-thread_local hipStream_t g_pending_stream = nullptr, g_last_stream = nullptr;
 
 inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -36,7 +35,6 @@ int launched(const char *path, hipError_t e) {
     if (e != hipSuccess) return W4_ERR_HIP;
     g_last_path = path;
     g_last_kernel = g_pending_kernel;
-    g_last_stream = g_pending_stream;
     return W4_OK;
 }
 
@@ -174,10 +172,7 @@ int check_workspace(int64_t M, int64_t K, void *workspace, size_t bytes) {
 
 }  // namespace
 
-void w4::note_kernel(const void *kernel, hipStream_t st) {
-    g_pending_kernel = kernel;
-    g_pending_stream = st;
-}
+void w4::note_kernel(const void *kernel, hipStream_t) { g_pending_kernel = kernel; }
 
 w4::TimingEvents w4::take_timing_events() {
     TimingEvents ev{g_time_start, g_time_stop};
@@ -213,7 +208,9 @@ const char *w4_last_path(void) { return g_last_path; }
 
 const char *w4_last_kernel(void) {
     if (!g_last_kernel) return "none";
-    const char *name = hipKernelNameRefByPtr(g_last_kernel, g_last_stream);
+    // the launch's stream may be gone by now; a kernel's symbol is the same on
+    // every device, so the null stream (current device) resolves it
+    const char *name = hipKernelNameRefByPtr(g_last_kernel, nullptr);
     return name ? name : "unknown";
 }
 
