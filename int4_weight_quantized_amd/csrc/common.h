@@ -172,6 +172,10 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Workgroup barrier that waits for no memory operation: orders the issue of
+// the loads before it (in every wave) ahead of the loads after it.
+__device__ __forceinline__ void issue_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
