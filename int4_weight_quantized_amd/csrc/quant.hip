@@ -451,8 +451,13 @@ __global__ __launch_bounds__(256) void k_quant_act_reg(const float *__restrict__
         for (int h = 0; h < 2; ++h)
             a = fmaxf(a, fmaxf(fmaxf(fabsf(v[u][h].x), fabsf(v[u][h].y)),
                                fmaxf(fabsf(v[u][h].z), fabsf(v[u][h].w))));
-    a = block_max<4>(a, red);
-    const float s = (a == 0.0f) ? 0.0f : a / 127.0f;
+    // row absmax: integer DPP max of the non-negative values' bits in each
+    // wave, then the 4 waves through LDS
+    a = wave_max_nonneg(a);
+    if ((threadIdx.x % kWave) == 0) red[threadIdx.x / kWave] = a;
+    __syncthreads();
+    a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = (a == 0.0f) ? 0.0f : div127(a);
     if (threadIdx.x == 0) sx[m] = s;
     auto quantize = [&](auto code) {
 #pragma unroll
@@ -474,8 +479,15 @@ __global__ __launch_bounds__(256) void k_quant_act_reg(const float *__restrict__
             *reinterpret_cast<uint2 *>(dst) = p;
         }
     };
-    const RowScale q = row_scale(s);
-    quantize([&](float x) { return quant_code_row(x, q); });
+    if (s >= kFastQuotientMinScale) {  // row-uniform
+        // correctly rounded quotient without a division, rounded by one add
+        // (|x / s| <= 127.5 for every value of the row)
+        const float rs = 1.0f / s;
+        quantize([&](float x) { return (int)code_in_low_byte(quotient_rn(x, s, rs)); });
+    } else {  // zero or tiny scale
+        const RowScale q = row_scale(s);
+        quantize([&](float x) { return quant_code_row(x, q); });
+    }
 }
 
 template <bool P8, bool DIV, bool STEP>
