@@ -723,16 +723,18 @@ static void go_mfma_w(const W4A8Args &a, hipStream_t st) {
 
 // Fused activation quantization (G > 0): worth it while the per-workgroup
 // quantization stays small.  Each wave quantizes ceil(M / 8) rows of K values
-// before its first MFMA; measured against quantizer + GEMV (two launches) the
-// fused kernel is faster up to ceil(M / 8) * K = 3072 (M = 16, K = 1536) and
-// slower from 4096 on (M = 8, K = 4096; M = 16, K = 2048).
+// before its first MFMA; measured against quantizer + GEMV (two launches),
+// with the activation loads ahead of the weights and the division-free
+// chain, the fused kernel is faster up to ceil(M / 8) * K = 4096 (7B-class
+// M = 8, K = 4096: 11.0 -> 9.85 us) and slower beyond (M = 16, K = 4096:
+// 11.1 -> 12.0 us).  Rows of up to 2048 k fit in 32 KB of LDS (G = 4), up to
+// 4096 k in 64 KB (G = 8).
 bool gemv_mfma_fused_ok(int64_t M, int64_t K) {
-    return M >= 1 && M <= 16 && K % 128 == 0 && K <= 2048 && ((M + 7) / 8) * K <= 3072;
+    return M >= 1 && M <= 16 && K % 128 == 0 && K <= 4096 && ((M + 7) / 8) * K <= 4096;
 }
 
-template <int NB, bool W8>
-static void go_mfma_fused(const W4A8Args &a, hipStream_t st) {
-    constexpr int G = 4;  // K <= 512 G = 2048
+template <int NB, bool W8, int G>
+static void go_mfma_fused_g(const W4A8Args &a, hipStream_t st) {
     dim3 grid((unsigned)((a.N + 16 * NB - 1) / (16 * NB)));
     if constexpr (!W8) {
         if (a.pp) {
@@ -741,6 +743,14 @@ static void go_mfma_fused(const W4A8Args &a, hipStream_t st) {
         }
     }
     launch_main(k_gemv_mfma<1, NB, 1, 8, Out::Y, W8, false, G>, grid, dim3(512), 0, st, a);
+}
+
+template <int NB, bool W8>
+static void go_mfma_fused(const W4A8Args &a, hipStream_t st) {
+    if (a.K <= 2048)
+        go_mfma_fused_g<NB, W8, 4>(a, st);  // K <= 512 G
+    else
+        go_mfma_fused_g<NB, W8, 8>(a, st);
 }
 
 template <bool W8>

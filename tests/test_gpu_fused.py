@@ -43,7 +43,8 @@ def bits_equal(a, b):
                           np.ascontiguousarray(b, np.float32).view(np.uint32))
 
 
-CASES = [(1, 1152, 200, "gemv_dot4"), (4, 4096, 70, "gemv_dot4"), (16, 512, 64, "gemv_mfma_fused"),
+CASES = [(1, 1152, 200, "gemv_dot4"), (3, 4096, 70, "gemv_dot4"), (4, 4096, 70, "gemv_mfma_fused"),
+         (4, 8192, 70, "gemv_dot4"), (16, 512, 64, "gemv_mfma_fused"),
          (24, 512, 64, "gemv_mfma"),
          (100, 384, 260, "gemm_mfma"), (300, 384, 520, "gemm_mfma"),  # interior + edge tiles
          (32, 10, 32, "w4a8_generic"), (3, 7, 5, "w4a8_generic")]
@@ -69,7 +70,8 @@ def test_w4a8_relu(M, K, N, path, with_bias):
     assert bits_equal(host(y0), oracle.w4a8_linear(d["x"], pref, sref, b))
 
 
-W8_CASES = [(1, 1152, 200, "w8_gemv_dot4"), (2, 8192, 64, "w8_gemv_mfma"),
+W8_CASES = [(1, 1152, 200, "w8_gemv_dot4"), (3, 4096, 64, "w8_gemv_dot4"),
+            (4, 4096, 64, "w8_gemv_mfma_fused"), (2, 8192, 64, "w8_gemv_mfma"),
             (16, 512, 64, "w8_gemv_mfma_fused"), (24, 512, 64, "w8_gemv_mfma"),
             (100, 384, 260, "w8_gemm_mfma"),
             (300, 256, 516, "w8_gemm_mfma"),

@@ -190,7 +190,8 @@ def _tiny_rows(M, K, seed):
 
 
 @pytest.mark.parametrize("M,K,N,path", [(1, 1152, 64, "gemv_dot4"), (3, 4096, 40, "gemv_dot4"),
-                                        (4, 1152, 48, "gemv_dot4"), (16, 512, 64, "gemv_mfma_fused"),
+                                        (4, 1152, 48, "gemv_mfma_fused"), (4, 4224, 48, "gemv_dot4"),
+                                        (16, 512, 64, "gemv_mfma_fused"),
                                         (24, 512, 64, "gemv_mfma"),
                                         (100, 384, 260, "gemm_mfma")])
 def test_tiny_activation_scales(M, K, N, path):
@@ -367,13 +368,17 @@ def test_gemv_mfma_widths(M, K, N):
 
 
 # the MFMA GEMV with the activation quantization in its prologue: M <= 16,
-# K <= 2048 and ceil(M / 8) * K <= 3072, rows past M padded to 16; at the
-# bounds and just outside them (the two-launch path runs there)
+# K <= 4096 and ceil(M / 8) * K <= 4096, rows past M padded to 16 (LDS rows of
+# up to 2048 k, and of up to 4096 k); at the bounds and just outside them (the
+# two-launch path runs there)
 FUSED_CASES = [(5, 128, 33, "gemv_mfma_fused"), (8, 1152, 130, "gemv_mfma_fused"),
                (8, 2048, 70, "gemv_mfma_fused"), (16, 1152, 260, "gemv_mfma_fused"),
                (9, 1536, 64, "gemv_mfma_fused"), (16, 1536, 50, "gemv_mfma_fused"),
-               (7, 2176, 50, "gemv_mfma"), (9, 2048, 40, "gemv_mfma"),
-               (16, 1664, 40, "gemv_mfma"), (16, 4096, 48, "gemv_mfma")]
+               (7, 2176, 50, "gemv_mfma_fused"), (9, 2048, 40, "gemv_mfma_fused"),
+               (16, 1664, 40, "gemv_mfma_fused"), (8, 4096, 48, "gemv_mfma_fused"),
+               (4, 4096, 40, "gemv_mfma_fused"), (9, 2176, 40, "gemv_mfma"),
+               (16, 2176, 40, "gemv_mfma"), (5, 4224, 40, "gemv_mfma"),
+               (16, 4096, 48, "gemv_mfma")]
 
 
 @pytest.mark.parametrize("M,K,N,path", FUSED_CASES)
