@@ -159,7 +159,7 @@ int w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N,
 /* w4a8_linear followed by an activation, fused into the product kernel's
  * epilogue: Y = act(fl(fl(float(acc) * fl(sx[m] * sw[n])) [+ bias[n]])).
  * For M <= 4 (K % 32 == 0, K <= 8192, 16-byte aligned X and packed), and for
- * M <= 16 with K % 128 == 0, K <= 2048 and ceil(M/8)*K <= 3072 (16-byte
+ * M <= 16 with K % 128 == 0, K <= 4096 and ceil(M/8)*K <= 4096 (16-byte
  * aligned X), the whole decode step -- activation quantization, unpacking,
  * product, dequantization, bias and activation -- is one kernel launch (the
  * workspace is then not touched).
