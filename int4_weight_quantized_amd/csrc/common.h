@@ -67,6 +67,22 @@ constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;
 constexpr int kRowMirror = 0x140;
+constexpr int kRowRor8 = 0x128;      // row_ror:8 (lane r of a row <- lane r ^ 8)
+
+// Lanes r and r ^ 8 of each row of 16 exchange one word: lanes r < 8 keep e
+// and take the partner's e as o, lanes r >= 8 keep o and take the partner's o
+// as e (two DPP moves, each writing one half of the row's lanes).
+__device__ __forceinline__ void swap_halves8(uint32_t &e, uint32_t &o) {
+    const int e0 = (int)e, o0 = (int)o;
+    e = (uint32_t)__builtin_amdgcn_update_dpp(e0, o0, kRowRor8, 0xF, 0xC, false);
+    o = (uint32_t)__builtin_amdgcn_update_dpp(o0, e0, kRowRor8, 0xF, 0x3, false);
+}
+__device__ __forceinline__ void swap_halves8(uint4 &e, uint4 &o) {
+    swap_halves8(e.x, o.x);
+    swap_halves8(e.y, o.y);
+    swap_halves8(e.z, o.z);
+    swap_halves8(e.w, o.w);
+}
 
 // Sum over each row of 16 lanes; every lane of the row gets the sum.
 __device__ __forceinline__ int sum16(int v) {

@@ -386,14 +386,29 @@ hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st) {
 // and the codes and row scales go to LDS before one barrier (the first
 // weight loads stay in flight).  The main loop
 // then reads the activation fragments from LDS.
-template <int MB, int NB, int D, int W, Out OUT, bool W8, bool PP = false, int G = 0>
+// LN (whole-line loads, canonical layout): a load above covers half of each
+// of 16 channels' 128-byte lines; with LN load 0 of a unit covers the whole
+// lines of channels 0-7 of the block and load 1 those of channels 8-15 (lane
+// (kq, r): 16-byte piece 2 kq + r / 8 of channel r % 8, resp. 8 + r % 8), and
+// lanes r and r ^ 8 then swap one of the two words (a DPP row rotate by 8),
+// after which every lane holds pieces 2 kq and 2 kq + 1 of its own channel r.
+// For int4 codes a line is two 128-k steps, so the loop runs over pairs of
+// steps (K % 256 = 0) and the activation fragments of pair t are the chunks
+// 16 t + 4 kq + j, j = 0..3; for int8 codes a line is one step and the pieces
+// are the ones the lane loads without LN.  Measured (graph-replayed, rotating
+// weights, 7B-class layer): M = 16 step 11.1 -> 10.4 us, M = 24 11.8 -> 11.7,
+// M = 48 13.8 -> 14.1 and M = 64 14.8 -> 15.4 (hence int4 LN only up to two
+// row blocks); W8 M = 16 14.9 -> 14.6, M = 64 20.4 -> 19.8; fused int4 M = 4
+// 9.4 -> 9.1, M = 8 9.8 -> 9.6; fused W8 M = 8 13.4 -> 13.6 (not used).
+template <int MB, int NB, int D, int W, Out OUT, bool W8, bool PP = false, int G = 0, bool LN = false>
 __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
     const W4A8Args a = args_now(args);
     constexpr bool FUSED = G > 0;
     static_assert(!FUSED || (MB == 1 && W == 8 && OUT == Out::Y), "fused: 16 rows, 8 waves");
     __shared__ __align__(16) int8_t xs[FUSED ? 16 * 512 * G : 16];  // [K/16][16][16]
     __shared__ float sxs[16];
-    constexpr int WL = W8 ? 2 : 1;  // 16-byte weight loads per lane and step
+    constexpr int WL = (W8 || LN) ? 2 : 1;  // 16-byte weight loads per lane and unit
+    constexpr bool LP = LN && !W8;  // int4 codes: units of two 128-k steps
     constexpr int kPairs = MB * NB;                 // 16x16 output blocks
     constexpr int kPerWave = (kPairs + W - 1) / W;  // epilogue blocks per wave
     __shared__ int red[kPairs * 4 * kWave];         // [pair][i][lane]
@@ -404,7 +419,8 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
     const int K = (int)a.K, KB = W8 ? K : K / 2;
     const int64_t N = a.N, M = a.M;
     const int S = K / 128;
-    const int s0 = S * wave / W, s1 = S * (wave + 1) / W;
+    const int SU = LP ? S / 2 : S;  // loop units: 128-k steps, or pairs of them
+    const int s0 = SU * wave / W, s1 = SU * (wave + 1) / W;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * NB;
     const int cols = (int)min((int64_t)(16 * NB), N - n0);
 
@@ -412,6 +428,7 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
     if (!FUSED) __syncthreads();  // (fused: the prologue's barrier covers it)
 
     static_assert(!PP || !W8, "shuffled layout of int4 codes");
+    static_assert(!LN || !PP, "whole-line loads: canonical layout");
     const auto rb = PP ? make_rsrc(a.packed + (n0 / 16) * (int64_t)S * 1024,
                                    (int64_t)((cols + 15) / 16) * S * 1024)
                        : make_rsrc(a.packed + n0 * KB, (int64_t)cols * KB);
@@ -420,12 +437,17 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
         boff[nb] = PP ? nb * S * 1024 + r16 * 64 + 16 * (kq ^ ((r16 / 2) % 4))
+                 : LN ? (16 * nb + r16 % 8) * KB + 16 * (2 * kq + r16 / 8)
                       : (16 * nb + r16) * KB + kq * 16 * WL;
-    const int wstep = PP ? 1024 : 64 * WL;  // bytes per 128-k step
+    const int wstep = PP ? 1024 : LP ? 128 : 64 * WL;  // bytes per unit
+    const int hstep = LN ? 8 * KB : 16;                 // second load of a unit
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) aoff[mb] = (2 * kq * (int)M + 16 * mb + r16) * 16;
+    for (int mb = 0; mb < MB; ++mb) aoff[mb] = ((LP ? 4 : 2) * kq * (int)M + 16 * mb + r16) * 16;
     // activations are chunk-major, [K/16][M][16]: chunk c = 8 s + 2 kq + half
-    const int achunk = (int)M * 16, astep = 8 * achunk;
+    // (LN with int4 codes: c = 16 t + 4 kq + j for pair t)
+    const int achunk = (int)M * 16, astep = (LP ? 16 : 8) * achunk;
+    // LDS copy (fused): [K/16][16][16]
+    const int xso = ((LP ? 4 : 2) * kq * 16 + r16) * 16, xsstep = LP ? 4096 : 2048;
 
     v4i acc[MB][NB];
 #pragma unroll
@@ -433,7 +455,7 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = v4i{0, 0, 0, 0};
 
-    uint4 wr[D][NB][WL], xr0[D][MB], xr1[D][MB];
+    uint4 wr[D][NB][WL], xr0[D][MB], xr1[D][MB], xr2[D][MB], xr3[D][MB];
     // Weight loads: a shuffled 1 KB tile is read whole by one load and never
     // again, so it streams (non-temporal); in the canonical layout a load
     // covers half of each 128-byte line (the next step or the second 16-byte
@@ -447,17 +469,25 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int h = 0; h < WL; ++h)
-                wr[d][nb][h] = wload(rb, ok ? boff[nb] + wstep * ss + 16 * h : kOOB);
+                wr[d][nb][h] = wload(rb, ok ? boff[nb] + wstep * ss + hstep * h : kOOB);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             if (FUSED) {  // from LDS (16 rows per chunk); steps past s1 hold zero weights
-                const int o = (2 * kq * 16 + r16) * 16 + 2048 * min(ss, S - 1);
+                const int o = xso + xsstep * min(ss, SU - 1);
                 xr0[d][mb] = *reinterpret_cast<const uint4 *>(xs + o);
                 xr1[d][mb] = *reinterpret_cast<const uint4 *>(xs + o + 256);
+                if (LP) {
+                    xr2[d][mb] = *reinterpret_cast<const uint4 *>(xs + o + 512);
+                    xr3[d][mb] = *reinterpret_cast<const uint4 *>(xs + o + 768);
+                }
             } else {
                 const int o = ok ? aoff[mb] + astep * ss : kOOB;
                 xr0[d][mb] = bload16(ra, o);
                 xr1[d][mb] = bload16(ra, ok ? o + achunk : kOOB);
+                if (LP) {
+                    xr2[d][mb] = bload16(ra, ok ? o + 2 * achunk : kOOB);
+                    xr3[d][mb] = bload16(ra, ok ? o + 3 * achunk : kOOB);
+                }
             }
         }
     };
@@ -487,7 +517,7 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int h = 0; h < WL; ++h)
-                    wr[d][nb][h] = wload(rb, s0 + d < s1 ? boff[nb] + wstep * (s0 + d) + 16 * h : kOOB);
+                    wr[d][nb][h] = wload(rb, s0 + d < s1 ? boff[nb] + wstep * (s0 + d) + hstep * h : kOOB);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
@@ -549,9 +579,13 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
             const int ss = s0 + d;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
-                const int o = (2 * kq * 16 + r16) * 16 + 2048 * min(ss, S - 1);
+                const int o = xso + xsstep * min(ss, SU - 1);
                 xr0[d][mb] = *reinterpret_cast<const uint4 *>(xs + o);
                 xr1[d][mb] = *reinterpret_cast<const uint4 *>(xs + o + 256);
+                if (LP) {
+                    xr2[d][mb] = *reinterpret_cast<const uint4 *>(xs + o + 512);
+                    xr3[d][mb] = *reinterpret_cast<const uint4 *>(xs + o + 768);
+                }
             }
         }
     } else {
@@ -587,12 +621,44 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
     for (int s = s0; s < s1; s += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            {
+            if constexpr (LP) {
+                // lanes r < 8 keep piece 2 kq of load 0 and take the partner's
+                // (piece 2 kq + 1 of the same channel); lanes r >= 8 keep piece
+                // 2 kq + 1 of load 1 and take the partner's piece 2 kq
+                v4i b0[NB], b1[NB], b2[NB], b3[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    uint4 e = wr[d][nb][0], o = wr[d][nb][1];
+                    swap_halves8(e, o);
+                    b0[nb] = v4i{(int)lo16(e.x), (int)hi16(e.x), (int)lo16(e.y), (int)hi16(e.y)};
+                    b1[nb] = v4i{(int)lo16(e.z), (int)hi16(e.z), (int)lo16(e.w), (int)hi16(e.w)};
+                    b2[nb] = v4i{(int)lo16(o.x), (int)hi16(o.x), (int)lo16(o.y), (int)hi16(o.y)};
+                    b3[nb] = v4i{(int)lo16(o.z), (int)hi16(o.z), (int)lo16(o.w), (int)hi16(o.w)};
+                }
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const uint4 x0 = xr0[d][mb], x1 = xr1[d][mb], x2 = xr2[d][mb], x3 = xr3[d][mb];
+                    const v4i a0 = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
+                    const v4i a1 = {(int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+                    const v4i a2 = {(int)x2.x, (int)x2.y, (int)x2.z, (int)x2.w};
+                    const v4i a3 = {(int)x3.x, (int)x3.y, (int)x3.z, (int)x3.w};
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0[nb], acc[mb][nb], 0, 0, 0);
+                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1[nb], acc[mb][nb], 0, 0, 0);
+                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, b2[nb], acc[mb][nb], 0, 0, 0);
+                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, b3[nb], acc[mb][nb], 0, 0, 0);
+                    }
+                }
+                fetch(d, s + d + D);
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
                 v4i b0[NB], b1[NB];
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     if (W8) {
-                        const uint4 w0 = wr[d][nb][0], w1 = wr[d][nb][WL - 1];
+                        uint4 w0 = wr[d][nb][0], w1 = wr[d][nb][WL - 1];
+                        if (LN) swap_halves8(w0, w1);
                         b0[nb] = v4i{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w};
                         b1[nb] = v4i{(int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
                     } else {
@@ -659,6 +725,18 @@ static void go_mfma(const W4A8Args &a, hipStream_t st) {
         if (a.pp) {
             launch_main(k_gemv_mfma<MB, NB, D, W, Out::Y, false, true>, grid, dim3(64 * W), 0, st,
                         a);
+            return;
+        }
+    }
+    // whole-line loads: int8 codes always, int4 codes up to two row blocks
+    if constexpr (W8 || MB <= 2) {
+        if (W8 || a.K % 256 == 0) {
+            if (a.out == Out::I32)
+                launch_main(k_gemv_mfma<MB, NB, D, W, Out::I32, W8, false, 0, true>, grid,
+                            dim3(64 * W), 0, st, a);
+            else
+                launch_main(k_gemv_mfma<MB, NB, D, W, Out::Y, W8, false, 0, true>, grid,
+                            dim3(64 * W), 0, st, a);
             return;
         }
     }
@@ -739,6 +817,11 @@ static void go_mfma_fused_g(const W4A8Args &a, hipStream_t st) {
     if constexpr (!W8) {
         if (a.pp) {
             launch_main(k_gemv_mfma<1, NB, 1, 8, Out::Y, false, true, G>, grid, dim3(512), 0, st, a);
+            return;
+        }
+        if (a.K % 256 == 0) {  // whole-line loads (int4 codes only)
+            launch_main(k_gemv_mfma<1, NB, 1, 8, Out::Y, false, false, G, true>, grid, dim3(512), 0,
+                        st, a);
             return;
         }
     }

@@ -367,6 +367,41 @@ def test_gemv_mfma_widths(M, K, N):
     assert np.array_equal(host(acc), oracle.matmul_i32(xq, pref, K))
 
 
+# whole-line weight loads of the MFMA GEMV: for int4 codes with K % 256 = 0
+# and up to two row blocks (M <= 32) the loop runs over pairs of 128-k steps
+# (waves with no pair, a ragged split of the pairs over the 8 waves, a ragged
+# last channel block); three row blocks and K % 256 = 128 take per-step loads;
+# int8 codes always load whole lines, one step per unit
+LINE_CASES = [(17, 256, 100), (24, 768, 130), (32, 3840, 70), (20, 1280, 9300),
+              (32, 640, 48), (33, 512, 50), (48, 1024, 40)]
+
+
+@pytest.mark.parametrize("M,K,N", LINE_CASES)
+def test_gemv_mfma_line_loads(M, K, N):
+    d = workloads.random_case(M * 7 + K + N, M, K, N, outliers=4, bias=True)
+    pref, sref = oracle.quantize_weight_sym(d["W"])
+    yref = oracle.w4a8_linear(d["x"], pref, sref, d["bias"])
+    packed, sw, _ = W4.w4_quantize_weight(dev(d["W"]), "sym")
+    bufy, y, py = guarded((M, N), torch.float32)
+    W4.w4a8_linear(dev(d["x"]), packed, sw, bias=dev(d["bias"]), Y=y)
+    assert W4.w4_last_path() == "gemv_mfma"
+    got = host(y)
+    assert bits_equal(got, yref), report("y", got, yref)
+    assert guards_intact(bufy, py)
+    xq, _ = oracle.quantize_act(d["x"])
+    acc = W4.w4a8_matmul_i32(dev(xq), packed)
+    assert W4.w4_last_path() == "gemv_mfma"
+    assert np.array_equal(host(acc), oracle.matmul_i32(xq, pref, K))
+    qref, s8 = oracle.quantize_weight_w8(d["W"])
+    Wq, sw8 = W4.w8_quantize_weight(dev(d["W"]))
+    y8 = host(W4.w8a8_linear(dev(d["x"]), Wq, sw8, bias=dev(d["bias"])))
+    assert W4.w4_last_path() == "w8_gemv_mfma"
+    assert bits_equal(y8, oracle.w8a8_linear(d["x"], qref, s8, d["bias"]))
+    acc8 = W4.w8a8_matmul_i32(dev(xq), Wq)
+    assert W4.w4_last_path() == "w8_gemv_mfma"
+    assert np.array_equal(host(acc8), oracle.matmul_w8_i32(xq, qref))
+
+
 # the MFMA GEMV with the activation quantization in its prologue: M <= 16,
 # K <= 4096 and ceil(M / 8) * K <= 4096, rows past M padded to 16 (LDS rows of
 # up to 2048 k, and of up to 4096 k); at the bounds and just outside them (the
