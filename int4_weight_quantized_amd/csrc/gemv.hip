@@ -400,6 +400,11 @@ hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st) {
 // M = 48 13.8 -> 14.1 and M = 64 14.8 -> 15.4 (hence int4 LN only up to two
 // row blocks); W8 M = 16 14.9 -> 14.6, M = 64 20.4 -> 19.8; fused int4 M = 4
 // 9.4 -> 9.1, M = 8 9.8 -> 9.6; fused W8 M = 8 13.4 -> 13.6 (not used).
+// In the fused kernel (activation fragments from LDS) the next pair's weights
+// are requested between the MFMAs of the pair's two halves (fused M = 4
+// 9.1 -> 8.9 us, M = 8 9.75 -> 9.5 us); with the activations from HBM / L2
+// that order was slower (M = 16 10.45 -> 10.87 us), so there the whole next
+// pair is requested after both halves.
 template <int MB, int NB, int D, int W, Out OUT, bool W8, bool PP = false, int G = 0, bool LN = false>
 __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
     const W4A8Args a = args_now(args);
@@ -463,7 +468,9 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
     auto wload = [&](const __amdgpu_buffer_rsrc_t &r, int off) {
         return PP ? bload16_nt(r, off) : bload16(r, off);
     };
-    auto fetch = [&](int d, int ss) {
+    // weights and the activation fragments of the unit's first half (for LP:
+    // the chunks of piece 2 kq), then those of its second half (piece 2 kq + 1)
+    auto fetch_wa = [&](int d, int ss) {
         const bool ok = ss < s1;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -476,20 +483,33 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
                 const int o = xso + xsstep * min(ss, SU - 1);
                 xr0[d][mb] = *reinterpret_cast<const uint4 *>(xs + o);
                 xr1[d][mb] = *reinterpret_cast<const uint4 *>(xs + o + 256);
-                if (LP) {
-                    xr2[d][mb] = *reinterpret_cast<const uint4 *>(xs + o + 512);
-                    xr3[d][mb] = *reinterpret_cast<const uint4 *>(xs + o + 768);
-                }
             } else {
                 const int o = ok ? aoff[mb] + astep * ss : kOOB;
                 xr0[d][mb] = bload16(ra, o);
                 xr1[d][mb] = bload16(ra, ok ? o + achunk : kOOB);
-                if (LP) {
-                    xr2[d][mb] = bload16(ra, ok ? o + 2 * achunk : kOOB);
-                    xr3[d][mb] = bload16(ra, ok ? o + 3 * achunk : kOOB);
+            }
+        }
+    };
+    auto fetch_b = [&](int d, int ss) {
+        if constexpr (LP) {
+            const bool ok = ss < s1;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                if (FUSED) {
+                    const int o = xso + xsstep * min(ss, SU - 1);
+                    xr2[d][mb] = *reinterpret_cast<const uint4 *>(xs + o + 512);
+                    xr3[d][mb] = *reinterpret_cast<const uint4 *>(xs + o + 768);
+                } else {
+                    const int o = ok ? aoff[mb] + astep * ss + 2 * achunk : kOOB;
+                    xr2[d][mb] = bload16(ra, o);
+                    xr3[d][mb] = bload16(ra, ok ? o + achunk : kOOB);
                 }
             }
         }
+    };
+    auto fetch = [&](int d, int ss) {
+        fetch_wa(d, ss);
+        fetch_b(d, ss);
     };
     if constexpr (FUSED) {
         // the activation row of the first pass first (every wave's before any
@@ -624,33 +644,53 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
             if constexpr (LP) {
                 // lanes r < 8 keep piece 2 kq of load 0 and take the partner's
                 // (piece 2 kq + 1 of the same channel); lanes r >= 8 keep piece
-                // 2 kq + 1 of load 1 and take the partner's piece 2 kq
-                v4i b0[NB], b1[NB], b2[NB], b3[NB];
+                // 2 kq + 1 of load 1 and take the partner's piece 2 kq.  The
+                // first half's MFMAs (piece 2 kq) run before the second half's
+                // activations are waited for; fused, the next unit's weights and
+                // first half are requested in between.
+                uint4 e[NB], o[NB];
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    uint4 e = wr[d][nb][0], o = wr[d][nb][1];
-                    swap_halves8(e, o);
-                    b0[nb] = v4i{(int)lo16(e.x), (int)hi16(e.x), (int)lo16(e.y), (int)hi16(e.y)};
-                    b1[nb] = v4i{(int)lo16(e.z), (int)hi16(e.z), (int)lo16(e.w), (int)hi16(e.w)};
-                    b2[nb] = v4i{(int)lo16(o.x), (int)hi16(o.x), (int)lo16(o.y), (int)hi16(o.y)};
-                    b3[nb] = v4i{(int)lo16(o.z), (int)hi16(o.z), (int)lo16(o.w), (int)hi16(o.w)};
+                    e[nb] = wr[d][nb][0];
+                    o[nb] = wr[d][nb][1];
+                    swap_halves8(e[nb], o[nb]);
                 }
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
-                    const uint4 x0 = xr0[d][mb], x1 = xr1[d][mb], x2 = xr2[d][mb], x3 = xr3[d][mb];
+                    const uint4 x0 = xr0[d][mb], x1 = xr1[d][mb];
                     const v4i a0 = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
                     const v4i a1 = {(int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const uint4 w = e[nb];
+                        const v4i b0 = {(int)lo16(w.x), (int)hi16(w.x), (int)lo16(w.y), (int)hi16(w.y)};
+                        const v4i b1 = {(int)lo16(w.z), (int)hi16(w.z), (int)lo16(w.w), (int)hi16(w.w)};
+                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc[mb][nb], 0, 0, 0);
+                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc[mb][nb], 0, 0, 0);
+                    }
+                }
+                if constexpr (FUSED) {
+                    fetch_wa(d, s + d + D);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const uint4 x2 = xr2[d][mb], x3 = xr3[d][mb];
                     const v4i a2 = {(int)x2.x, (int)x2.y, (int)x2.z, (int)x2.w};
                     const v4i a3 = {(int)x3.x, (int)x3.y, (int)x3.z, (int)x3.w};
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
-                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0[nb], acc[mb][nb], 0, 0, 0);
-                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1[nb], acc[mb][nb], 0, 0, 0);
-                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, b2[nb], acc[mb][nb], 0, 0, 0);
-                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, b3[nb], acc[mb][nb], 0, 0, 0);
+                        const uint4 w = o[nb];
+                        const v4i b2 = {(int)lo16(w.x), (int)hi16(w.x), (int)lo16(w.y), (int)hi16(w.y)};
+                        const v4i b3 = {(int)lo16(w.z), (int)hi16(w.z), (int)lo16(w.w), (int)hi16(w.w)};
+                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, b2, acc[mb][nb], 0, 0, 0);
+                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, b3, acc[mb][nb], 0, 0, 0);
                     }
                 }
-                fetch(d, s + d + D);
+                if constexpr (FUSED)
+                    fetch_b(d, s + d + D);
+                else
+                    fetch(d, s + d + D);
                 __builtin_amdgcn_sched_barrier(0);
             } else {
                 v4i b0[NB], b1[NB];
