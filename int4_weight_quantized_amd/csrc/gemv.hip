@@ -851,21 +851,31 @@ bool gemv_mfma_fused_ok(int64_t M, int64_t K) {
     return M >= 1 && M <= 16 && K % 128 == 0 && K <= 4096 && ((M + 7) / 8) * K <= 4096;
 }
 
+// Two units in flight per wave (D = 2) in the fused kernel: a wave's slice of
+// a K <= 4096 layer is a few units, so with D = 2 most of its weights are
+// requested before the prologue's quantization.  Measured (graph-replayed,
+// rotating weights, us): shuffled tiles 7B-class M = 4 8.65 -> 8.0, M = 8
+// 9.3 -> 8.7; whole-line loads M = 4 8.75 -> 8.5, M = 8 even; int8 weights
+// Gemma-like M = 4 5.42 -> 5.05, M = 16 7.0 -> 6.67, 7B-class M = 4
+// 12.6 -> 12.35; but the half-line int4 loads (K % 256 = 128) Gemma-like
+// M = 4, 8, 16 4.5 -> 4.65, 4.7 -> 4.95, 5.7 -> 6.0, so those keep D = 1.
+// (In the non-fused kernel D = 2 was slower on every path: 7B-class M = 16
+// 10.45 -> 11.46, shuffled 9.8 -> 10.1, int8 14.6 -> 15.3.)
 template <int NB, bool W8, int G>
 static void go_mfma_fused_g(const W4A8Args &a, hipStream_t st) {
     dim3 grid((unsigned)((a.N + 16 * NB - 1) / (16 * NB)));
     if constexpr (!W8) {
         if (a.pp) {
-            launch_main(k_gemv_mfma<1, NB, 1, 8, Out::Y, false, true, G>, grid, dim3(512), 0, st, a);
+            launch_main(k_gemv_mfma<1, NB, 2, 8, Out::Y, false, true, G>, grid, dim3(512), 0, st, a);
             return;
         }
         if (a.K % 256 == 0) {  // whole-line loads (int4 codes only)
-            launch_main(k_gemv_mfma<1, NB, 1, 8, Out::Y, false, false, G, true>, grid, dim3(512), 0,
+            launch_main(k_gemv_mfma<1, NB, 2, 8, Out::Y, false, false, G, true>, grid, dim3(512), 0,
                         st, a);
             return;
         }
     }
-    launch_main(k_gemv_mfma<1, NB, 1, 8, Out::Y, W8, false, G>, grid, dim3(512), 0, st, a);
+    launch_main(k_gemv_mfma<1, NB, W8 ? 2 : 1, 8, Out::Y, W8, false, G>, grid, dim3(512), 0, st, a);
 }
 
 template <int NB, bool W8>
