@@ -43,7 +43,8 @@ def bits_equal(a, b):
                           np.ascontiguousarray(b, np.float32).view(np.uint32))
 
 
-CASES = [(1, 1152, 200, "gemv_dot4"), (3, 4096, 70, "gemv_dot4"), (4, 4096, 70, "gemv_mfma_fused"),
+CASES = [(1, 1152, 200, "gemv_dot4"), (2, 4096, 70, "gemv_dot4"), (3, 4096, 70, "gemv_mfma_fused"),
+         (3, 1152, 70, "gemv_mfma_fused"), (4, 4096, 70, "gemv_mfma_fused"),
          (4, 8192, 70, "gemv_dot4"), (16, 512, 64, "gemv_mfma_fused"),
          (24, 512, 64, "gemv_mfma"),
          (100, 384, 260, "gemm_mfma"), (300, 384, 520, "gemm_mfma"),  # interior + edge tiles

@@ -189,7 +189,8 @@ def _tiny_rows(M, K, seed):
     return X
 
 
-@pytest.mark.parametrize("M,K,N,path", [(1, 1152, 64, "gemv_dot4"), (3, 4096, 40, "gemv_dot4"),
+@pytest.mark.parametrize("M,K,N,path", [(1, 1152, 64, "gemv_dot4"), (2, 4096, 40, "gemv_dot4"),
+                                        (3, 4096, 40, "gemv_mfma_fused"),
                                         (4, 1152, 48, "gemv_mfma_fused"), (4, 4224, 48, "gemv_dot4"),
                                         (16, 512, 64, "gemv_mfma_fused"),
                                         (24, 512, 64, "gemv_mfma"),

@@ -101,7 +101,8 @@ def test_w4_prepack_weights(K, N):
     assert np.array_equal(host(W4.w4_unprepack_weights(wpp, K, N)), p)
 
 
-W4A8_PP = [(1, 1152, 200, "gemv_dot4_prepacked"), (3, 4096, 70, "gemv_dot4_prepacked"),
+W4A8_PP = [(1, 1152, 200, "gemv_dot4_prepacked"), (2, 4096, 70, "gemv_dot4_prepacked"),
+           (3, 4096, 70, "gemv_mfma_fused_prepacked"),
            (4, 4096, 70, "gemv_mfma_fused_prepacked"),
            (3, 8192 + 128, 40, "gemv_mfma_prepacked"), (8, 1152, 130, "gemv_mfma_fused_prepacked"),
            (16, 4096, 96, "gemv_mfma_prepacked"), (64, 512, 33, "gemv_mfma_prepacked"),
