@@ -268,9 +268,16 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_mfma(const uint16_t *__restric
 // one round over the CUs (the 28672-channel layer: 7 waves per half, 256
 // blocks).
 //
-// LDS layouts (all reads are 16 rows x one 16-byte chunk per quarter-wave of
-// 64-byte rows, chunk kq at slot kq ^ ((row/2) % 4), which is conflict-free):
-//   W plane j (step j of the stage): [16*WPH channels][64 B]
+// LDS layouts (all reads are 16 rows x one 16-byte chunk per quarter-wave,
+// conflict-free):
+//   W (canonical layout): [16*WPH channels][128 B], the channel's whole
+//     128-byte line of the stage (both steps; one 1 KB load covers 8
+//     channels' lines), piece 4 j + kq (step j, chunk kq) at slot
+//     (4 j + kq) ^ ((channel/2) % 8).  Loading 64-byte halves of 16
+//     channels' lines per load instead measured 45.5 -> 43.1 us (median,
+//     70B-class layer).
+//   W plane j (shuffled layout, step j of the stage): [16*WPH channels][64 B],
+//     chunk kq at slot kq ^ ((channel/2) % 4)
 //   X plane (j, kq): [16 rows][64 B] = the 32 activations x[r][128 j + 32 kq ..
 //     + 32] of each row, 16-byte chunk q at slot q ^ kq ^ ((r/2) % 4) (the
 //     quarter-waves kq then read distinct slot columns: conflict-free)
@@ -337,8 +344,8 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
     uint8_t *const hbase = ring + half * kLStages * L::kStage;
 
     // Stage t of a half covers steps s0 + 2t, s0 + 2t + 1.  Its 1 KB
-    // wave-loads q: weights (step j = q / WPH, channels 16*(q % WPH) + lane/4),
-    // then activations (step, plane kq, row lane/4: 64 contiguous bytes per
+    // wave-loads q: weights (canonical: channels 8q + lane/8, both steps;
+    // shuffled: step j = q / WPH, block q % WPH), then activations (step, plane kq, row lane/4: 64 contiguous bytes per
     // row), then the scale and
     // zero-point tables (lane = channel within a 64-channel group).
     // Wave wl issues q = wl + WPH*i, i < kPerWave; indices past the end repeat
@@ -352,11 +359,13 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
         for (int i = 0; i < L::kPerWave; ++i) {
             const int q = min(wl + WPH * i, L::kLoads - 1);
             if (q < L::kLoadsW) {
-                const int j = q / WPH, c = 16 * (q % WPH) + lane / 4;
-                if (PP)  // 1 KB of block q % WPH, step + j, already in LDS order
+                if (PP) {  // 1 KB of block q % WPH, step + j, already in LDS order
+                    const int j = q / WPH;
                     dma16(rw, base + q * 1024, (q % WPH) * G * 1024 + lane * 16, (step + j) * 1024);
-                else
-                    dma16(rw, base + q * 1024, c * KB + 16 * sw4, (step + j) * 64);
+                } else {   // the whole 128-byte lines (both steps) of channels 8q .. 8q + 7
+                    const int c = 8 * q + lane / 8;
+                    dma16(rw, base + q * 1024, c * KB + 16 * ((lane % 8) ^ ((c / 2) % 8)), step * 64);
+                }
             } else if (q < L::kLoadsW + L::kLoadsX) {
                 const int qq = q - L::kLoadsW, j = qq / 4, pk = qq % 4, r = lane / 4;
                 dma16(rx, base + L::kW + qq * 1024, r * K * 2 + 64 * pk + 16 * (sw4 ^ pk),
@@ -380,6 +389,12 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
     const int ch = 16 * wl + r16;                         // this lane's channel
     const int swz = (kq ^ ((r16 / 2) % 4)) * 16;          // (row/2)%4 = (r16/2)%4
     const int woff = ch * 64 + swz;
+    // canonical layout: channel ch's line at (ch / 8) KB + (ch % 8) * 128,
+    // piece 4 j + kq at slot (4 j + kq) ^ ((ch / 2) % 8)
+    int wline[kLSteps];
+#pragma unroll
+    for (int j = 0; j < kLSteps; ++j)
+        wline[j] = (ch / 8) * 1024 + (ch % 8) * 128 + 16 * ((4 * j + kq) ^ ((ch / 2) % 8));
     const int xoff = L::kW + kq * 1024 + r16 * 64;
 
     auto compute = [&](int t) {
@@ -403,7 +418,7 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
         const bool fast = __all(ok);
 #pragma unroll
         for (int j = 0; j < kLSteps; ++j) {
-            const uint4 w = *reinterpret_cast<const uint4 *>(sb + j * (L::kCh * 64) + woff);
+            const uint4 w = *reinterpret_cast<const uint4 *>(sb + (PP ? j * (L::kCh * 64) + woff : wline[j]));
             uint4 xr[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
