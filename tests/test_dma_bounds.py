@@ -133,9 +133,10 @@ def w4a16_lds_loads(M, K, N, WPH, pp=False):
                             if pp:
                                 voff = (q % WPH) * G * 1024 + LANES * 16
                                 soff = (step + j) * 1024
-                            else:
-                                c = 16 * (q % WPH) + LANES // 4
-                                voff, soff = c * KB + 16 * sw4, (step + j) * 64
+                            else:  # whole 128-byte lines of channels 8q .. 8q + 7
+                                c = 8 * q + LANES // 8
+                                voff = c * KB + 16 * ((LANES % 8) ^ ((c // 2) % 8))
+                                soff = step * 64
                             _check("W", w_alloc, w_base, w_range, voff, soff)
                         elif q < loads_w + loads_x:
                             qq = q - loads_w
@@ -148,10 +149,14 @@ def w4a16_lds_loads(M, K, N, WPH, pp=False):
                             voff = bq * (G // 2) * 256 + (LANES % 16) * 16
                             _check("SZ", t_alloc, t_base, t_range, voff, (step // 2) * 256)
                         else:
+                            # the first stage of each pair of stages loads the
+                            # quads; the second one's loads are out of range
                             qq = q - loads_w - loads_x
                             part = qq % loads_sz
-                            voff = (64 * part + LANES) * G * 4
-                            _check("S/Z", t_alloc, t_base, t_range, voff, (step // 4) * 16)
+                            first = (step % 4 == 0) | (np.arange(T)[:, None] == 0)
+                            voff = np.where(first, (64 * part + LANES) * G * 4, 0x7FFF0000)
+                            soff = np.where(first, (step // 4) * 16, 0)
+                            _check("S/Z", t_alloc, t_base, t_range, voff, soff)
 
 
 GEMM_SHAPES = [(300, 512, 1000), (130, 256, 129), (65, 128, 17), (257, 384, 300), (512, 256, 512),
