@@ -159,8 +159,9 @@ int w4a8_linear(const float *X, int64_t M, int64_t K, int64_t N,
 /* w4a8_linear followed by an activation, fused into the product kernel's
  * epilogue: Y = act(fl(fl(float(acc) * fl(sx[m] * sw[n])) [+ bias[n]])).
  * For M <= 4 (K % 32 == 0, K <= 8192, 16-byte aligned X and packed), and for
- * M <= 16 with K % 128 == 0, K <= 4096 and ceil(M/8)*K <= 4096 (16-byte
- * aligned X), the whole decode step -- activation quantization, unpacking,
+ * M <= 16 with K % 128 == 0 and K <= 4096 (16-byte aligned X; with int8
+ * weights or shuffled tiles also ceil(M/8)*K <= 4096), the whole decode
+ * step -- activation quantization, unpacking,
  * product, dequantization, bias and activation -- is one kernel launch (the
  * workspace is then not touched).
  *   activation  W4_ACT_NONE or W4_ACT_RELU; any other value: W4_ERR_ARG.

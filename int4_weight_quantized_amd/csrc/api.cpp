@@ -91,7 +91,7 @@ int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const floa
 
     // the MFMA GEMV that quantizes the activations itself (one launch)
     const bool fused_ok = fast && src == Src::FP32 && !act_div && !acc && aligned(X, 16) &&
-                          gemv_mfma_fused_ok(M, K);
+                          gemv_mfma_fused_ok(M, K, w8, pp);
     // Few rows: one VALU GEMV launch (activation quantization fused); from
     // three rows on (int8 weights: four) the fused MFMA GEMV is faster where it
     // applies (measured, graph-replayed, us: M = 3 7B-class 9.0-9.5 -> 8.3,

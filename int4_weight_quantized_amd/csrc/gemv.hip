@@ -379,7 +379,8 @@ hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st) {
 // G > 0 (fused activation quantization, M <= 16, K <= 512 G, fp32 X): the
 // workgroup quantizes the activation rows itself into LDS, in the same
 // chunk-major layout with 16 rows (rows past M get zero codes): wave w takes
-// rows w and w + 8, lane l the 8-groups l, l + 64, ... of the row; the loads
+// rows w and w + 8 (8 waves) or row w (16 waves), lane l the 8-groups l,
+// l + 64, ... of the row; the loads
 // of row w precede the weight loads of the first steps, the row absmax is a
 // wave reduction, the codes come from the same division-free chain as in the
 // dot4 kernel (measured: Gemma-like M = 8 4.90 -> 4.63 us, bit-identical),
@@ -409,7 +410,8 @@ template <int MB, int NB, int D, int W, Out OUT, bool W8, bool PP = false, int G
 __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
     const W4A8Args a = args_now(args);
     constexpr bool FUSED = G > 0;
-    static_assert(!FUSED || (MB == 1 && W == 8 && OUT == Out::Y), "fused: 16 rows, 8 waves");
+    static_assert(!FUSED || (MB == 1 && (W == 8 || W == 16) && OUT == Out::Y),
+                  "fused: 16 rows, 8 or 16 waves");
     __shared__ __align__(16) int8_t xs[FUSED ? 16 * 512 * G : 16];  // [K/16][16][16]
     __shared__ float sxs[16];
     constexpr int WL = (W8 || LN) ? 2 : 1;  // 16-byte weight loads per lane and unit
@@ -540,8 +542,8 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
                     wr[d][nb][h] = wload(rb, s0 + d < s1 ? boff[nb] + wstep * (s0 + d) + hstep * h : kOOB);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            const int m = wave + 8 * pass;
+        for (int pass = 0; pass < (FUSED ? 16 / W : 1); ++pass) {
+            const int m = wave + W * pass;
             if (m < M) {  // wave-uniform
                 if (pass == 1) xload(m);  // rows 8 .. 15
                 float am = 0.0f;
@@ -840,15 +842,21 @@ static void go_mfma_w(const W4A8Args &a, hipStream_t st) {
 }
 
 // Fused activation quantization (G > 0): worth it while the per-workgroup
-// quantization stays small.  Each wave quantizes ceil(M / 8) rows of K values
-// before its first MFMA; measured against quantizer + GEMV (two launches),
-// with the activation loads ahead of the weights and the division-free
-// chain, the fused kernel is faster up to ceil(M / 8) * K = 4096 (7B-class
+// quantization stays small.  With 8 waves each wave quantizes ceil(M / 8)
+// rows of K values before its first MFMA; measured against quantizer + GEMV
+// (two launches), with the activation loads ahead of the weights and the
+// division-free chain, that is faster up to ceil(M / 8) * K = 4096 (7B-class
 // M = 8, K = 4096: 11.0 -> 9.85 us) and slower beyond (M = 16, K = 4096:
-// 11.1 -> 12.0 us).  Rows of up to 2048 k fit in 32 KB of LDS (G = 4), up to
-// 4096 k in 64 KB (G = 8).
-bool gemv_mfma_fused_ok(int64_t M, int64_t K) {
-    return M >= 1 && M <= 16 && K % 128 == 0 && K <= 4096 && ((M + 7) / 8) * K <= 4096;
+// 11.1 -> 12.0 us).  The canonical int4 layout takes 16 waves from 8 or 9
+// rows on (below), one row per wave, and then every M <= 16 with K <= 4096
+// is faster fused (7B-class M = 10, 12, 16: 10.3 -> 9.5, 10.35 -> 9.7,
+// 10.65 -> 10.35 us); int8 weights and shuffled tiles keep the 8-wave bound
+// (16 waves measured slower there: W8 7B-class M = 16 14.55 -> 15.05 us,
+// shuffled M = 16 9.65 -> 9.85 us).  Rows of up to 2048 k fit in 32 KB of
+// LDS (G = 4), up to 4096 k in 64 KB (G = 8).
+bool gemv_mfma_fused_ok(int64_t M, int64_t K, bool w8, bool pp) {
+    if (!(M >= 1 && M <= 16 && K % 128 == 0 && K <= 4096)) return false;
+    return (!w8 && !pp) || ((M + 7) / 8) * K <= 4096;
 }
 
 // Two units in flight per wave (D = 2) in the fused kernel: a wave's slice of
@@ -869,9 +877,23 @@ static void go_mfma_fused_g(const W4A8Args &a, hipStream_t st) {
             launch_main(k_gemv_mfma<1, NB, 2, 8, Out::Y, false, true, G>, grid, dim3(512), 0, st, a);
             return;
         }
+        // 16 waves, one activation row each (and twice the waves to spread a
+        // short K over), from 8 rows on with whole-line loads and from 9 rows
+        // on with half-line loads (graph-replayed, us: 7B-class M = 8
+        // 9.48 -> 9.15, Gemma-like M = 12 5.35 -> 5.12, M = 16 5.72 -> 5.38;
+        // at M = 4 and Gemma-like M = 8 they were slower: 8.5 -> 9.0,
+        // 4.64 -> 4.80)
         if (a.K % 256 == 0) {  // whole-line loads (int4 codes only)
-            launch_main(k_gemv_mfma<1, NB, 2, 8, Out::Y, false, false, G, true>, grid, dim3(512), 0,
-                        st, a);
+            if (a.M >= 8)
+                launch_main(k_gemv_mfma<1, NB, 1, 16, Out::Y, false, false, G, true>, grid,
+                            dim3(1024), 0, st, a);
+            else
+                launch_main(k_gemv_mfma<1, NB, 2, 8, Out::Y, false, false, G, true>, grid,
+                            dim3(512), 0, st, a);
+            return;
+        }
+        if (a.M > 8) {
+            launch_main(k_gemv_mfma<1, NB, 1, 16, Out::Y, false, false, G>, grid, dim3(1024), 0, st, a);
             return;
         }
     }

@@ -91,8 +91,8 @@ hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st);
 // inside (natural for 8-bit weights).
 hipError_t launch_gemv_mfma(const W4A8Args &a, hipStream_t st);
 // MFMA GEMV with the activation quantization in its prologue (a.X fp32,
-// Out::Y, no divisors): for gemv_mfma_fused_ok(M, K) shapes.
-bool gemv_mfma_fused_ok(int64_t M, int64_t K);
+// Out::Y, no divisors): for gemv_mfma_fused_ok(M, K, w8, pp) shapes.
+bool gemv_mfma_fused_ok(int64_t M, int64_t K, bool w8, bool pp);
 hipError_t launch_gemv_mfma_fused(const W4A8Args &a, hipStream_t st);
 
 // Any M, K % 128 == 0: LDS-tiled MFMA GEMM; a.Xq in P8 layout (natural for

@@ -55,7 +55,8 @@ def _op(kind, W, b, K):
 CASES = [
     ("w4a8", 1, 1152, 6912, "gemv_dot4"),
     ("w4a8", 8, 1152, 6912, "gemv_mfma_fused"),
-    ("w4a8", 16, 4096, 1024, "gemv_mfma"),
+    ("w4a8", 16, 4096, 1024, "gemv_mfma_fused"),     # 16 waves, one row each
+    ("w4a8", 24, 4096, 1024, "gemv_mfma"),
     ("w4a8", 300, 512, 520, "gemm_mfma"),
     ("w4a8_relu_pp", 8, 1152, 1000, "gemv_mfma_fused_prepacked"),
     ("w8a8", 16, 4096, 1024, "w8_gemv_mfma"),

@@ -403,22 +403,27 @@ def test_gemv_mfma_line_loads(M, K, N):
     assert np.array_equal(host(acc8), oracle.matmul_w8_i32(xq, qref))
 
 
-# the MFMA GEMV with the activation quantization in its prologue: M <= 16,
-# K <= 4096 and ceil(M / 8) * K <= 4096, rows past M padded to 16 (LDS rows of
-# up to 2048 k, and of up to 4096 k); at the bounds and just outside them (the
-# two-launch path runs there)
-FUSED_CASES = [(5, 128, 33, "gemv_mfma_fused"), (8, 1152, 130, "gemv_mfma_fused"),
-               (8, 2048, 70, "gemv_mfma_fused"), (16, 1152, 260, "gemv_mfma_fused"),
-               (9, 1536, 64, "gemv_mfma_fused"), (16, 1536, 50, "gemv_mfma_fused"),
-               (7, 2176, 50, "gemv_mfma_fused"), (9, 2048, 40, "gemv_mfma_fused"),
-               (16, 1664, 40, "gemv_mfma_fused"), (8, 4096, 48, "gemv_mfma_fused"),
-               (4, 4096, 40, "gemv_mfma_fused"), (9, 2176, 40, "gemv_mfma"),
-               (16, 2176, 40, "gemv_mfma"), (5, 4224, 40, "gemv_mfma"),
-               (16, 4096, 48, "gemv_mfma")]
+# the MFMA GEMV with the activation quantization in its prologue: M <= 16 and
+# K <= 4096 on the canonical int4 layout (8 waves up to 8 rows with half-line
+# loads and up to 7 rows with whole-line loads, 16 waves, one row each, above),
+# and also ceil(M / 8) * K <= 4096 for shuffled tiles and int8 weights; rows
+# past M padded to 16 (LDS rows of up to 2048 k, and of up to 4096 k); at the
+# bounds and just outside them (the two-launch path runs there).
+# (M, K, N, fused on the canonical layout, fused with shuffled tiles / int8)
+FUSED_CASES = [(5, 128, 33, True, True), (8, 1152, 130, True, True),
+               (8, 2048, 70, True, True), (16, 1152, 260, True, True),
+               (9, 1536, 64, True, True), (16, 1536, 50, True, True),
+               (7, 2176, 50, True, True), (9, 2048, 40, True, True),
+               (16, 1664, 40, True, True), (8, 4096, 48, True, True),
+               (4, 4096, 40, True, True), (9, 2176, 40, True, False),
+               (16, 2176, 40, True, False), (12, 4096, 70, True, False),
+               (10, 2688, 50, True, False), (16, 3968, 33, True, False),
+               (16, 4096, 48, True, False), (5, 4224, 40, False, False)]
 
 
-@pytest.mark.parametrize("M,K,N,path", FUSED_CASES)
-def test_gemv_mfma_fused(M, K, N, path):
+@pytest.mark.parametrize("M,K,N,fused,fused8", FUSED_CASES)
+def test_gemv_mfma_fused(M, K, N, fused, fused8):
+    path = "gemv_mfma_fused" if fused else "gemv_mfma"
     d = workloads.random_case(M * 11 + K + N, M, K, N, outliers=min(6, K), bias=True)
     X = d["x"]
     if M > 6:
@@ -438,13 +443,13 @@ def test_gemv_mfma_fused(M, K, N, path):
     if K % 128 == 0:
         wpp = W4.w4_prepack_weights(packed)
         y2 = host(W4.w4a8_linear_prepacked(dev(X), wpp, sw, bias=dev(d["bias"])))
-        want = "gemv_mfma_fused_prepacked" if path == "gemv_mfma_fused" else "gemv_mfma_prepacked"
+        want = "gemv_mfma_fused_prepacked" if fused8 else "gemv_mfma_prepacked"
         assert W4.w4_last_path() == want
         assert bits_equal(y2, yref)
     qref, s8 = oracle.quantize_weight_w8(d["W"])
     Wq, sw8 = W4.w8_quantize_weight(dev(d["W"]))
     y8 = host(W4.w8a8_linear(dev(X), Wq, sw8, bias=dev(d["bias"])))
-    assert W4.w4_last_path() == "w8_" + path
+    assert W4.w4_last_path() == ("w8_gemv_mfma_fused" if fused8 else "w8_gemv_mfma")
     assert bits_equal(y8, oracle.w8a8_linear(X, qref, s8, d["bias"]))
 
 
