@@ -93,12 +93,12 @@ int w4a8_dispatch(Src src, bool w8, const float *X, const int8_t *Xq, const floa
     const bool fused_ok = fast && src == Src::FP32 && !act_div && !acc && aligned(X, 16) &&
                           gemv_mfma_fused_ok(M, K, w8, pp);
     // Few rows: one VALU GEMV launch (activation quantization fused); from
-    // three rows on (int8 weights: four) the fused MFMA GEMV is faster where it
-    // applies (measured, graph-replayed, us: M = 3 7B-class 9.0-9.5 -> 8.3,
-    // shuffled tiles 9.1-9.5 -> 7.8, Gemma-like shuffled 4.28 -> 3.93, canonical
-    // even; int8 weights at M = 3 even or slower (7B-class 11.9 -> 12.45); at
-    // M = 2 the VALU GEMV is faster on every path: 7B-class 7.46 against 8.13).
-    if (aligned16 && gemv_dot4_ok(M, K, w8) && !(M >= (w8 ? 4 : 3) && fused_ok)) {
+    // three rows on the fused MFMA GEMV is faster where it applies (measured,
+    // graph-replayed, us: M = 3 7B-class 9.0-9.5 -> 8.3, shuffled tiles
+    // 9.1-9.5 -> 7.8, Gemma-like shuffled 4.28 -> 3.93, canonical even; int8
+    // weights 7B-class 11.95 -> 11.55, Gemma-like 4.95 -> 4.70); at M = 2 the
+    // VALU GEMV is faster on every path (7B-class 7.46 against 8.13).
+    if (aligned16 && gemv_dot4_ok(M, K, w8) && !(M >= 3 && fused_ok)) {
         if (src == Src::FP32) a.X = X;
         return launched(w8 ? "w8_gemv_dot4" : pp ? "gemv_dot4_prepacked" : "gemv_dot4",
                         launch_gemv_dot4(a, st));

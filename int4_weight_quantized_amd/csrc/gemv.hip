@@ -400,7 +400,8 @@ hipError_t launch_gemv_dot4(const W4A8Args &a, hipStream_t st) {
 // weights, 7B-class layer): M = 16 step 11.1 -> 10.4 us, M = 24 11.8 -> 11.7,
 // M = 48 13.8 -> 14.1 and M = 64 14.8 -> 15.4 (hence int4 LN only up to two
 // row blocks); W8 M = 16 14.9 -> 14.6, M = 64 20.4 -> 19.8; fused int4 M = 4
-// 9.4 -> 9.1, M = 8 9.8 -> 9.6; fused W8 M = 8 13.4 -> 13.6 (not used).
+// 9.4 -> 9.1, M = 8 9.8 -> 9.6; fused W8 M = 8 13.4 -> 13.6 before the loads
+// were made non-temporal, 13.4 -> 12.5 after (used).
 // In the fused kernel (activation fragments from LDS) the next pair's weights
 // are requested between the MFMAs of the pair's two halves (fused M = 4
 // 9.1 -> 8.9 us, M = 8 9.75 -> 9.5 us); with the activations from HBM / L2
@@ -463,12 +464,14 @@ __global__ __launch_bounds__(64 * W) void k_gemv_mfma(W4A8Args args) {
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = v4i{0, 0, 0, 0};
 
     uint4 wr[D][NB][WL], xr0[D][MB], xr1[D][MB], xr2[D][MB], xr3[D][MB];
-    // Weight loads: a shuffled 1 KB tile is read whole by one load and never
-    // again, so it streams (non-temporal); in the canonical layout a load
-    // covers half of each 128-byte line (the next step or the second 16-byte
-    // load reads the other half), so those lines must stay cached.
+    // Weight loads: a shuffled 1 KB tile, or with LN a set of whole 128-byte
+    // lines, is read whole by one load and never again, so it streams
+    // (non-temporal; with LN, graph-replayed 7B-class M = 16 10.45 -> 10.15 us,
+    // M = 24 11.6 -> 11.05, W8 M = 16 14.5 -> 13.05, M = 64 19.9 -> 19.0); a
+    // half-line load (canonical layout without LN) leaves the other half of
+    // its lines to the next step or the second load, so those stay cached.
     auto wload = [&](const __amdgpu_buffer_rsrc_t &r, int off) {
-        return PP ? bload16_nt(r, off) : bload16(r, off);
+        return (PP || LN) ? bload16_nt(r, off) : bload16(r, off);
     };
     // weights and the activation fragments of the unit's first half (for LP:
     // the chunks of piece 2 kq), then those of its second half (piece 2 kq + 1)
@@ -850,9 +853,9 @@ static void go_mfma_w(const W4A8Args &a, hipStream_t st) {
 // 11.1 -> 12.0 us).  The canonical int4 layout takes 16 waves from 8 or 9
 // rows on (below), one row per wave, and then every M <= 16 with K <= 4096
 // is faster fused (7B-class M = 10, 12, 16: 10.3 -> 9.5, 10.35 -> 9.7,
-// 10.65 -> 10.35 us); int8 weights and shuffled tiles keep the 8-wave bound
-// (16 waves measured slower there: W8 7B-class M = 16 14.55 -> 15.05 us,
-// shuffled M = 16 9.65 -> 9.85 us).  Rows of up to 2048 k fit in 32 KB of
+// 10.65 -> 10.35 us); int8 weights and shuffled tiles keep the bound (fused
+// with 16 waves, 7B-class M = 16: int8 13.4-14.0 against 12.95 us for the
+// two launches, shuffled 9.85 against 9.65 us).  Rows of up to 2048 k fit in 32 KB of
 // LDS (G = 4), up to 4096 k in 64 KB (G = 8).
 bool gemv_mfma_fused_ok(int64_t M, int64_t K, bool w8, bool pp) {
     if (!(M >= 1 && M <= 16 && K % 128 == 0 && K <= 4096)) return false;
@@ -897,7 +900,19 @@ static void go_mfma_fused_g(const W4A8Args &a, hipStream_t st) {
             return;
         }
     }
-    launch_main(k_gemv_mfma<1, NB, W8 ? 2 : 1, 8, Out::Y, W8, false, G>, grid, dim3(512), 0, st, a);
+    if constexpr (W8) {
+        // whole-line loads (non-temporal: 7B-class M = 4 12.6 -> 11.6 us,
+        // Gemma-like M = 8 5.29 -> 4.97 us); 16 waves above 8 rows
+        // (Gemma-like M = 12 6.08 -> 5.33 us, M = 16 6.47 -> 5.37 us)
+        if (a.M > 8)
+            launch_main(k_gemv_mfma<1, NB, 1, 16, Out::Y, true, false, G, true>, grid, dim3(1024),
+                        0, st, a);
+        else
+            launch_main(k_gemv_mfma<1, NB, 2, 8, Out::Y, true, false, G, true>, grid, dim3(512), 0,
+                        st, a);
+        return;
+    }
+    launch_main(k_gemv_mfma<1, NB, 1, 8, Out::Y, false, false, G>, grid, dim3(512), 0, st, a);
 }
 
 template <int NB, bool W8>

@@ -71,7 +71,8 @@ def test_w4a8_relu(M, K, N, path, with_bias):
     assert bits_equal(host(y0), oracle.w4a8_linear(d["x"], pref, sref, b))
 
 
-W8_CASES = [(1, 1152, 200, "w8_gemv_dot4"), (3, 4096, 64, "w8_gemv_dot4"),
+W8_CASES = [(1, 1152, 200, "w8_gemv_dot4"), (2, 4096, 64, "w8_gemv_dot4"),
+            (3, 4096, 64, "w8_gemv_mfma_fused"), (12, 1152, 64, "w8_gemv_mfma_fused"),
             (4, 4096, 64, "w8_gemv_mfma_fused"), (2, 8192, 64, "w8_gemv_mfma"),
             (16, 512, 64, "w8_gemv_mfma_fused"), (24, 512, 64, "w8_gemv_mfma"),
             (100, 384, 260, "w8_gemm_mfma"),
