@@ -48,6 +48,7 @@ INT8_PEAK_TOPS = 5000.0      # dense int8 MFMA
 BF16_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA
 ROTATE_BYTES = 640 << 20     # > 2 x the 256 MB Infinity Cache
 METRIC = "W4A8 linear: GB/s (M=1 GEMV) and int8 TOPS (M=4096), % of roofline"
+PLAIN_WRITES = {"write67m": 67108864}  # the 4096 x 4096 prefill's fp32 output
 
 
 def log(msg):
@@ -364,6 +365,15 @@ def platform_probes(torch, hip, w4, head_grid):
         del bufs
         torch.cuda.empty_cache()
     out["plain_read"] = reads
+    # a plain write of the prefill product's fp32 output (4 M N bytes) into one
+    # buffer, as the product writes its output
+    nbytes = PLAIN_WRITES["write67m"]
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sec, L = region_time(torch, hip, lambda i: w4.w4_probe_write(dst, i), nbytes / 5e12 + 2e-6, 20)
+    out["plain_write"] = [{"bytes": nbytes, "as": "prefill_output", "us": round(sec * 1e6, 3),
+                           "GBps": round(nbytes / sec / 1e9, 1), "launches": L}]
+    del dst
+    torch.cuda.empty_cache()
     # the matrix units' clock under load (shader-clock / 100 MHz counters of
     # each workgroup) and their int8 rate on constant operands
     import statistics
@@ -566,6 +576,8 @@ def main():
                          "w8a8_gemma_m1, "
                          "w8a8_mlp7b_m1, w8a8_prefill, pp_<W4A8 workload> (shuffled tiles); "
                          "copy (a 64 MiB device copy, for counter calibration); "
+                         "write67m (a plain streaming write of the 4096^3 prefill's fp32 "
+                         "output bytes); "
                          "empty (an empty kernel of the headline's grid); read4m, read22m, "
                          "read134m (plain streaming reads of the headline's, the 7B-class and "
                          "the 70B-class W4A16 layer's bytes)")
@@ -587,6 +599,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     hip = Hip()
 
+    if args.only in PLAIN_WRITES:
+        # a plain write of the prefill product's output bytes into one buffer
+        dst = torch.empty(PLAIN_WRITES[args.only], dtype=torch.uint8, device="cuda")
+        for i in range(args.warmup + args.steps):
+            w4.w4_probe_write(dst, i)
+        torch.cuda.synchronize()
+        log(f"{args.only}: {args.warmup + args.steps} launches done")
+        return
     if args.only == "empty" or (args.only or "").startswith("read"):
         # platform references for the profilers: an empty launch of the
         # headline kernel's grid, or plain reads of 4 / 22.6 / 134 MB

@@ -399,6 +399,14 @@ int w4_probe_empty(int64_t blocks, void *stream);
  * W4_ERR_ALIGN or W4_ERR_HIP. */
 int w4_probe_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
 
+/* A plain streaming write of `bytes` device bytes at `dst` (16-byte aligned;
+ * 16 <= bytes <= 0x7F000000, bytes % 16 == 0): every 32-bit word becomes
+ * `value`, each byte written once with a 16-byte non-temporal store.  The
+ * fastest a kernel that only writes those bytes once can go (the prefill
+ * product's fp32 output is 4 M N bytes).  Returns W4_OK, W4_ERR_NULL,
+ * W4_ERR_SHAPE, W4_ERR_ALIGN or W4_ERR_HIP. */
+int w4_probe_write(void *dst, int64_t bytes, uint32_t value, void *stream);
+
 /* Back-to-back int8 MFMAs (v_mfma_i32_16x16x64_i8, 16 independent chains per
  * wave, 8 waves per workgroup, small constant operands) for `iters`
  * iterations in each of `blocks` workgroups (1 <= blocks <= 65536, iters >= 1).

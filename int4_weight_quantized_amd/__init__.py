@@ -115,6 +115,7 @@ def lib():
             "w4_last_kernel": ([], ctypes.c_char_p),
             "w4_probe_empty": ([_I, _P], ctypes.c_int),
             "w4_probe_read": ([_P, _I, _P, _P], ctypes.c_int),
+            "w4_probe_write": ([_P, _I, ctypes.c_uint32, _P], ctypes.c_int),
             "w4_probe_mfma": ([_I, ctypes.c_int, _P, _P, _P], ctypes.c_int),
             "w4_time_next_kernel": ([_P, _P], ctypes.c_int),
         }
@@ -152,6 +153,13 @@ def w4_probe_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
                                                 src.element_size(),
                                                 _dev(sink, "sink", torch.int32, (64,), dev),
                                                 _stream(stream)))
+
+
+def w4_probe_write(dst: torch.Tensor, value: int = 0, stream=None) -> None:
+    """Write every byte of `dst` once, each 32-bit word = `value` (a measurement helper)."""
+    _check("w4_probe_write", lib().w4_probe_write(_dev(dst, "dst", dst.dtype),
+                                                  dst.numel() * dst.element_size(),
+                                                  int(value) & 0xFFFFFFFF, _stream(stream)))
 
 
 def w4_probe_mfma(blocks: int, iters: int, times: torch.Tensor, sink: torch.Tensor,

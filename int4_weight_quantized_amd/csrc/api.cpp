@@ -245,6 +245,14 @@ int w4_probe_read(const void *src, int64_t bytes, uint32_t *sink, void *stream) 
                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
+int w4_probe_write(void *dst, int64_t bytes, uint32_t value, void *stream) {
+    if (!dst) return W4_ERR_NULL;
+    if (bytes < 16 || bytes % 16 != 0 || bytes > 0x7F000000) return W4_ERR_SHAPE;
+    if (!aligned(dst, 16)) return W4_ERR_ALIGN;
+    return launched("probe_write", w4::launch_probe_write(static_cast<uint8_t *>(dst), bytes, value,
+                                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
 int w4_quantize_weight(const float *W, int64_t K, int64_t N, int scheme, int64_t group_size,
                        uint8_t *packed, float *scales, float *zeros, void *stream) {
     if (!W || !packed || !scales) return W4_ERR_NULL;

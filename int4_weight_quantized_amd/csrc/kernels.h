@@ -128,9 +128,11 @@ hipError_t launch_w4a16_generic(const uint16_t *X, int64_t M, int64_t K, int64_t
                                 const uint8_t *packed, const float *scales, const float *zeros,
                                 int64_t group, float *Y, hipStream_t st);
 
-// Measurement helpers (probe.hip): an empty kernel and a plain streaming read.
+// Measurement helpers (probe.hip): an empty kernel, a plain streaming read and
+// write, and an MFMA clock probe.
 hipError_t launch_probe_empty(int64_t blocks, hipStream_t st);
 hipError_t launch_probe_read(const uint8_t *src, int64_t bytes, uint32_t *sink, hipStream_t st);
+hipError_t launch_probe_write(uint8_t *dst, int64_t bytes, uint32_t value, hipStream_t st);
 hipError_t launch_probe_mfma(int64_t blocks, int iters, uint64_t *times, uint32_t *sink,
                              hipStream_t st);
 

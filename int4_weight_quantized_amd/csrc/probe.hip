@@ -8,6 +8,10 @@
 //    buffer loads, 4 per thread, whole 64-byte pieces per quarter-wave), with
 //    one conditional store so the loads are kept; the best a kernel that only
 //    reads those bytes once can do.
+//  * k_probe_write: a plain streaming write of `bytes` (16-byte non-temporal
+//    buffer stores, 4 per thread, the same pattern as the read); the best a
+//    kernel that only writes those bytes once can do (the prefill GEMM's
+//    fp32 output, for one).
 //  * k_probe_mfma: back-to-back int8 MFMAs on constant operands, timed with
 //    the shader clock and the constant-rate clock: the clock the matrix units
 //    run at under load on this machine, and their rate on such operands.
@@ -34,6 +38,18 @@ __global__ __launch_bounds__(256) void k_probe_read(const uint8_t *__restrict__ 
 #pragma unroll
     for (int i = 0; i < kProbeUnroll; ++i) x ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
     if (x == 0x9E3779B9u) sink[blockIdx.x % 64] = x;  // data-dependent: keeps the loads
+}
+
+__global__ __launch_bounds__(256) void k_probe_write(uint8_t *__restrict__ dst, int64_t bytes,
+                                                    uint32_t value) {
+    const auto r = make_rsrc(dst, bytes);
+    const int64_t base = ((int64_t)blockIdx.x * kProbeUnroll * 256) * 16;
+    const v4i v = {(int)value, (int)value, (int)value, (int)value};
+#pragma unroll
+    for (int i = 0; i < kProbeUnroll; ++i) {
+        const int64_t off = base + ((int64_t)i * 256 + threadIdx.x) * 16;
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off < bytes ? (int)off : kOOB, 0, kNonTemporal);
+    }
 }
 
 // Matrix-unit clock and rate: 8 waves per workgroup (two per SIMD), each
@@ -81,6 +97,13 @@ hipError_t launch_probe_read(const uint8_t *src, int64_t bytes, uint32_t *sink, 
     const int64_t per_block = (int64_t)kProbeUnroll * 256 * 16;
     launch_main(k_probe_read, dim3((unsigned)((bytes + per_block - 1) / per_block)), dim3(256), 0,
                 st, src, bytes, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_write(uint8_t *dst, int64_t bytes, uint32_t value, hipStream_t st) {
+    const int64_t per_block = (int64_t)kProbeUnroll * 256 * 16;
+    launch_main(k_probe_write, dim3((unsigned)((bytes + per_block - 1) / per_block)), dim3(256), 0,
+                st, dst, bytes, value);
     return hipGetLastError();
 }
 

@@ -239,6 +239,18 @@ def test_w4a16_checks(w4):
     assert f(FAKE + 1, 1, 256, 8, FAKE, FAKE, FAKE, 128, FAKE, None) == W4_ERR_ALIGN
 
 
+def test_probe_checks(w4):
+    lib = w4.lib()
+    assert lib.w4_probe_read(None, 64, FAKE, None) == W4_ERR_NULL
+    assert lib.w4_probe_read(FAKE, 24, FAKE, None) == W4_ERR_SHAPE
+    assert lib.w4_probe_read(FAKE + 8, 64, FAKE, None) == W4_ERR_ALIGN
+    assert lib.w4_probe_write(None, 64, 0, None) == W4_ERR_NULL
+    assert lib.w4_probe_write(FAKE, 8, 0, None) == W4_ERR_SHAPE
+    assert lib.w4_probe_write(FAKE, 24, 0, None) == W4_ERR_SHAPE
+    assert lib.w4_probe_write(FAKE, 0x7F000010, 0, None) == W4_ERR_SHAPE
+    assert lib.w4_probe_write(FAKE + 8, 64, 0, None) == W4_ERR_ALIGN
+
+
 def test_binding_refuses_cpu_tensors(w4):
     import torch
     with pytest.raises(ValueError):

@@ -42,6 +42,12 @@ def test_plain_read_probes_read_the_layers_bytes():
         assert f'"{name}": {n}' in src, name
 
 
+def test_plain_write_probe_writes_the_prefill_output():
+    # the --only write67m probe stands for the prefill product's fp32 output
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    assert f'"write67m": {4 * 4096 * 4096}' in src
+
+
 def test_more_than_one_gpu_is_refused_before_any_gpu_work():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=60)

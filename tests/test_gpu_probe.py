@@ -35,6 +35,21 @@ def test_probes_run():
         W4.w4_probe_read(src[:15], sink)
 
 
+def test_write_probe_writes_exactly_its_bytes():
+    # 3 blocks of 16 KB plus 48 bytes: the last block's stores past the range
+    # are dropped by the descriptor, so the guard words after it stay zero
+    n = 3 * 16384 + 48
+    buf = torch.zeros(n + 4096, dtype=torch.uint8, device="cuda:0")
+    W4.w4_probe_write(buf[:n], 0x01020304)
+    torch.cuda.synchronize()
+    words = buf.view(torch.int32).cpu()
+    assert (words[: n // 4] == 0x01020304).all()
+    assert (words[n // 4:] == 0).all()
+    assert W4.w4_last_path() == "probe_write" and "k_probe_write" in W4.w4_last_kernel()
+    with pytest.raises(W4.W4Error):
+        W4.w4_probe_write(buf[:24])
+
+
 def test_mfma_probe_reports_a_clock():
     times = torch.zeros((8, 4), dtype=torch.int64, device="cuda:0")
     sink = torch.zeros(64, dtype=torch.int32, device="cuda:0")
