@@ -466,8 +466,8 @@ int orc_merge_delta(const uint8_t *packed, const float *scales, const float *zer
     return rc;
 }
 
-/* A second, GPU-shuffled layout of the W4A16 weights (the survey's
- * "prepacked" format; the pages define none, they only pack two codes per
+/* A second, GPU-shuffled layout of the W4A16 weights (a "prepacked"
+ * format of this library; the pages define none, they only pack two codes per
  * byte).  It is a pure rearrangement of the canonical packed bytes and group
  * tables, defined for group 128, K % 512 == 0; channels are padded to
  * N16 = 16 * ceil(N / 16) with zero bytes / zero table entries:
