@@ -375,28 +375,40 @@ def platform_probes(torch, hip, w4, head_grid):
     del dst
     torch.cuda.empty_cache()
     # the matrix units' clock under load (shader-clock / 100 MHz counters of
-    # each workgroup) and their int8 rate on constant operands
+    # each workgroup) and their int8 rate, on constant operands and on random
+    # bytes (the switching activity of a real product lowers the clock)
     import statistics
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     times = torch.zeros((cus, 4), dtype=torch.int64, device="cuda")
-    w4.w4_probe_mfma(cus, 100, times, sink)
-    torch.cuda.synchronize()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20251014)
+    rnd = torch.randint(-2 ** 31, 2 ** 31 - 1, (cus * 512 * 32,), dtype=torch.int32, device="cuda",
+                        generator=g)
     iters = 9000
-    a, b = hip.event(), hip.event()
-    st = torch.cuda.current_stream().cuda_stream
-    hip.record(a, st)
-    w4.w4_probe_mfma(cus, iters, times, sink)
-    hip.record(b, st)
-    sec = hip.elapsed_ms(a, b) / 1e3
-    t = times.cpu().numpy().astype("float64")
-    clocks = (t[:, 1] - t[:, 0]) / ((t[:, 3] - t[:, 2]) / 1e8)
-    out["mfma_probe"] = {"clock_GHz": round(statistics.median(clocks.tolist()) / 1e9, 4),
-                         "clock_GHz_min": round(float(clocks.min()) / 1e9, 4),
-                         "int8_TOPS_constant_operands": round(
-                             cus * 8 * 16 * iters * 32768 / sec / 1e12, 1),
-                         "ms": round(sec * 1e3, 3)}
-    hip.destroy(a)
-    hip.destroy(b)
+
+    def mfma_leg(ops):
+        w4.w4_probe_mfma(cus, 100, times, sink, ops)
+        torch.cuda.synchronize()
+        a, b = hip.event(), hip.event()
+        st = torch.cuda.current_stream().cuda_stream
+        hip.record(a, st)
+        w4.w4_probe_mfma(cus, iters, times, sink, ops)
+        hip.record(b, st)
+        sec = hip.elapsed_ms(a, b) / 1e3
+        hip.destroy(a)
+        hip.destroy(b)
+        t = times.cpu().numpy().astype("float64")
+        clocks = (t[:, 1] - t[:, 0]) / ((t[:, 3] - t[:, 2]) / 1e8)
+        return {"clock_GHz": round(statistics.median(clocks.tolist()) / 1e9, 4),
+                "clock_GHz_min": round(float(clocks.min()) / 1e9, 4),
+                "int8_TOPS": round(cus * 8 * 16 * iters * 32768 / sec / 1e12, 1),
+                "ms": round(sec * 1e3, 3)}
+
+    const = mfma_leg(None)
+    out["mfma_probe"] = {"clock_GHz": const["clock_GHz"], "clock_GHz_min": const["clock_GHz_min"],
+                         "int8_TOPS_constant_operands": const["int8_TOPS"], "ms": const["ms"],
+                         "random_operands": mfma_leg(rnd)}
+    del rnd
     p = torch.cuda.get_device_properties(0)
     out["device"] = {"name": p.name, "arch": p.gcnArchName, "cus": p.multi_processor_count,
                      "pci": f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}",

@@ -408,14 +408,19 @@ int w4_probe_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
 int w4_probe_write(void *dst, int64_t bytes, uint32_t value, void *stream);
 
 /* Back-to-back int8 MFMAs (v_mfma_i32_16x16x64_i8, 16 independent chains per
- * wave, 8 waves per workgroup, small constant operands) for `iters`
- * iterations in each of `blocks` workgroups (1 <= blocks <= 65536, iters >= 1).
- * Wave 0 of workgroup b writes times[4b .. 4b+3] = shader-clock counter at
- * start and end, constant 100 MHz counter at start and end, so the host can
- * read the clock the matrix units ran at; `sink` is a device array of 64
- * uint32 written only for one particular result.  Returns W4_OK, W4_ERR_NULL,
- * W4_ERR_SHAPE, W4_ERR_ALIGN or W4_ERR_HIP. */
-int w4_probe_mfma(int64_t blocks, int iters, uint64_t *times, uint32_t *sink, void *stream);
+ * wave, 8 waves per workgroup, each chain cycling over four activation and
+ * four weight operands) for `iters` iterations in each of `blocks` workgroups
+ * (1 <= blocks <= 65536; iters >= 4, a multiple of 4).  `ops` (nullable,
+ * 16-byte aligned) holds blocks * 512 * 32 int32: thread t of workgroup b
+ * takes its 4 + 4 operands from ops[32 (512 b + t) ...]; NULL selects small
+ * constant operands.  Wave 0 of workgroup b writes times[4b .. 4b+3] =
+ * shader-clock counter at start and end, constant 100 MHz counter at start
+ * and end, so the host can read the clock the matrix units ran at (it falls
+ * with the operands' switching activity); `sink` is a device array of 64
+ * uint32 written only for one particular result.  Returns W4_OK,
+ * W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN or W4_ERR_HIP. */
+int w4_probe_mfma(int64_t blocks, int iters, const int32_t *ops, uint64_t *times, uint32_t *sink,
+                  void *stream);
 
 #ifdef __cplusplus
 }

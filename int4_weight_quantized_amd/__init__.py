@@ -116,7 +116,7 @@ def lib():
             "w4_probe_empty": ([_I, _P], ctypes.c_int),
             "w4_probe_read": ([_P, _I, _P, _P], ctypes.c_int),
             "w4_probe_write": ([_P, _I, ctypes.c_uint32, _P], ctypes.c_int),
-            "w4_probe_mfma": ([_I, ctypes.c_int, _P, _P, _P], ctypes.c_int),
+            "w4_probe_mfma": ([_I, ctypes.c_int, _P, _P, _P, _P], ctypes.c_int),
             "w4_time_next_kernel": ([_P, _P], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
@@ -163,10 +163,13 @@ def w4_probe_write(dst: torch.Tensor, value: int = 0, stream=None) -> None:
 
 
 def w4_probe_mfma(blocks: int, iters: int, times: torch.Tensor, sink: torch.Tensor,
-                  stream=None) -> None:
-    """Int8 MFMA clock / rate probe (a measurement helper); times: int64 [blocks, 4]."""
+                  ops: torch.Tensor = None, stream=None) -> None:
+    """Int8 MFMA clock / rate probe (a measurement helper); times: int64
+    [blocks, 4]; ops: int32 [blocks * 512 * 32] operands, or None for constant ones."""
     dev = times.device
     _check("w4_probe_mfma", lib().w4_probe_mfma(int(blocks), int(iters),
+                                                _opt(ops, "ops", torch.int32,
+                                                     (int(blocks) * 512 * 32,), dev),
                                                 _dev(times, "times", torch.int64, (blocks, 4)),
                                                 _dev(sink, "sink", torch.int32, (64,), dev),
                                                 _stream(stream)))

@@ -228,11 +228,12 @@ int w4_probe_empty(int64_t blocks, void *stream) {
                     w4::launch_probe_empty(blocks, reinterpret_cast<hipStream_t>(stream)));
 }
 
-int w4_probe_mfma(int64_t blocks, int iters, uint64_t *times, uint32_t *sink, void *stream) {
+int w4_probe_mfma(int64_t blocks, int iters, const int32_t *ops, uint64_t *times, uint32_t *sink,
+                  void *stream) {
     if (!times || !sink) return W4_ERR_NULL;
-    if (blocks < 1 || blocks > 65536 || iters < 1) return W4_ERR_SHAPE;
-    if (!aligned(times, 8) || !aligned(sink, 4)) return W4_ERR_ALIGN;
-    return launched("probe_mfma", w4::launch_probe_mfma(blocks, iters, times, sink,
+    if (blocks < 1 || blocks > 65536 || iters < 4 || iters % 4 != 0) return W4_ERR_SHAPE;
+    if (!aligned(times, 8) || !aligned(sink, 4) || (ops && !aligned(ops, 16))) return W4_ERR_ALIGN;
+    return launched("probe_mfma", w4::launch_probe_mfma(blocks, iters, ops, times, sink,
                                                         reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -133,7 +133,7 @@ hipError_t launch_w4a16_generic(const uint16_t *X, int64_t M, int64_t K, int64_t
 hipError_t launch_probe_empty(int64_t blocks, hipStream_t st);
 hipError_t launch_probe_read(const uint8_t *src, int64_t bytes, uint32_t *sink, hipStream_t st);
 hipError_t launch_probe_write(uint8_t *dst, int64_t bytes, uint32_t value, hipStream_t st);
-hipError_t launch_probe_mfma(int64_t blocks, int iters, uint64_t *times, uint32_t *sink,
-                             hipStream_t st);
+hipError_t launch_probe_mfma(int64_t blocks, int iters, const int32_t *ops, uint64_t *times,
+                             uint32_t *sink, hipStream_t st);
 
 }  // namespace w4

@@ -12,9 +12,10 @@
 //    buffer stores, 4 per thread, the same pattern as the read); the best a
 //    kernel that only writes those bytes once can do (the prefill GEMM's
 //    fp32 output, for one).
-//  * k_probe_mfma: back-to-back int8 MFMAs on constant operands, timed with
-//    the shader clock and the constant-rate clock: the clock the matrix units
-//    run at under load on this machine, and their rate on such operands.
+//  * k_probe_mfma: back-to-back int8 MFMAs on constant or caller-given
+//    (e.g. random) operands, timed with the shader clock and the
+//    constant-rate clock: the clock the matrix units run at under that load
+//    on this machine, and their rate on such operands.
 #include "common.h"
 #include "kernels.h"
 
@@ -53,21 +54,41 @@ __global__ __launch_bounds__(256) void k_probe_write(uint8_t *__restrict__ dst, 
 }
 
 // Matrix-unit clock and rate: 8 waves per workgroup (two per SIMD), each
-// issuing 16 independent v_mfma_i32_16x16x64_i8 per iteration on small
-// constant operands; wave 0 of each workgroup records the shader-clock and
-// the constant 100 MHz counters at its start and end (times[4 b .. 4 b + 3]).
-__global__ __launch_bounds__(512) void k_probe_mfma(int iters, uint64_t *__restrict__ times,
+// issuing 16 independent v_mfma_i32_16x16x64_i8 per iteration, cycling over
+// four activation and four weight operands so consecutive MFMAs see
+// different data; wave 0 of each workgroup records the shader-clock and the
+// constant 100 MHz counters at its start and end (times[4 b .. 4 b + 3]).
+// OPS: each lane loads its 4 + 4 operands (32 int32) from `ops`, e.g. random
+// bytes, whose switching activity is that of a real product; else small
+// constant operands.
+template <bool OPS>
+__global__ __launch_bounds__(512) void k_probe_mfma(int iters, const int *__restrict__ ops,
+                                                    uint64_t *__restrict__ times,
                                                     uint32_t *__restrict__ sink) {
     const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
     const int lane = threadIdx.x % kWave;
-    const v4i a = {0x01010101 * (lane % 3), 0x02020202, 0x01010101, 0x03030303 * (lane % 2)};
-    const v4i b = {0x10101010, 0x20202020 * (lane % 2), 0x10101010, 0x30303030};
+    v4i a[4], b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (OPS) {
+            const int64_t base = ((int64_t)blockIdx.x * 512 + threadIdx.x) * 32 + 8 * j;
+            a[j] = v4i{ops[base], ops[base + 1], ops[base + 2], ops[base + 3]};
+            b[j] = v4i{ops[base + 4], ops[base + 5], ops[base + 6], ops[base + 7]};
+        } else {
+            a[j] = v4i{0x01010101 * (lane % 3), 0x02020202, 0x01010101, 0x03030303 * (lane % 2)};
+            b[j] = v4i{0x10101010, 0x20202020 * (lane % 2), 0x10101010, 0x30303030};
+        }
+    }
     v4i acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = v4i{0, 0, 0, 0};
-    for (int it = 0; it < iters; ++it) {
+    for (int it = 0; it < iters; it += 4) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[i], 0, 0, 0);
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i % 4], b[(i / 4 + u) % 4], acc[i],
+                                                               0, 0, 0);
     }
     int x = 0;
 #pragma unroll
@@ -82,9 +103,14 @@ __global__ __launch_bounds__(512) void k_probe_mfma(int iters, uint64_t *__restr
     if (x == 0x5A5A5A5A) sink[blockIdx.x % 64] = (uint32_t)x;  // keeps the products
 }
 
-hipError_t launch_probe_mfma(int64_t blocks, int iters, uint64_t *times, uint32_t *sink,
-                             hipStream_t st) {
-    launch_main(k_probe_mfma, dim3((unsigned)blocks), dim3(512), 0, st, iters, times, sink);
+hipError_t launch_probe_mfma(int64_t blocks, int iters, const int32_t *ops, uint64_t *times,
+                             uint32_t *sink, hipStream_t st) {
+    if (ops)
+        launch_main(k_probe_mfma<true>, dim3((unsigned)blocks), dim3(512), 0, st, iters,
+                    (const int *)ops, times, sink);
+    else
+        launch_main(k_probe_mfma<false>, dim3((unsigned)blocks), dim3(512), 0, st, iters,
+                    (const int *)nullptr, times, sink);
     return hipGetLastError();
 }
 

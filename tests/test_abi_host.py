@@ -249,6 +249,11 @@ def test_probe_checks(w4):
     assert lib.w4_probe_write(FAKE, 24, 0, None) == W4_ERR_SHAPE
     assert lib.w4_probe_write(FAKE, 0x7F000010, 0, None) == W4_ERR_SHAPE
     assert lib.w4_probe_write(FAKE + 8, 64, 0, None) == W4_ERR_ALIGN
+    assert lib.w4_probe_mfma(8, 100, None, None, FAKE, None) == W4_ERR_NULL
+    assert lib.w4_probe_mfma(0, 100, None, FAKE, FAKE, None) == W4_ERR_SHAPE
+    assert lib.w4_probe_mfma(8, 102, None, FAKE, FAKE, None) == W4_ERR_SHAPE
+    assert lib.w4_probe_mfma(8, 0, None, FAKE, FAKE, None) == W4_ERR_SHAPE
+    assert lib.w4_probe_mfma(8, 100, FAKE + 8, FAKE, FAKE, None) == W4_ERR_ALIGN
 
 
 def test_binding_refuses_cpu_tensors(w4):

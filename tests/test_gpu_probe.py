@@ -53,9 +53,17 @@ def test_write_probe_writes_exactly_its_bytes():
 def test_mfma_probe_reports_a_clock():
     times = torch.zeros((8, 4), dtype=torch.int64, device="cuda:0")
     sink = torch.zeros(64, dtype=torch.int32, device="cuda:0")
-    W4.w4_probe_mfma(8, 200, times, sink)
-    torch.cuda.synchronize()
-    t = times.cpu().numpy().astype("float64")
-    assert (t[:, 1] > t[:, 0]).all() and (t[:, 3] > t[:, 2]).all()
-    ghz = (t[:, 1] - t[:, 0]) / ((t[:, 3] - t[:, 2]) / 1e8) / 1e9
-    assert ((ghz > 0.3) & (ghz < 5.0)).all(), ghz
+    ops = torch.randint(-2 ** 31, 2 ** 31 - 1, (8 * 512 * 32,), dtype=torch.int32,
+                        device="cuda:0")
+    for o in (None, ops):
+        times.zero_()
+        W4.w4_probe_mfma(8, 200, times, sink, o)
+        torch.cuda.synchronize()
+        t = times.cpu().numpy().astype("float64")
+        assert (t[:, 1] > t[:, 0]).all() and (t[:, 3] > t[:, 2]).all()
+        ghz = (t[:, 1] - t[:, 0]) / ((t[:, 3] - t[:, 2]) / 1e8) / 1e9
+        assert ((ghz > 0.3) & (ghz < 5.0)).all(), ghz
+    with pytest.raises(W4.W4Error):
+        W4.w4_probe_mfma(8, 202, times, sink)  # iterations come in fours
+    with pytest.raises(ValueError):
+        W4.w4_probe_mfma(8, 200, times, sink, ops[:100])
