@@ -49,9 +49,16 @@ bool gemv_dot4_ok(int64_t M, int64_t K, bool w8) {
 // PP: the int4 codes come in the shuffled tile layout (ROWS == 16, K % 128 ==
 // 0): chunk c of block row r sits in tile c / 4 at slot (c % 4) ^ ((r / 2) % 4),
 // so the 4 rows of a wave still read 256 contiguous bytes per tile.
+// PRE (FUSED): the lane requests its first PRE weight chunks before the
+// activation quantization and the rest right after it (PRE == UB: all
+// before).  The quantization's barriers wait for every wave of the block,
+// and a wave whose weight requests back up in the CU's memory pipeline
+// reaches them late; with one block per CU and half of the chunks requested
+// up front the block's codes are ready while the first half streams in.
 template <int M, int ROWS, int UB, bool FUSED, Out OUT, bool W8, bool DIV = false,
-          bool PP = false>
+          bool PP = false, int PRE = UB>
 __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args args) {
+    static_assert(PRE >= 0 && PRE <= UB && (FUSED || PRE == UB), "chunks before the quantization");
     const W4A8Args a = args_now(args);
     constexpr int T = 16 * ROWS;  // threads
     constexpr int KPC = W8 ? 16 : 32;  // codes per 16-byte chunk
@@ -121,13 +128,14 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args args) {
                        : make_rsrc(a.packed + n0 * KB, (int64_t)rows * KB);
     const int rowoff = r * KB;
     uint4 wb[UB];
-#pragma unroll
-    for (int u = 0; u < UB; ++u) {
+    auto wload = [&](int u) {
         const int c = j + 16 * u;
         const int off = PP ? ((c / 4) * 16 + r) * 64 + 16 * ((c % 4) ^ ((r / 2) % 4))
                            : rowoff + 16 * c;
         wb[u] = bload16_nt(rw, c < C ? off : kOOB);
-    }
+    };
+#pragma unroll
+    for (int u = 0; u < PRE; ++u) wload(u);
 
     // Epilogue operands, so their latency hides behind the main work.
     const int64_t n = n0 + r;
@@ -233,6 +241,8 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args args) {
         }
     }
     lds_barrier();
+#pragma unroll
+    for (int u = PRE; u < UB; ++u) wload(u);
 
     // (4) int8 dot products of 16*code with the P8 activations (of the int8
     // codes with the natural-order activations for 8-bit weights).
@@ -295,6 +305,35 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args args) {
     }
 }
 
+static int device_cus();
+
+// Canonical int4 codes, fused quantization, M <= 2: one block per CU (the
+// fewest channels per block, a multiple of 16 up to 64, that needs no more
+// blocks than the device has CUs) with half of each lane's chunks requested
+// before the quantization (graph-free back-to-back launches, us: 7B-class
+// M = 1 6.10 -> 5.40 with 48 channels, Gemma-like 3.17 -> 3.00 with 32;
+// with 16 channels and half of the chunks early 7B-class 5.68, Gemma-like
+// with a third early 3.57).  Layers of up to 16 blocks per CU keep 16
+// channels and every chunk up front.
+template <int M, int UB, bool DIV>
+static bool go_dot4_wide(const W4A8Args &a, hipStream_t st) {
+    const int64_t cus = device_cus();
+    constexpr int PRE = (UB + 1) / 2;
+    const uint32_t shm = (uint32_t)(M * a.K);
+    auto go = [&](auto kernel, int rows) {
+        launch_main(kernel, dim3((unsigned)((a.N + rows - 1) / rows)), dim3(16 * rows), shm, st,
+                    a);
+    };
+    if (a.N <= 16 * cus) return false;
+    if (a.N <= 32 * cus)
+        go(k_gemv_dot4<M, 32, UB, true, Out::Y, false, DIV, false, PRE>, 32);
+    else if (a.N <= 48 * cus)
+        go(k_gemv_dot4<M, 48, UB, true, Out::Y, false, DIV, false, PRE>, 48);
+    else
+        go(k_gemv_dot4<M, 64, UB, true, Out::Y, false, DIV, false, PRE>, 64);
+    return true;
+}
+
 template <int M, int ROWS, int UB, bool W8>
 static void go_dot4(const W4A8Args &a, hipStream_t st) {
     dim3 grid((unsigned)((a.N + ROWS - 1) / ROWS));
@@ -304,6 +343,12 @@ static void go_dot4(const W4A8Args &a, hipStream_t st) {
             launch_main(k_gemv_dot4<M, ROWS, UB, true, Out::Y, false, false, true>, grid,
                         dim3(16 * ROWS), shm, st, a);
             return;
+        }
+        if constexpr (M <= 2) {
+            if (a.out == Out::Y && a.X) {
+                if (a.act_div ? go_dot4_wide<M, UB, true>(a, st) : go_dot4_wide<M, UB, false>(a, st))
+                    return;
+            }
         }
     }
     if (a.out == Out::I32)
