@@ -122,15 +122,19 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args args) {
     __builtin_amdgcn_sched_barrier(0);
 
     // (2) weights of this block's rows: all UB chunks of the lane.
-    static_assert(!PP || (ROWS == 16 && !W8), "shuffled int4 tiles of 16 channels");
-    const auto rw = PP ? make_rsrc(a.packed + (n0 / 16) * (int64_t)(K / 128) * 1024,
-                                   (int64_t)(K / 128) * 1024)
+    static_assert(!PP || (ROWS % 16 == 0 && !W8), "shuffled int4 tiles of 16 channels");
+    // (shuffled tiles: the block's ROWS / 16 channel blocks of K / 128 tiles
+    // each; channels past N are zero padding inside their block)
+    const int tiles = K / 128;
+    const auto rw = PP ? make_rsrc(a.packed + (n0 / 16) * (int64_t)tiles * 1024,
+                                   (int64_t)((rows + 15) / 16) * tiles * 1024)
                        : make_rsrc(a.packed + n0 * KB, (int64_t)rows * KB);
-    const int rowoff = r * KB;
+    const int rowoff = PP ? (r / 16) * tiles * 1024 : r * KB;
+    const int rr = r % 16;  // row inside the channel block (shuffled tiles)
     uint4 wb[UB];
     auto wload = [&](int u) {
         const int c = j + 16 * u;
-        const int off = PP ? ((c / 4) * 16 + r) * 64 + 16 * ((c % 4) ^ ((r / 2) % 4))
+        const int off = PP ? rowoff + ((c / 4) * 16 + rr) * 64 + 16 * ((c % 4) ^ ((rr / 2) % 4))
                            : rowoff + 16 * c;
         wb[u] = bload16_nt(rw, c < C ? off : kOOB);
     };
@@ -307,15 +311,15 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args args) {
 
 static int device_cus();
 
-// Canonical int4 codes, fused quantization, M <= 2: one block per CU (the
-// fewest channels per block, a multiple of 16 up to 64, that needs no more
-// blocks than the device has CUs) with half of each lane's chunks requested
-// before the quantization (graph-free back-to-back launches, us: 7B-class
-// M = 1 6.10 -> 5.40 with 48 channels, Gemma-like 3.17 -> 3.00 with 32;
-// with 16 channels and half of the chunks early 7B-class 5.68, Gemma-like
-// with a third early 3.57).  Layers of up to 16 blocks per CU keep 16
-// channels and every chunk up front.
-template <int M, int UB, bool DIV>
+// Int4 codes, fused quantization, M <= 2: one block per CU (the fewest channels per
+// block, a multiple of 16 up to 64, that needs no more blocks than the device
+// has CUs) with half of each lane's chunks requested before the quantization
+// (graph-free back-to-back launches, us: 7B-class M = 1 6.10 -> 5.40 with 48
+// channels, Gemma-like 3.17 -> 3.00 with 32; with 16 channels and half of
+// the chunks early 7B-class 5.68, Gemma-like with a third early 3.57).
+// Layers of up to 16 channels per CU keep 16 channels and every chunk up
+// front.
+template <int M, int UB, bool W8, bool DIV, bool PP>
 static bool go_dot4_wide(const W4A8Args &a, hipStream_t st) {
     const int64_t cus = device_cus();
     constexpr int PRE = (UB + 1) / 2;
@@ -326,11 +330,11 @@ static bool go_dot4_wide(const W4A8Args &a, hipStream_t st) {
     };
     if (a.N <= 16 * cus) return false;
     if (a.N <= 32 * cus)
-        go(k_gemv_dot4<M, 32, UB, true, Out::Y, false, DIV, false, PRE>, 32);
+        go(k_gemv_dot4<M, 32, UB, true, Out::Y, W8, DIV, PP, PRE>, 32);
     else if (a.N <= 48 * cus)
-        go(k_gemv_dot4<M, 48, UB, true, Out::Y, false, DIV, false, PRE>, 48);
+        go(k_gemv_dot4<M, 48, UB, true, Out::Y, W8, DIV, PP, PRE>, 48);
     else
-        go(k_gemv_dot4<M, 64, UB, true, Out::Y, false, DIV, false, PRE>, 64);
+        go(k_gemv_dot4<M, 64, UB, true, Out::Y, W8, DIV, PP, PRE>, 64);
     return true;
 }
 
@@ -338,17 +342,26 @@ template <int M, int ROWS, int UB, bool W8>
 static void go_dot4(const W4A8Args &a, hipStream_t st) {
     dim3 grid((unsigned)((a.N + ROWS - 1) / ROWS));
     const uint32_t shm = (uint32_t)(M * a.K);
+    // (int4 codes only: with int8 codes it measured slower at 7B-class size,
+    // 9.14 -> 9.67 us, and within noise at Gemma-like size; on shuffled tiles
+    // faster at 7B-class size, 5.84 -> 5.44 us, slower with three chunks per
+    // lane, Gemma-like 2.82 -> 3.06 us)
+    if constexpr (M <= 2 && !W8) {
+        if (a.pp) {
+            if constexpr (UB >= 8) {
+                if (go_dot4_wide<M, UB, false, false, true>(a, st)) return;
+            }
+        } else if (a.out == Out::Y && a.X) {
+            if (a.act_div ? go_dot4_wide<M, UB, false, true, false>(a, st)
+                          : go_dot4_wide<M, UB, false, false, false>(a, st))
+                return;
+        }
+    }
     if constexpr (!W8) {
         if (a.pp) {  // shuffled layout: fused forward only
             launch_main(k_gemv_dot4<M, ROWS, UB, true, Out::Y, false, false, true>, grid,
                         dim3(16 * ROWS), shm, st, a);
             return;
-        }
-        if constexpr (M <= 2) {
-            if (a.out == Out::Y && a.X) {
-                if (a.act_div ? go_dot4_wide<M, UB, true>(a, st) : go_dot4_wide<M, UB, false>(a, st))
-                    return;
-            }
         }
     }
     if (a.out == Out::I32)

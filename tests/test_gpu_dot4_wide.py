@@ -1,5 +1,6 @@
-"""The decode GEMV's one-block-per-CU launch shape (canonical int4 codes,
-fused activation quantization, M <= 2): layers with more than 16 output
+"""The decode GEMV's one-block-per-CU launch shape (int4 codes, fused
+activation quantization, M <= 2; on shuffled tiles from 8 chunks per lane):
+layers with more than 16 output
 channels per CU run 32, 48 or 64 channels per block, each lane requesting
 half of its weight chunks before the activation quantization and the rest
 after it.  Bit-exact against the CPU oracle over every chunk count (K from 96
@@ -87,4 +88,32 @@ def test_wide_dot4_awq(M, K, N):
     y = W4.w4a8_linear_awq(dev(d["x"]), gp, gsw, gs, bias=dev(d["bias"]))
     assert W4.w4_last_path() == "gemv_dot4"
     assert f"ILi{M}ELi{expected_rows(N)}E" in W4.w4_last_kernel()
+    assert bits_equal(host(y), yref)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 1152, 6912), (2, 4096, 11008), (1, 2048, 16500),
+                                   (1, 8192, 4100), (2, 3072, 9000)])
+def test_wide_dot4_prepacked(M, K, N):
+    d = workloads.random_case(M * 13 + K + N, M, K, N, outliers=min(6, K), bias=True)
+    pref, sref = oracle.quantize_weight_sym(d["W"])
+    yref = oracle.w4a8_linear(d["x"], pref, sref, d["bias"])
+    packed, sw, _ = W4.w4_quantize_weight(dev(d["W"]), "sym")
+    wpp = W4.w4_prepack_weights(packed)
+    y = W4.w4a8_linear_prepacked(dev(d["x"]), wpp, sw, bias=dev(d["bias"]))
+    assert W4.w4_last_path() == "gemv_dot4_prepacked"
+    chunks = (K // 32 + 15) // 16  # chunks per lane before rounding up to an instantiated count
+    rows = expected_rows(N) if chunks > 4 else 16
+    assert f"ILi{M}ELi{rows}E" in W4.w4_last_kernel()
+    assert bits_equal(host(y), yref)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 1152, 6912), (2, 4096, 11008), (2, 96, 4100)])
+def test_dot4_w8_keeps_16_channels(M, K, N):
+    d = workloads.random_case(M * 17 + K + N, M, K, N, outliers=min(6, K), bias=True)
+    qref, sref = oracle.quantize_weight_w8(d["W"])
+    yref = oracle.w8a8_linear(d["x"], qref, sref, d["bias"])
+    Wq, sw = W4.w8_quantize_weight(dev(d["W"]))
+    y = W4.w8a8_linear(dev(d["x"]), Wq, sw, bias=dev(d["bias"]))
+    assert W4.w4_last_path() == "w8_gemv_dot4"
+    assert f"ILi{M}ELi16E" in W4.w4_last_kernel()  # int8 codes keep 16 channels per block
     assert bits_equal(host(y), yref)
