@@ -2,7 +2,7 @@
 activation quantization, M <= 2; on shuffled tiles from 8 chunks per lane):
 layers with more than 16 output
 channels per CU run 32, 48 or 64 channels per block, each lane requesting
-half of its weight chunks before the activation quantization and the rest
+part of its weight chunks before the activation quantization and the rest
 after it.  Bit-exact against the CPU oracle over every chunk count (K from 96
 to 8192), every block width, ragged last blocks, bias, ReLU and the AWQ
 division; the kernel that ran is checked for the expected block width."""
@@ -115,5 +115,5 @@ def test_dot4_w8_keeps_16_channels(M, K, N):
     Wq, sw = W4.w8_quantize_weight(dev(d["W"]))
     y = W4.w8a8_linear(dev(d["x"]), Wq, sw, bias=dev(d["bias"]))
     assert W4.w4_last_path() == "w8_gemv_dot4"
-    assert f"ILi{M}ELi16E" in W4.w4_last_kernel()  # int8 codes keep 16 channels per block
+    assert f"ILi{M}ELi16E" in W4.w4_last_kernel()
     assert bits_equal(host(y), yref)
