@@ -815,10 +815,15 @@ def main():
             del c
             torch.cuda.empty_cache()
         pre = [p for p in parts if p["workload"] == "prefill_4096"][0]
+        pps = [p for p in parts if p["workload"] == "pp_prefill_4096"]
         out["prefill_int8"] = {"metric": "int8 TOPS (M=4096 prefill GEMM)",
                                "TOPS_kernel": pre["TOPS_kernel"], "TOPS_step": pre["TOPS_step"],
                                "peak": INT8_PEAK_TOPS,
                                "frac_kernel": pre["frac_int8_mfma_kernel"]}
+        if pps:  # the same product on the shuffled weight tiles
+            out["prefill_int8"]["shuffled_tiles"] = {
+                "TOPS_kernel": pps[0]["TOPS_kernel"], "TOPS_step": pps[0]["TOPS_step"],
+                "frac_kernel": pps[0]["frac_int8_mfma_kernel"]}
     out["parts"] = parts
     out["headline_weight_quantize_ms"] = round(head.quant_s * 1e3, 3)
     if not args.no_cpu:
