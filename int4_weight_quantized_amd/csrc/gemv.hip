@@ -28,13 +28,13 @@ namespace w4 {
 // ------------------------------------------------------------------ dot4
 // Block = ROWS output channels x 16 lanes.  Lane j of a channel streams the
 // 16-byte chunks j, j+16, ..., j+16*(UB-1) of that channel's packed row (one
-// chunk = 32 codes), so a wave reads 4 rows x 256 contiguous bytes per load
-// and every weight byte of the block is requested before any arithmetic.
+// chunk = 32 codes), so a wave reads 4 rows x 256 contiguous bytes per load.
 // Order of work: (1) issue the activation loads, (2) once every wave of the
-// block has, issue the weight chunks, (3) quantize the activations into LDS
-// (P8 layout) while the weights are in flight (the barriers wait for LDS only,
-// so the weight loads stay in flight), (4) dot products, chunk by chunk as
-// the loads land, (5) 16-lane DPP sum and epilogue.
+// block has, issue the weight chunks (all of them, or the first PRE), (3)
+// quantize the activations into LDS (P8 layout) while the weights are in
+// flight (the barriers wait for LDS only, so the weight loads stay in
+// flight), then issue the remaining chunks, (4) dot products, chunk by chunk
+// as the loads land, (5) 16-lane DPP sum and epilogue.
 // With W8 a 16-byte chunk holds 16 int8 codes (instead of 32 int4 codes) and
 // the activations stay in natural order.
 constexpr int kDot4MaxK = 8192, kDot4MaxKW8 = 4096;
@@ -46,9 +46,10 @@ bool gemv_dot4_ok(int64_t M, int64_t K, bool w8) {
 // DIV (with FUSED): the activations are divided by per-column divisors
 // (a.act_div) before their quantization -- the activation side of AWQ-style
 // channel scaling.
-// PP: the int4 codes come in the shuffled tile layout (ROWS == 16, K % 128 ==
-// 0): chunk c of block row r sits in tile c / 4 at slot (c % 4) ^ ((r / 2) % 4),
-// so the 4 rows of a wave still read 256 contiguous bytes per tile.
+// PP: the int4 codes come in the shuffled tile layout (ROWS % 16 == 0, K % 128
+// == 0): chunk c of row r of a 16-channel block sits in tile c / 4 at slot
+// (c % 4) ^ ((r / 2) % 4), so the 4 rows of a wave still read 256 contiguous
+// bytes per tile.
 // PRE (FUSED): the lane requests its first PRE weight chunks before the
 // activation quantization and the rest right after it (PRE == UB: all
 // before).  The quantization's barriers wait for every wave of the block,
@@ -121,7 +122,8 @@ __global__ __launch_bounds__(16 * ROWS) void k_gemv_dot4(W4A8Args args) {
     issue_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
-    // (2) weights of this block's rows: all UB chunks of the lane.
+    // (2) weights of this block's rows: the lane's first PRE chunks here, the
+    // rest right after the quantization.
     static_assert(!PP || (ROWS % 16 == 0 && !W8), "shuffled int4 tiles of 16 channels");
     // (shuffled tiles: the block's ROWS / 16 channel blocks of K / 128 tiles
     // each; channels past N are zero padding inside their block)
