@@ -109,3 +109,21 @@ def test_demangle():
     name = "_ZN2w411k_gemv_dot4ILi1ELi16ELi3ELb1ELNS_3OutE0ELb0ELb0ELb0EEEvNS_8W4A8ArgsE"
     out = bench.demangle(name)
     assert out == name or out.startswith("void w4::k_gemv_dot4<1, 16, 3, true")
+
+
+@pytest.mark.parametrize("est_s, true_s", [(3.7e-6, 2.8e-6), (2.8e-6, 2.8e-6), (1e-5, 2e-7),
+                                           (1e-7, 5e-6)])
+def test_timed_region_spans_two_ms(monkeypatch, est_s, true_s):
+    # the graph is sized from an estimate; when replays run faster than it,
+    # the region is captured again, sized by the measured rate
+    sizes = []
+
+    def replay(torch, hip, step, L):
+        sizes.append(L)
+        return true_s
+
+    monkeypatch.setattr(bench, "region_replay", replay)
+    sec, L = bench.region_time(None, None, None, est_s, 20)
+    assert sec == true_s and L == sizes[-1] and L >= 20
+    assert L * sec >= 2e-3
+    assert len(sizes) == (1 if sizes[0] * true_s >= 2e-3 else 2)
