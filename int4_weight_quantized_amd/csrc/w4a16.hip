@@ -10,12 +10,24 @@
 // channel (codes k = 128*s + 32*(l/16) + [0, 32)) and the matching 32 bf16
 // activations of row l%16; the 32 codes feed four MFMAs of 8 codes each.
 //
-// Dequantization in 25 VALU operations per 8 codes: for an integer zero
-// point z in [-112, 128] the byte 128 + q - z never leaves [0, 255], so one integer add
-// per 4 codes forms it in place, v_cvt_f32_ubyte turns it into a float v, and
-//   fma(v, s, -128*s) = fl((v - 128) * s) = fl((q - z) * s)
-// exactly (one rounding of the exact product; 128*s is exact).  Other groups
-// take the direct fl(fl(q - z) * s).
+// Two exact fast forms for groups whose zero point z is an integer in
+// [-112, 128] (both give fl(fl(q - z) * s), bit for bit; other groups take
+// that direct form):
+//  * byte form (register-ring kernel), 25 VALU operations per 8 codes: the
+//    byte 128 + q - z never leaves [0, 255], so one integer add per 4 codes
+//    forms it in place, v_cvt_f32_ubyte turns it into a float v, and
+//      fma(v, s, -128*s) = fl((v - 128) * s) = fl((q - z) * s)
+//    exactly (one rounding of the exact product; 128*s is exact);
+//  * fp16 form (LDS-staged kernel), 21 VALU operations per 8 codes: one
+//    and-or per pair of codes places two nibbles in the mantissas of two
+//    fp16 1024s (1024 + q, or 1024 + 16 q for a nibble at bits 4-7), one
+//    packed fp16 add (or fma with 1/16) per pair subtracts 1024 + z, exact
+//    since every value involved is an integer below 2048 in magnitude, and
+//    one mixed-precision fma per code takes the fp16 q - z times the fp32
+//    scale plus -0, i.e. the single rounding fl((q - z) * s).  With
+//    |s| >= 2^-100 no product is subnormal.  Measured on the 70B-class layer
+//    (shuffled tiles): its k-loop takes 4 % fewer shader cycles than with
+//    the byte form.
 #include "common.h"
 #include "kernels.h"
 
@@ -63,11 +75,37 @@ __device__ __forceinline__ v4i dequant8_direct(uint32_t w, float s, float zp) {
                (int)pk_bf16(fl[3], fh[3])};
 }
 
-// A group may take the fast form when its zero point is an integer in
-// [-112, 128] (the byte 128 + q - z then stays in [0, 255]; a fractional zero
-// point must not be truncated there) and 128 * s is finite and exact.
+// A group may take a fast form when its zero point is an integer in
+// [-112, 128] (the byte 128 + q - z then stays in [0, 255], and 1024 + z and
+// 64 + z are exact fp16 integers; a fractional zero point must not be
+// truncated there) and 2^-100 <= |s| < 2^100 (128 * s finite and exact, no
+// subnormal product).
 __device__ __forceinline__ bool fast_group_ok(float s, float zp) {
-    return zp >= -112.0f && zp <= 128.0f && zp == rintf(zp) && fabsf(s) < 0x1p100f;
+    return zp >= -112.0f && zp <= 128.0f && zp == rintf(zp) && fabsf(s) < 0x1p100f &&
+           fabsf(s) >= 0x1p-100f;
+}
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// fp16 form (see above): c0 = (-1024 - z) and c1 = (-64 - z) in both halves,
+// nz = -0 (kept opaque so that the fma is not turned into a multiply), mg =
+// 0x64006400 (two fp16 1024s, in a register so that each pair takes one
+// v_and_or_b32).
+__device__ __forceinline__ v4i dequant8_f16(uint32_t w, float s, float nz, half2v c0, half2v c1,
+                                            uint32_t mg) {
+    const uint32_t w8 = w >> 8;
+    const half2v t0 = __builtin_bit_cast(half2v, (w & 0x000F000Fu) | mg);   // 1024 + q, k = 0, 4
+    const half2v t1 = __builtin_bit_cast(half2v, (w & 0x00F000F0u) | mg);   // 1024 + 16 q, k = 1, 5
+    const half2v t2 = __builtin_bit_cast(half2v, (w8 & 0x000F000Fu) | mg);  // k = 2, 6
+    const half2v t3 = __builtin_bit_cast(half2v, (w8 & 0x00F000F0u) | mg);  // k = 3, 7
+    const half2v k16 = half2v{(_Float16)0.0625f, (_Float16)0.0625f};
+    const half2v d0 = t0 + c0, d2 = t2 + c0;  // q - z, exact
+    const half2v d1 = __builtin_elementwise_fma(t1, k16, c1), d3 = __builtin_elementwise_fma(t3, k16, c1);
+    const float f0 = fmaf((float)d0.x, s, nz), f4 = fmaf((float)d0.y, s, nz);
+    const float f1 = fmaf((float)d1.x, s, nz), f5 = fmaf((float)d1.y, s, nz);
+    const float f2 = fmaf((float)d2.x, s, nz), f6 = fmaf((float)d2.y, s, nz);
+    const float f3 = fmaf((float)d3.x, s, nz), f7 = fmaf((float)d3.y, s, nz);
+    return v4i{(int)pk_bf16(f0, f1), (int)pk_bf16(f2, f3), (int)pk_bf16(f4, f5), (int)pk_bf16(f6, f7)};
 }
 
 __device__ __forceinline__ v4f mfma_bf16(uint4 a, v4i b, v4f c) {
@@ -442,12 +480,15 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
                 xr[q] = *reinterpret_cast<const uint4 *>(sb + xoff + 4096 * j + (swz ^ (16 * q)));
             v4i b0, b1, b2, b3;
             if (fast) {
-                const uint32_t cadd = (uint32_t)(128 - (int)zps[j]) * 0x01010101u;
-                const float nbias = -128.0f * scs[j];
-                b0 = dequant8_fast(w.x, scs[j], cadd, nbias);
-                b1 = dequant8_fast(w.y, scs[j], cadd, nbias);
-                b2 = dequant8_fast(w.z, scs[j], cadd, nbias);
-                b3 = dequant8_fast(w.w, scs[j], cadd, nbias);
+                uint32_t mg = 0x64006400u;
+                asm volatile("" : "+v"(mg));  // a register operand, not a literal
+                const float nz = -0.0f * fabsf(scs[j]);
+                const _Float16 e0 = (_Float16)(-1024.0f - zps[j]), e1 = (_Float16)(-64.0f - zps[j]);
+                const half2v c0 = half2v{e0, e0}, c1 = half2v{e1, e1};
+                b0 = dequant8_f16(w.x, scs[j], nz, c0, c1, mg);
+                b1 = dequant8_f16(w.y, scs[j], nz, c0, c1, mg);
+                b2 = dequant8_f16(w.z, scs[j], nz, c0, c1, mg);
+                b3 = dequant8_f16(w.w, scs[j], nz, c0, c1, mg);
             } else {
                 b0 = dequant8_direct(w.x, scs[j], zps[j]);
                 b1 = dequant8_direct(w.y, scs[j], zps[j]);
