@@ -10,24 +10,19 @@
 // channel (codes k = 128*s + 32*(l/16) + [0, 32)) and the matching 32 bf16
 // activations of row l%16; the 32 codes feed four MFMAs of 8 codes each.
 //
-// Two exact fast forms for groups whose zero point z is an integer in
-// [-112, 128] (both give fl(fl(q - z) * s), bit for bit; other groups take
-// that direct form):
-//  * byte form (register-ring kernel), 25 VALU operations per 8 codes: the
-//    byte 128 + q - z never leaves [0, 255], so one integer add per 4 codes
-//    forms it in place, v_cvt_f32_ubyte turns it into a float v, and
-//      fma(v, s, -128*s) = fl((v - 128) * s) = fl((q - z) * s)
-//    exactly (one rounding of the exact product; 128*s is exact);
-//  * fp16 form (LDS-staged kernel), 21 VALU operations per 8 codes: one
-//    and-or per pair of codes places two nibbles in the mantissas of two
-//    fp16 1024s (1024 + q, or 1024 + 16 q for a nibble at bits 4-7), one
-//    packed fp16 add (or fma with 1/16) per pair subtracts 1024 + z, exact
-//    since every value involved is an integer below 2048 in magnitude, and
-//    one mixed-precision fma per code takes the fp16 q - z times the fp32
-//    scale plus -0, i.e. the single rounding fl((q - z) * s).  With
-//    |s| >= 2^-100 no product is subnormal.  Measured on the 70B-class layer
-//    (shuffled tiles): its k-loop takes 4 % fewer shader cycles than with
-//    the byte form.
+// Fast form for groups whose zero point z is an integer in [-112, 128] and
+// whose scale has 2^-100 <= |s| < 2^100 (it gives fl(fl(q - z) * s), bit for
+// bit; other groups take that direct form), 21 VALU operations per 8 codes:
+// one and-or per pair of codes places two nibbles in the mantissas of two
+// fp16 1024s (1024 + q, or 1024 + 16 q for a nibble at bits 4-7), one packed
+// fp16 add (or fma with 1/16) per pair subtracts 1024 + z (or 64 + z),
+// exact since every value involved is an integer below 2048 in magnitude,
+// and one mixed-precision fma per code takes the fp16 q - z times the fp32
+// scale plus -0, i.e. the single rounding fl((q - z) * s); no product is
+// subnormal.  Measured on the 70B-class layer (shuffled tiles, LDS-staged
+// kernel, alternated runs on two boxes): its k-loop takes 2-4 % fewer shader
+// cycles than an earlier byte form (v_cvt_f32_ubyte of 128 + q - z, then
+// fma with s and -128 s; 25 operations per 8 codes).
 #include "common.h"
 #include "kernels.h"
 
@@ -45,21 +40,6 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
 }
 
 // 8 codes of one packed dword -> 4 dwords of bf16 pairs in natural k order.
-// Fast form (zero point in [-112, 128], see above): bytes 128 + q - z, one
-// fma per code.
-__device__ __forceinline__ v4i dequant8_fast(uint32_t w, float s, uint32_t cadd, float nbias) {
-    const uint32_t lb = (w & 0x0F0F0F0Fu) + cadd;          // k = 0, 2, 4, 6
-    const uint32_t hb = ((w >> 4) & 0x0F0F0F0Fu) + cadd;   // k = 1, 3, 5, 7
-    float fl[4], fh[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        fl[i] = fmaf((float)((lb >> (8 * i)) & 0xFFu), s, nbias);
-        fh[i] = fmaf((float)((hb >> (8 * i)) & 0xFFu), s, nbias);
-    }
-    return v4i{(int)pk_bf16(fl[0], fh[0]), (int)pk_bf16(fl[1], fh[1]), (int)pk_bf16(fl[2], fh[2]),
-               (int)pk_bf16(fl[3], fh[3])};
-}
-
 // Direct form for any zero point: fl(fl(q - z) * s).
 __device__ __forceinline__ v4i dequant8_direct(uint32_t w, float s, float zp) {
     const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
@@ -75,11 +55,10 @@ __device__ __forceinline__ v4i dequant8_direct(uint32_t w, float s, float zp) {
                (int)pk_bf16(fl[3], fh[3])};
 }
 
-// A group may take a fast form when its zero point is an integer in
-// [-112, 128] (the byte 128 + q - z then stays in [0, 255], and 1024 + z and
-// 64 + z are exact fp16 integers; a fractional zero point must not be
-// truncated there) and 2^-100 <= |s| < 2^100 (128 * s finite and exact, no
-// subnormal product).
+// A group may take the fast form when its zero point is an integer in
+// [-112, 128] (1024 + z and 64 + z are then exact fp16 integers and q - z
+// stays within [-128, 127]; a fractional zero point must not be rounded
+// there) and 2^-100 <= |s| < 2^100 (no product is subnormal or overflows).
 __device__ __forceinline__ bool fast_group_ok(float s, float zp) {
     return zp >= -112.0f && zp <= 128.0f && zp == rintf(zp) && fabsf(s) < 0x1p100f &&
            fabsf(s) >= 0x1p-100f;
@@ -87,7 +66,7 @@ __device__ __forceinline__ bool fast_group_ok(float s, float zp) {
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
-// fp16 form (see above): c0 = (-1024 - z) and c1 = (-64 - z) in both halves,
+// Fast form (see above): c0 = (-1024 - z) and c1 = (-64 - z) in both halves,
 // nz = -0 (kept opaque so that the fma is not turned into a multiply), mg =
 // 0x64006400 (two fp16 1024s, in a register so that each pair takes one
 // v_and_or_b32).
@@ -174,15 +153,18 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_mfma(const uint16_t *__restric
         for (int nb = 0; nb < NB; ++nb)
             ok = ok && fast_group_ok(sc[nb], zp[nb]);
         if (__all(ok)) {
+            uint32_t mg = 0x64006400u;
+            asm volatile("" : "+v"(mg));  // a register operand, not a literal
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const uint32_t cadd = (uint32_t)(128 - (int)zp[nb]) * 0x01010101u;
-                const float nbias = -128.0f * sc[nb];
+                const float nz = -0.0f * fabsf(sc[nb]);
+                const _Float16 e0 = (_Float16)(-1024.0f - zp[nb]), e1 = (_Float16)(-64.0f - zp[nb]);
+                const half2v c0 = half2v{e0, e0}, c1 = half2v{e1, e1};
                 const uint4 w = wr[d][nb];
-                const v4i b0 = dequant8_fast(w.x, sc[nb], cadd, nbias);
-                const v4i b1 = dequant8_fast(w.y, sc[nb], cadd, nbias);
-                const v4i b2 = dequant8_fast(w.z, sc[nb], cadd, nbias);
-                const v4i b3 = dequant8_fast(w.w, sc[nb], cadd, nbias);
+                const v4i b0 = dequant8_f16(w.x, sc[nb], nz, c0, c1, mg);
+                const v4i b1 = dequant8_f16(w.y, sc[nb], nz, c0, c1, mg);
+                const v4i b2 = dequant8_f16(w.z, sc[nb], nz, c0, c1, mg);
+                const v4i b3 = dequant8_f16(w.w, sc[nb], nz, c0, c1, mg);
                 acc[nb] = mfma_bf16(xr[d][0], b0, acc[nb]);
                 acc[nb] = mfma_bf16(xr[d][1], b1, acc[nb]);
                 acc[nb] = mfma_bf16(xr[d][2], b2, acc[nb]);
