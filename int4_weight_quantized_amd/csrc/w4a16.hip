@@ -69,7 +69,7 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 // Fast form (see above): c0 = (-1024 - z) and c1 = (-64 - z) in both halves,
 // nz = -0 (kept opaque so that the fma is not turned into a multiply), mg =
 // 0x64006400 (two fp16 1024s, in a register so that each pair takes one
-// v_and_or_b32).
+// v_and_or_b32); the kernels set nz and mg once.
 __device__ __forceinline__ v4i dequant8_f16(uint32_t w, float s, float nz, half2v c0, half2v c1,
                                             uint32_t mg) {
     const uint32_t w8 = w >> 8;
@@ -86,6 +86,14 @@ __device__ __forceinline__ v4i dequant8_f16(uint32_t w, float s, float nz, half2
     const float f3 = fmaf((float)d3.x, s, nz), f7 = fmaf((float)d3.y, s, nz);
     return v4i{(int)pk_bf16(f0, f1), (int)pk_bf16(f2, f3), (int)pk_bf16(f4, f5), (int)pk_bf16(f6, f7)};
 }
+
+// c0 of the fast form, -1024 - z in both halves (exact: an integer below
+// 2048 in magnitude); c1 = c0 + 960 = -64 - z, also exact
+__device__ __forceinline__ half2v zero_point_pair(float zp) {
+    const _Float16 e = (_Float16)(-1024.0f - zp);
+    return half2v{e, e};
+}
+constexpr half2v k960 = half2v{(_Float16)960.0f, (_Float16)960.0f};
 
 __device__ __forceinline__ v4f mfma_bf16(uint4 a, v4i b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
@@ -129,6 +137,12 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_mfma(const uint16_t *__restric
     const int xoff = r16 * K * 2 + kq * 64;
 
     v4f acc[NB];
+    // the fast form's constants, set once: two fp16 1024s (a register
+    // operand of v_and_or_b32, not a literal) and the addend -0 (opaque, so
+    // that the fma is not turned into a multiply)
+    uint32_t mg = 0x64006400u;
+    float nz = -0.0f;
+    asm volatile("" : "+v"(mg), "+v"(nz));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[nb] = v4f{0.f, 0.f, 0.f, 0.f};
 
@@ -153,13 +167,9 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_mfma(const uint16_t *__restric
         for (int nb = 0; nb < NB; ++nb)
             ok = ok && fast_group_ok(sc[nb], zp[nb]);
         if (__all(ok)) {
-            uint32_t mg = 0x64006400u;
-            asm volatile("" : "+v"(mg));  // a register operand, not a literal
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const float nz = -0.0f * fabsf(sc[nb]);
-                const _Float16 e0 = (_Float16)(-1024.0f - zp[nb]), e1 = (_Float16)(-64.0f - zp[nb]);
-                const half2v c0 = half2v{e0, e0}, c1 = half2v{e1, e1};
+                const half2v c0 = zero_point_pair(zp[nb]), c1 = c0 + k960;
                 const uint4 w = wr[d][nb];
                 const v4i b0 = dequant8_f16(w.x, sc[nb], nz, c0, c1, mg);
                 const v4i b1 = dequant8_f16(w.y, sc[nb], nz, c0, c1, mg);
@@ -417,6 +427,10 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
     };
 
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    // the fast form's constants, set once (as in the register-ring kernel)
+    uint32_t mg = 0x64006400u;
+    float nz = -0.0f;
+    asm volatile("" : "+v"(mg), "+v"(nz));
     const int ch = 16 * wl + r16;                         // this lane's channel
     const int swz = (kq ^ ((r16 / 2) % 4)) * 16;          // (row/2)%4 = (r16/2)%4
     const int woff = ch * 64 + swz;
@@ -462,11 +476,7 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
                 xr[q] = *reinterpret_cast<const uint4 *>(sb + xoff + 4096 * j + (swz ^ (16 * q)));
             v4i b0, b1, b2, b3;
             if (fast) {
-                uint32_t mg = 0x64006400u;
-                asm volatile("" : "+v"(mg));  // a register operand, not a literal
-                const float nz = -0.0f * fabsf(scs[j]);
-                const _Float16 e0 = (_Float16)(-1024.0f - zps[j]), e1 = (_Float16)(-64.0f - zps[j]);
-                const half2v c0 = half2v{e0, e0}, c1 = half2v{e1, e1};
+                const half2v c0 = zero_point_pair(zps[j]), c1 = c0 + k960;
                 b0 = dequant8_f16(w.x, scs[j], nz, c0, c1, mg);
                 b1 = dequant8_f16(w.y, scs[j], nz, c0, c1, mg);
                 b2 = dequant8_f16(w.z, scs[j], nz, c0, c1, mg);
