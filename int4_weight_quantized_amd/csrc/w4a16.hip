@@ -60,8 +60,10 @@ __device__ __forceinline__ v4i dequant8_direct(uint32_t w, float s, float zp) {
 // stays within [-128, 127]; a fractional zero point must not be rounded
 // there) and 2^-100 <= |s| < 2^100 (no product is subnormal or overflows).
 __device__ __forceinline__ bool fast_group_ok(float s, float zp) {
-    return zp >= -112.0f && zp <= 128.0f && zp == rintf(zp) && fabsf(s) < 0x1p100f &&
-           fabsf(s) >= 0x1p-100f;
+    // bitwise &: straight-line compares instead of short-circuit branches,
+    // which made the stage's operand reads wait behind the table read
+    return (zp >= -112.0f) & (zp <= 128.0f) & (zp == rintf(zp)) & (fabsf(s) < 0x1p100f) &
+           (fabsf(s) >= 0x1p-100f);
 }
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(64 * W) void k_w4a16_mfma(const uint16_t *__restric
         bool ok = true;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-            ok = ok && fast_group_ok(sc[nb], zp[nb]);
+            ok = ok & fast_group_ok(sc[nb], zp[nb]);
         if (__all(ok)) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
@@ -445,6 +447,18 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
     float next_s[2] = {0.f, 0.f}, next_z[2] = {0.f, 0.f};  // the pair's second stage
     auto compute = [&](int t) {
         const uint8_t *sb = hbase + (t % kLStages) * L::kStage;
+        auto rd_w = [&](int j) {
+            return *reinterpret_cast<const uint4 *>(sb + (PP ? j * (L::kCh * 64) + woff : wline[j]));
+        };
+        auto rd_x = [&](int j, int q) {
+            return *reinterpret_cast<const uint4 *>(sb + xoff + 4096 * j + (swz ^ (16 * q)));
+        };
+        // the first step's operands are read before the tables and the vote
+        // (measured: 3.8 % fewer loop cycles together with the branch-free vote)
+        const uint4 w_first = rd_w(0);
+        uint4 x_first[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x_first[q] = rd_x(0, q);
         float scs[2], zps[2];
         if (PP) {  // (scale, zero) of the stage's two groups
             const float4 e = *reinterpret_cast<const float4 *>(sb + L::kW + L::kX + ch * 16);
@@ -465,15 +479,14 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
         bool ok = true;
 #pragma unroll
         for (int j = 0; j < kLSteps; ++j)
-            ok = ok && fast_group_ok(scs[j], zps[j]);
+            ok = ok & fast_group_ok(scs[j], zps[j]);
         const bool fast = __all(ok);
 #pragma unroll
         for (int j = 0; j < kLSteps; ++j) {
-            const uint4 w = *reinterpret_cast<const uint4 *>(sb + (PP ? j * (L::kCh * 64) + woff : wline[j]));
+            const uint4 w = j == 0 ? w_first : rd_w(j);
             uint4 xr[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                xr[q] = *reinterpret_cast<const uint4 *>(sb + xoff + 4096 * j + (swz ^ (16 * q)));
+            for (int q = 0; q < 4; ++q) xr[q] = j == 0 ? x_first[q] : rd_x(j, q);
             v4i b0, b1, b2, b3;
             if (fast) {
                 const half2v c0 = zero_point_pair(zps[j]), c1 = c0 + k960;
