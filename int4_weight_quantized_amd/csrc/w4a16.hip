@@ -445,7 +445,10 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
     const int xoff = L::kW + kq * 1024 + r16 * 64;
 
     float next_s[2] = {0.f, 0.f}, next_z[2] = {0.f, 0.f};  // the pair's second stage
-    auto compute = [&](int t) {
+    // `after_vote` (the DMA issue of stage t + 2) runs once the stage's first
+    // LDS reads and the vote are issued, so that those reads start right
+    // after the barrier (measured: 1.2 % fewer loop cycles)
+    auto compute = [&](int t, auto after_vote) {
         const uint8_t *sb = hbase + (t % kLStages) * L::kStage;
         auto rd_w = [&](int j) {
             return *reinterpret_cast<const uint4 *>(sb + (PP ? j * (L::kCh * 64) + woff : wline[j]));
@@ -481,6 +484,7 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
         for (int j = 0; j < kLSteps; ++j)
             ok = ok & fast_group_ok(scs[j], zps[j]);
         const bool fast = __all(ok);
+        after_vote();
 #pragma unroll
         for (int j = 0; j < kLSteps; ++j) {
             const uint4 w = j == 0 ? w_first : rd_w(j);
@@ -518,8 +522,12 @@ __global__ __launch_bounds__(128 * WPH) void k_w4a16_lds(const uint16_t *__restr
             wait_and_barrier<L::kPerWave>();
         else
             wait_and_barrier<0>();
-        if (t + 2 < T) issue(t + 2);
-        compute(t);
+        // the slot of stage t + 2 held stage t - 1, which every wave finished
+        // before this barrier; the next barrier's wait still leaves only
+        // stage t + 2's loads outstanding
+        compute(t, [&] {
+            if (t + 2 < T) issue(t + 2);
+        });
     }
 
     // the second half's partial sums, added to the first half's in LDS
